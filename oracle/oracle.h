@@ -1,0 +1,89 @@
+/* Reference oracle for speculative-decoding verification -- TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, single-threaded C++17 in double precision. Only the tests, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it; the
+ * product library never does, and the two share no code.
+ *
+ * What it follows (pages: "Accelerating Sonar through speculation", original
+ * German page and its Chinese / Hindi translations; "Speculative-Decoding, LLM推理的加速 /
+ * Medusa 方法阅读"):
+ *  - the longest acceptable draft prefix plus one extra target token: a draft of
+ *    n tokens yields up to n+1 tokens (Sonar page, section "Spekulatives Decoding");
+ *  - acceptance decided by comparing the full draft and target distributions, and
+ *    the logits after the accepted prefix sampled for one more token (Sonar page,
+ *    section "Ziel-Entwurf"; section "Spekulatives Decoding", phases "Akzeptanz"
+ *    and "Zielgenerierung"). The page cites Leviathan et al. for the rule but does
+ *    not print it; the rule used is that method's: accept draft token x at
+ *    position i iff u_i < p_t,i(x) / p_d,i(x); on the first rejection at position
+ *    L, sample from the residual max(0, p_t,L - p_d,L) renormalised; if every
+ *    draft is accepted, sample from p_t,k;
+ *  - the Medusa tree walk: sample (or take the argmax of) the root's logits,
+ *    look for a level-1 candidate holding that token, follow it level by level
+ *    until no child matches (Medusa page, section 三 "Attention Tree");
+ *  - the expected accepted length E[L] = sum over tree nodes of the product of
+ *    per-level accuracies along the node's path (Medusa page, section 四).
+ *
+ * Parity pins: every function here is pinned by CPU tests (closed forms,
+ * library routines, brute force, chi-square losslessness, the pages' counts);
+ * see the test files under tests/ that start with test_oracle_.
+ */
+#ifndef SV_ORACLE_H
+#define SV_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype: 0 fp32, 1 bf16, 2 fp16. mode: 0 greedy, 1 stochastic. */
+
+/* Row statistics at temperature T over rows x[rows][V]:
+ * m = max_v x_v, lse = log sum_v exp(x_v / T) = m/T + log sum_v exp((x_v - m)/T),
+ * argmax = lowest index of the largest value (NaN entries never chosen).
+ * flags[r]: bit1 if no entry exceeds -inf or the sum is not finite. */
+int orc_row_stats(int dtype, double T, int64_t rows, int64_t V, const void* x,
+                  double* m, double* lse, int32_t* argmax, int32_t* flags);
+
+/* Inverse CDF over non-negative weights w[0..n): S = sum w, C_v = prefix sums in
+ * ascending order; returns min{v : C_v > u*S}, or the last v with w_v > 0 when
+ * rounding leaves none; -1 if S is not a positive finite number.
+ * lo/hi (optional) receive C_{y-1}/S and C_y/S. */
+int64_t orc_invcdf(const double* w, int64_t n, double u, double* lo, double* hi);
+
+/* Linear verification for B sequences (see header comment). Outputs:
+ *  accept_len[B] in [0,k] (-1 on a data error), out_tokens[B][k+1] (-1 padded),
+ *  p_target/p_draft[B][k] (optional, NaN on error), err_flags[B]
+ *  (bit0 token out of range, bit1 non-finite row), near_tie[B] (1 if an
+ *  evaluated draw lies within tie_eps of its threshold), n_eval[B] (evaluated
+ *  draws). Returns 0, or -1 on bad arguments. */
+int orc_verify_linear(int mode, double T, int64_t B, int64_t k, int64_t V, int dtype,
+                      const void* target, const void* draft, const int32_t* draft_tokens,
+                      const float* uniforms, double tie_eps,
+                      int32_t* accept_len, int32_t* out_tokens, double* p_target,
+                      double* p_draft, int32_t* err_flags, int32_t* near_tie, int32_t* n_eval);
+
+/* Tree verification for B trees of n_nodes (node 0 = root). parent[n_nodes] is
+ * shared when parent_stride == 0, else [B][n_nodes]. Outputs: accept_len[B],
+ * path_nodes[B][max_depth], out_tokens[B][max_depth+1], err_flags[B]
+ * (bit0 candidate out of range, bit1 non-finite row, bit2 invalid tree or depth
+ * above max_depth), near_tie[B], n_eval[B], and optional node_token[B][n_nodes]
+ * (the per-node argmax / sampled token). */
+int orc_verify_tree(int mode, double T, int64_t B, int64_t n_nodes, int64_t V, int dtype,
+                    const int32_t* parent, int64_t parent_stride, const int32_t* cand,
+                    const void* logits, const float* uniforms, int64_t max_depth, double tie_eps,
+                    int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
+                    int32_t* err_flags, int32_t* near_tie, int32_t* n_eval, int32_t* node_token);
+
+/* E[L] of a candidate tree under independent per-level accuracies:
+ * sum over non-root nodes of prod_{edges on the path} acc[(depth-1)*S + rank-1],
+ * rank in 1..S (Medusa page, section 四, items 2-4). */
+double orc_expected_accept_len(int64_t n_nodes, const int32_t* parent, const int32_t* rank,
+                               int64_t S, const double* acc);
+
+/* Planted-mistake switch for negative-control tests only (0 = off). */
+void orc_set_mutation(int which);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
