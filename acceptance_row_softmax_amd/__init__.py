@@ -1,0 +1,273 @@
+"""Python binding of libspecverify (speculative-decoding verification on MI355X).
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels of ``libspecverify.so``; PyTorch supplies device buffers and the
+current stream. There is no fallback: if the library is missing this module
+raises on first use.
+
+Entry points mirror the C ABI in ``include/specverify.h``:
+
+* :func:`verify_linear` -- longest acceptable draft prefix + one target token
+  ("Accelerating Sonar through speculation", sections "Spekulatives Decoding"
+  and "Ziel-Entwurf").
+* :func:`verify_tree` -- candidate-tree walk ("Speculative-Decoding, LLM推理的加速 /
+  Medusa 方法阅读", section 三).
+* :func:`row_stats` -- per-row max, log-sum-exp and argmax at a temperature.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+from . import _build
+
+SV_GREEDY, SV_STOCHASTIC = 0, 1
+SV_F32, SV_BF16, SV_F16 = 0, 1, 2
+SV_ERR_TOKEN, SV_ERR_ROW, SV_ERR_TREE = 1, 2, 4
+SV_MAX_K, SV_MAX_TREE_NODES = 64, 16384
+
+LIB_PATH = _build.LIB
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libspecverify.so not found at {LIB_PATH}; run "
+                               "acceptance_row_softmax_amd._build.build() (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, f32, sz, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+        L.spec_verify_status_string.restype = ctypes.c_char_p
+        L.spec_verify_status_string.argtypes = [i32]
+        L.spec_verify_linear_workspace.restype = sz
+        L.spec_verify_linear_workspace.argtypes = [i64, i64, i64, i32, i32]
+        L.spec_verify_linear.restype = i32
+        L.spec_verify_linear.argtypes = [i32, f32, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp]
+        L.spec_verify_tree_workspace.restype = sz
+        L.spec_verify_tree_workspace.argtypes = [i64, i64, i64, i32, i32]
+        L.spec_verify_tree.restype = i32
+        L.spec_verify_tree.argtypes = [i32, f32, i64, i64, i64, i32, vp, i64, vp, vp, vp, i64, vp, vp,
+                                       vp, vp, vp, sz, vp]
+        L.spec_row_stats_workspace.restype = sz
+        L.spec_row_stats_workspace.argtypes = [i64, i64, i32]
+        L.spec_row_stats.restype = i32
+        L.spec_row_stats.argtypes = [i32, f32, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_workspace_clear.restype = i32
+        L.spec_workspace_clear.argtypes = [vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_tree_workspace",
+            "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
+            "spec_workspace_clear", "spec_verify_status_string")
+
+
+def status_string(status: int) -> str:
+    return lib().spec_verify_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SpecVerifyError(status, where)
+
+
+# ------------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def sv_dtype(t) -> int:
+    torch = _torch()
+    m = {torch.float32: SV_F32, torch.bfloat16: SV_BF16, torch.float16: SV_F16}
+    if t.dtype not in m:
+        raise TypeError(f"logits dtype {t.dtype} not supported (float32, bfloat16, float16)")
+    return m[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _need(t, name, dtype=None, device=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Workspace:
+    """Device workspace cache keyed by (device, kind, shape). Buffers are
+    zero-filled at allocation; calls leave their control words zero."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, device, key, nbytes: int):
+        torch = _torch()
+        k = (str(device), key)
+        buf = self._bufs.get(k)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._bufs[k] = buf
+        return buf
+
+
+_WS = Workspace()
+
+
+def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic",
+                  temperature: float = 1.0, *, with_probs: bool = True, err_flags: bool = True,
+                  workspace=None, stream=None):
+    """Verify B linear drafts of k tokens.
+
+    target [B][k+1][V], draft [B][k][V] (same dtype; draft unused in greedy mode),
+    draft_tokens [B][k] int32, uniforms [B][k+1] float32 (stochastic only).
+    Returns a dict of device tensors: accept_len [B], out_tokens [B][k+1],
+    p_target / p_draft [B][k] (stochastic, if with_probs), err_flags [B].
+    """
+    torch = _torch()
+    stoch = mode == "stochastic"
+    if mode not in ("stochastic", "greedy"):
+        raise ValueError("mode must be 'greedy' or 'stochastic'")
+    _need(target, "target")
+    dev = target.device
+    if target.dim() != 3:
+        raise ValueError("target must be [B][k+1][V]")
+    B, k1, V = target.shape
+    k = k1 - 1
+    dt = sv_dtype(target)
+    if stoch and k > 0:
+        _need(draft, "draft", target.dtype, dev)
+        if tuple(draft.shape) != (B, k, V):
+            raise ValueError("draft must be [B][k][V]")
+    else:
+        draft = None
+    if k > 0:
+        _need(draft_tokens, "draft_tokens", torch.int32, dev)
+        if tuple(draft_tokens.shape) != (B, k):
+            raise ValueError("draft_tokens must be [B][k]")
+    else:
+        draft_tokens = None
+    if stoch:
+        _need(uniforms, "uniforms", torch.float32, dev)
+        if tuple(uniforms.shape) != (B, k + 1):
+            raise ValueError("uniforms must be [B][k+1]")
+    else:
+        uniforms = None
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    pt = torch.empty((B, k), dtype=torch.float32, device=dev) if (stoch and with_probs) else None
+    pd = torch.empty((B, k), dtype=torch.float32, device=dev) if (stoch and with_probs) else None
+    ef = torch.empty(B, dtype=torch.int32, device=dev) if err_flags else None
+    L = lib()
+    mcode = SV_STOCHASTIC if stoch else SV_GREEDY
+    nbytes = L.spec_verify_linear_workspace(B, k, V, dt, mcode)
+    ws = workspace if workspace is not None else _WS.get(dev, ("linear", B, k, V, dt, mcode), nbytes)
+    st = L.spec_verify_linear(mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft),
+                              _ptr(draft_tokens), _ptr(uniforms), _ptr(acc), _ptr(out), _ptr(pt),
+                              _ptr(pd), _ptr(ef), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "spec_verify_linear")
+    res = {"accept_len": acc, "out_tokens": out, "err_flags": ef}
+    if pt is not None:
+        res["p_target"], res["p_draft"] = pt, pd
+    return res
+
+
+def verify_tree(parent, cand_tokens, logits, uniforms, max_depth: int, mode: str = "greedy",
+                temperature: float = 1.0, *, workspace=None, stream=None):
+    """Verify B candidate trees of n_nodes (node 0 = root).
+
+    parent [n_nodes] (shared) or [B][n_nodes] int32, cand_tokens [B][n_nodes] int32,
+    logits [B][n_nodes][V], uniforms [B][n_nodes] float32 (stochastic only).
+    Returns accept_len [B], path_nodes [B][max_depth], out_tokens [B][max_depth+1],
+    err_flags [B].
+    """
+    torch = _torch()
+    stoch = mode == "stochastic"
+    if mode not in ("stochastic", "greedy"):
+        raise ValueError("mode must be 'greedy' or 'stochastic'")
+    _need(logits, "logits")
+    dev = logits.device
+    B, N, V = logits.shape
+    dt = sv_dtype(logits)
+    _need(parent, "parent", torch.int32, dev)
+    if parent.dim() == 1:
+        if parent.shape[0] != N:
+            raise ValueError("parent must have n_nodes entries")
+        stride = 0
+    else:
+        if tuple(parent.shape) != (B, N):
+            raise ValueError("parent must be [n_nodes] or [B][n_nodes]")
+        stride = N
+    _need(cand_tokens, "cand_tokens", torch.int32, dev)
+    if tuple(cand_tokens.shape) != (B, N):
+        raise ValueError("cand_tokens must be [B][n_nodes]")
+    if stoch:
+        _need(uniforms, "uniforms", torch.float32, dev)
+        if tuple(uniforms.shape) != (B, N):
+            raise ValueError("uniforms must be [B][n_nodes]")
+    else:
+        uniforms = None
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, max_depth), dtype=torch.int32, device=dev)
+    out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    ef = torch.empty(B, dtype=torch.int32, device=dev)
+    L = lib()
+    mcode = SV_STOCHASTIC if stoch else SV_GREEDY
+    nbytes = L.spec_verify_tree_workspace(B, N, V, dt, mcode)
+    ws = workspace if workspace is not None else _WS.get(dev, ("tree", B, N, V, dt, mcode), nbytes)
+    st = L.spec_verify_tree(mcode, float(temperature), B, N, V, dt, _ptr(parent), stride,
+                            _ptr(cand_tokens), _ptr(logits), _ptr(uniforms), int(max_depth),
+                            _ptr(acc), _ptr(path) if max_depth > 0 else None, _ptr(out), _ptr(ef),
+                            _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "spec_verify_tree")
+    return {"accept_len": acc, "path_nodes": path, "out_tokens": out, "err_flags": ef}
+
+
+def row_stats(x, temperature: float = 1.0, *, workspace=None, stream=None):
+    """Per-row max, log-sum-exp at temperature T, argmax and error bits of x [rows][V]."""
+    torch = _torch()
+    _need(x, "x")
+    dev = x.device
+    V = x.shape[-1]
+    rows = x.numel() // V
+    dt = sv_dtype(x)
+    m = torch.empty(rows, dtype=torch.float32, device=dev)
+    lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    am = torch.empty(rows, dtype=torch.int32, device=dev)
+    ef = torch.empty(rows, dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.spec_row_stats_workspace(rows, V, dt)
+    ws = workspace if workspace is not None else _WS.get(dev, ("rows", rows, V, dt), nbytes)
+    st = L.spec_row_stats(dt, float(temperature), rows, V, _ptr(x), _ptr(m), _ptr(lse), _ptr(am),
+                          _ptr(ef), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "spec_row_stats")
+    return {"max": m, "lse": lse, "argmax": am, "err_flags": ef}

@@ -1,0 +1,169 @@
+/* libspecverify -- speculative-decoding verification on AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the acceptance step of speculative decoding: given the
+ * target model's logits at the verified positions and the draft's logits (or a
+ * candidate tree), it finds the longest acceptable draft prefix and emits one
+ * more token from the target.
+ *
+ * Sources (web pages; sections named as on the pages):
+ *  [S-SD]  "Accelerating Sonar through speculation", section "Spekulatives Decoding":
+ *          each candidate prefix is scored, the longest one above the acceptance
+ *          threshold is kept, and a draft of n tokens yields up to n+1 tokens;
+ *          phases "Akzeptanz" and "Zielgenerierung": the target logits at the first
+ *          mismatch, or after the last draft, are sampled for one more token.
+ *  [S-ZE]  same page, section "Ziel-Entwurf": the sampler finds the accepted length
+ *          by comparing the full draft and target distributions, then samples the
+ *          target's extra logits row.
+ *  [S-MTP] same page, section "MTP": all schemes share sampling and logit
+ *          processing; section "MTP-Zeitplan für ein einzelnes Token": the target
+ *          verifies 2*D tokens for a decode batch of D (k = 1).
+ *  [S-INF] same page, section "Inferenz mit spekulativem Decoding": the accepted
+ *          count sets the next sequence length; the library never synchronises
+ *          with the host, so results stay on the device.
+ *  [M-3]   "Speculative-Decoding, LLM推理的加速 / Medusa 方法阅读", section 三
+ *          (Attention Tree): tree nodes get logits from one pass; the sampler's token
+ *          at the root is looked up among level-1 candidates and followed level by
+ *          level while a child matches.
+ * The acceptance rule is the one of the method the Sonar page cites (Leviathan et
+ * al.) but does not print: accept draft token x at position i iff
+ * u_i < p_t,i(x) / p_d,i(x); after the first rejection at L, draw from
+ * max(0, p_t,L - p_d,L) renormalised; if all k drafts pass, draw from p_t,k.
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers unless stated otherwise; the caller
+ *    owns every buffer. The library allocates nothing, frees nothing and keeps no
+ *    pointer after returning.
+ *  - Logits are row-major with contiguous rows of V elements in the stated dtype.
+ *    Rows whose start is 16-byte aligned take the vector path; other rows are
+ *    handled element by element (correct, slower).
+ *  - softmax at temperature T: p(v) = exp(x_v / T) / sum_w exp(x_w / T). Greedy
+ *    mode ignores T and the uniforms and uses argmax (largest value, lowest index
+ *    on ties, NaN entries never chosen).
+ *  - Inverse CDF draw with uniform u over weights w: the smallest v whose
+ *    cumulative weight exceeds u * sum(w).
+ *  - Calls only enqueue work on `stream` and never synchronise; outputs are valid
+ *    once the stream reaches that point. Concurrent calls need distinct workspaces.
+ *  - Workspace: device memory of at least the size the *_workspace function
+ *    returns, 256-byte aligned, zero-filled before its first use (for instance with
+ *    spec_workspace_clear). Every call leaves its control words zero again, so a
+ *    workspace can be reused without clearing by calls of the same entry point and
+ *    shape (B, k or n_nodes, V, dtype, mode); clear it again before a call of another
+ *    shape, since the control words sit at offsets that depend on the shape.
+ *  - Errors detectable on the host return a non-zero status before anything is
+ *    enqueued. Data errors seen on the device set bits in err_flags (if given) and
+ *    give that sequence accept_len = -1 and -1 tokens:
+ *      bit0 SV_ERR_TOKEN   a draft or candidate token outside [0, V)
+ *      bit1 SV_ERR_ROW     a row with no entry above -inf, or (stochastic) a
+ *                          non-finite softmax normaliser (NaN or +inf logits)
+ *      bit2 SV_ERR_TREE    parent[0] != -1, parent[i] outside [0, i), or a node
+ *                          deeper than max_depth
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* sv_stream_t; /* the same type as hipStream_t; NULL = default stream */
+
+typedef enum {
+  SV_OK = 0,
+  SV_EINVAL = 1,      /* bad size, NULL required pointer, bad temperature or mode */
+  SV_EDTYPE = 2,      /* unknown dtype */
+  SV_EWORKSPACE = 3,  /* workspace NULL, misaligned or too small */
+  SV_EHIP = 4,        /* a HIP launch failed */
+  SV_ELIMIT = 5       /* shape beyond a documented limit */
+} sv_status;
+
+typedef enum { SV_GREEDY = 0, SV_STOCHASTIC = 1 } sv_mode;
+typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
+
+enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4 };
+
+/* Limits: k <= SV_MAX_K drafts per sequence; n_nodes <= SV_MAX_TREE_NODES; V < 2^31. */
+enum { SV_MAX_K = 64, SV_MAX_TREE_NODES = 16384 };
+
+/* ---------------------------------------------------------------- linear drafts
+ * [S-SD], [S-ZE], [S-MTP]. B sequences, k draft tokens each (k = 0 is plain
+ * sampling from target row 0).
+ *   target_logits  [B][k+1][V]  target logits at the k draft positions and after them
+ *   draft_logits   [B][k][V]    draft logits; read in SV_STOCHASTIC only (may be NULL in greedy)
+ *   draft_tokens   [B][k]       int32 draft tokens (may be NULL when k = 0)
+ *   uniforms       [B][k+1]     float in [0,1): u[b][i<k] decides draft i, u[b][k] is the
+ *                               final draw; SV_STOCHASTIC only (may be NULL in greedy)
+ * Outputs:
+ *   accept_len     [B]          L in [0,k], or -1 on a data error
+ *   out_tokens     [B][k+1]     the L accepted drafts, then the target's token, then -1
+ *   p_target, p_draft [B][k]    optional (NULL to skip), SV_STOCHASTIC only: p_t,i(x_i) and
+ *                               p_d,i(x_i) for every i < k (NaN on a data error)
+ *   err_flags      [B]          optional data-error bits (see above)
+ * Greedy mode accepts x_i iff x_i = argmax(target row i) and emits argmax(target row L).
+ */
+size_t spec_verify_linear_workspace(int64_t B, int64_t k, int64_t V, sv_dtype dtype, sv_mode mode);
+
+sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                             sv_dtype dtype, const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const float* uniforms,
+                             int32_t* accept_len, int32_t* out_tokens, float* p_target,
+                             float* p_draft, int32_t* err_flags, void* workspace,
+                             size_t workspace_bytes, sv_stream_t stream);
+
+/* ---------------------------------------------------------------- candidate trees
+ * [M-3]; "Accelerating Sonar through speculation", section "EAGLE" (keep the longest
+ * suitable candidate sequence and append one target token).
+ *   n_nodes        nodes per tree including the root (node 0)
+ *   parent         [n_nodes] shared by all trees when parent_batch_stride = 0, else
+ *                  parent + b * parent_batch_stride; parent[0] = -1, 0 <= parent[i] < i
+ *   cand_tokens    [B][n_nodes] int32 candidate token of each node (entry 0 ignored)
+ *   target_logits  [B][n_nodes][V] target logits at every node
+ *   uniforms       [B][n_nodes] one draw per node; SV_STOCHASTIC only
+ *   max_depth      caller's bound on the tree depth; sizes path_nodes / out_tokens
+ * Each node n gets token y_n: argmax of its row (greedy) or the inverse-CDF draw
+ * from softmax(row / T) with u[b][n] (stochastic). Node i is accepted iff its parent
+ * is accepted and cand_i = y_parent(i); the root always is. The accepted node of
+ * greatest depth (lowest index on ties) ends the path.
+ * Outputs:
+ *   accept_len     [B]                 depth of that node, or -1 on a data error
+ *   path_nodes     [B][max_depth]      its path from level 1 down, then -1
+ *   out_tokens     [B][max_depth + 1]  the path's candidate tokens, then y of the last
+ *                                      node, then -1
+ *   err_flags      [B]                 optional data-error bits
+ */
+size_t spec_verify_tree_workspace(int64_t B, int64_t n_nodes, int64_t V, sv_dtype dtype,
+                                  sv_mode mode);
+
+sv_status spec_verify_tree(sv_mode mode, float temperature, int64_t B, int64_t n_nodes, int64_t V,
+                           sv_dtype dtype, const int32_t* parent, int64_t parent_batch_stride,
+                           const int32_t* cand_tokens, const void* target_logits,
+                           const float* uniforms, int64_t max_depth, int32_t* accept_len,
+                           int32_t* path_nodes, int32_t* out_tokens, int32_t* err_flags,
+                           void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+/* ---------------------------------------------------------------- row statistics
+ * The streaming row softmax the verifier is built on, exposed for diagnostics:
+ * for rows x[rows][V], row_max = max_v x_v, row_lse = log sum_v exp(x_v / T),
+ * row_argmax = lowest index of the maximum (-1 and SV_ERR_ROW if no entry exceeds
+ * -inf). Any output pointer may be NULL. row_lse is NaN when the normaliser is not
+ * finite (SV_ERR_ROW).
+ */
+size_t spec_row_stats_workspace(int64_t rows, int64_t V, sv_dtype dtype);
+
+sv_status spec_row_stats(sv_dtype dtype, float temperature, int64_t rows, int64_t V,
+                         const void* x, float* row_max, float* row_lse, int32_t* row_argmax,
+                         int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                         sv_stream_t stream);
+
+/* Zero-fill `bytes` of a 16-byte aligned workspace on `stream` with a fill kernel (no host sync). */
+sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream);
+
+/* Static description of a status code. */
+const char* spec_verify_status_string(sv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

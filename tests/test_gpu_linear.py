@@ -1,0 +1,124 @@
+"""GPU parity of linear verification: libspecverify through its C ABI against the
+oracle, element by element, on seeded synthetic inputs.
+
+Bar: accept lengths and tokens bit-exact (greedy: always; stochastic: except
+sequences where an evaluated uniform lies within 1e-6 of its threshold, which
+are counted and must stay below 1e-4 of evaluated draws); p_target / p_draft
+within 1e-5 relative of the oracle's double values."""
+import numpy as np
+import pytest
+
+import gen
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, seqs=None):
+    G.say(f"{w.name} {w.mode} B={w.B} k={w.k} V={w.V} dtype={w.dtype} T={w.temperature}")
+    g = G.run_linear(w)
+    o = G.oracle_linear(w, seqs)
+    near, n_eval = G.compare_linear(g, o, w.mode == "stochastic", seqs)
+    return g, o, near, n_eval
+
+
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_c1_tiny_many_sequences(mode):
+    # 20000 independent sequences of the tiny configuration (fp32, V=1000, k=4)
+    w = gen.c1_tiny(0, mode, B=20000)
+    g, o, near, n_eval = _check(w)
+    if mode == "stochastic":
+        assert n_eval > 50000
+        assert near / n_eval < 1e-4, (near, n_eval)
+        # the acceptance rate is in the expected regime (1 - total variation ~ 0.8)
+        assert 0.6 < np.mean(g["accept_len"] >= 1) < 0.95
+    else:
+        assert near == 0
+
+
+@pytest.mark.parametrize("dtype", [gen.DT_F32, gen.DT_BF16, gen.DT_F16])
+@pytest.mark.parametrize("V", [12345, 20000, 8192, 8193, 3])
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_tiles_and_ragged_tails(dtype, V, mode):
+    # several 16 KiB chunks, a partial last chunk, and (V=12345, 8193, 3 in 2-byte
+    # dtypes) rows that do not start on a 16-byte boundary
+    w = gen.linear_draft_target(90 + dtype, V, 8, 3, V, dtype, 3.0, 1.0, mode, 0.8, f"ragged{V}")
+    _check(w)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_c2_draft_target_full_size(seed):
+    w = gen.c2_linear(seed)            # B=32, k=4, V=128256, bf16, T=0.7
+    _check(w)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "stochastic"])
+def test_c3_mtp_full_size(mode):
+    w = gen.c3_mtp(0, mode)            # D=256, k=1, V=129280, bf16, T=1
+    g, o, near, n_eval = _check(w)
+
+
+def test_identity_accepts_all_plus_bonus():
+    w = gen.c2_linear(5, B=8)
+    w.draft = np.ascontiguousarray(w.target[:, :w.k, :])
+    w.draft_tokens = gen.gumbel_rows(gen.key(2, 5, 9), w.dtype, w.draft, w.V, w.temperature).reshape(w.B, w.k)
+    g, o, near, n_eval = _check(w)
+    assert np.all(g["accept_len"] == w.k)
+    np.testing.assert_array_equal(g["out_tokens"][:, :w.k], w.draft_tokens)
+    np.testing.assert_array_equal(g["p_target"], g["p_draft"])
+
+
+@pytest.mark.parametrize("k", [0, 1, 8, 64])
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_draft_lengths(k, mode):
+    w = gen.linear_draft_target(80, k, 6, k, 3000, gen.DT_BF16, 1.0, 0.3, mode, 1.0, f"k{k}")
+    _check(w)
+
+
+def test_argmax_ties_across_chunks():
+    # bf16 rows of V=20000 (chunks of 8192): equal maxima placed on both sides of
+    # chunk boundaries and in the tail; the lowest index must win
+    B, k, V = 6, 2, 20000
+    rng = np.random.default_rng(3)
+    x = np.round(rng.normal(0, 1, size=(B, k + 1, V)) * 8) / 8
+    spots = [(8191, 8192), (8192, 19999), (0, 16384), (16383, 16384), (5, 6), (19998, 19999)]
+    for b in range(B):
+        for r in range(k + 1):
+            for s in spots[(b + r) % len(spots)]:
+                x[b, r, s] = 20.0
+    t = gen.round_to(gen.DT_BF16, x)
+    am = np.argmax(gen.decode(gen.DT_BF16, t), axis=2)
+    tok = am[:, :k].astype(np.int32)
+    tok[::2, 1] = (tok[::2, 1] + 1) % V
+    w = gen.LinearWorkload("ties", "greedy", 1.0, B, k, V, gen.DT_BF16, t,
+                           np.zeros((B, k, V), np.uint16), tok, np.zeros((B, k + 1), np.float32))
+    g, o, _, _ = _check(w)
+    np.testing.assert_array_equal(g["out_tokens"][1::2, k], am[1::2, k])
+
+
+def test_data_errors():
+    w = gen.linear_draft_target(70, 0, 5, 2, 5000, gen.DT_F16, 2.0, 0.5, "stochastic", 1.0, "errs")
+    w.draft_tokens[0, 1] = w.V                       # token out of range
+    w.target[1, 1, 77] = 0x7E00                      # NaN (fp16 bits)
+    w.draft[2, 0, :] = 0xFC00                        # -inf row
+    w.target[3, 2, 10] = 0x7C00                      # +inf
+    g, o, _, _ = _check(w)
+    assert list(g["err_flags"]) == [1, 2, 2, 2, 0]
+    assert list(g["accept_len"][:4]) == [-1] * 4
+    wg = gen.linear_draft_target(70, 0, 5, 2, 5000, gen.DT_F16, 2.0, 0.5, "greedy", 1.0, "errs")
+    wg.target[1, 1, :] = 0xFC00                      # no usable entry in a target row
+    wg.draft_tokens[2, 0] = -1
+    g, o, _, _ = _check(wg)
+    assert list(g["err_flags"]) == [0, 2, 1, 0, 0]
+
+
+def test_deterministic_and_workspace_reuse():
+    w1 = gen.c2_linear(7, B=8)
+    w2 = gen.c2_linear(8, B=8)
+    a = G.run_linear(w1)
+    b = G.run_linear(w2)
+    c = G.run_linear(w1)
+    for key in a:
+        if a[key] is not None:
+            np.testing.assert_array_equal(a[key], c[key])
+    G.compare_linear(b, G.oracle_linear(w2), True)

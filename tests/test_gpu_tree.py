@@ -1,0 +1,109 @@
+"""GPU parity of candidate-tree verification against the oracle.
+
+Bar: accept_len, path_nodes and out_tokens bit-exact (greedy: always;
+stochastic: except trees with an accepted node whose uniform lies within 1e-6
+of one of its bin edges, counted)."""
+import numpy as np
+import pytest
+
+import gen
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, trees=None, max_depth=None):
+    G.say(f"{w.name} {w.mode} B={w.B} N={w.n_nodes} V={w.V} dtype={w.dtype}")
+    g = G.run_tree(w, max_depth)
+    o = G.oracle_tree(w, trees, max_depth)
+    near, n_eval = G.compare_tree(g, o, trees)
+    return g, o, near, n_eval
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_c4_sparse_tree_full_size(seed):
+    w = gen.c4_medusa_sparse(seed)          # B=16, 64 nodes + root, V=32000, fp16, greedy
+    g, o, _, _ = _check(w)
+    assert np.all(g["err_flags"] == 0)
+
+
+def test_c4_sparse_tree_stochastic():
+    w = gen.c4_medusa_sparse(4, mode="stochastic")
+    _check(w)
+
+
+def test_c5_full_tree_greedy():
+    w = gen.c5_medusa_full(0)               # B=4, 4680 nodes + root, V=32000, fp16
+    g, o, _, _ = _check(w)
+    assert w.n_nodes == 4681
+
+
+def test_c5_full_tree_stochastic_sampled_trees():
+    w = gen.c5_medusa_full(1, mode="stochastic")
+    _check(w, trees=[0, 3])                 # oracle checks two of the four trees
+
+
+@pytest.mark.parametrize("dtype", [gen.DT_F32, gen.DT_BF16, gen.DT_F16])
+@pytest.mark.parametrize("V", [12345, 20000, 7])
+@pytest.mark.parametrize("mode", ["greedy", "stochastic"])
+def test_small_trees_ragged(dtype, V, mode):
+    parent, rank = gen.cartesian_tree([3, 2, 2])
+    n = len(parent)
+    B = 6
+    logits_d = gen.normal_pair(gen.key(60, V, 1), 2.0, 0, 0.0, B * n * V, dtype, want_b=False)[0]
+    logits = logits_d.reshape(B, n, V)
+    am = gen.argmax_rows(dtype, logits, V).reshape(B, n)
+    rng = np.random.default_rng(V + dtype)
+    cand = np.where(rng.random((B, n)) < 0.6, am[:, parent], rng.integers(0, V, (B, n))).astype(np.int32)
+    cand[:, 0] = -1
+    u = gen.uniforms(gen.key(60, V, 4), B * n).reshape(B, n)
+    w = gen.TreeWorkload("small", mode, 0.9, B, n, V, dtype, parent, cand, logits, u, 3)
+    _check(w)
+
+
+def test_chain_tree_equals_linear_greedy():
+    lw = gen.linear_draft_target(61, 0, 16, 4, 9000, gen.DT_BF16, 2.0, 0.3, "greedy", 1.0, "chain")
+    parent = np.arange(-1, 4, dtype=np.int32)
+    cand = np.concatenate([np.full((16, 1), -1, np.int32), lw.draft_tokens], axis=1)
+    w = gen.TreeWorkload("chain", "greedy", 1.0, 16, 5, lw.V, lw.dtype, parent, cand, lw.target,
+                         np.zeros((16, 5), np.float32), 4)
+    g, o, _, _ = _check(w)
+    lin = G.run_linear(lw)
+    np.testing.assert_array_equal(g["accept_len"], lin["accept_len"])
+    np.testing.assert_array_equal(g["out_tokens"], lin["out_tokens"])
+
+
+def test_per_tree_parents_and_errors():
+    B, V = 5, 4000
+    n = 6
+    rng = np.random.default_rng(8)
+    logits = gen.round_to(gen.DT_F16, rng.normal(0, 2, size=(B, n, V)))
+    am = np.argmax(gen.decode(gen.DT_F16, logits), axis=2)
+    parent = np.tile(np.array([-1, 0, 0, 1, 3, 4], np.int32), (B, 1))
+    cand = np.zeros((B, n), np.int32)
+    for b in range(B):
+        for i in range(1, n):
+            cand[b, i] = am[b, parent[b, i]]
+    parent[1, 4] = 4          # not an earlier node
+    parent[2, 0] = 3          # the root must have parent -1
+    cand[3, 2] = V + 1        # candidate out of range
+    w = gen.TreeWorkload("errs", "greedy", 1.0, B, n, V, gen.DT_F16, parent, cand, logits,
+                         np.zeros((B, n), np.float32), 4)
+    g, o, _, _ = _check(w)
+    assert list(g["err_flags"]) == [0, 4, 4, 1, 0]
+    assert g["accept_len"][0] == 4 and g["accept_len"][4] == 4
+    # a bound below the tree's depth is an error for every tree
+    g2, o2, _, _ = _check(w, max_depth=3)
+    assert np.all(g2["err_flags"] & 4)
+
+
+def test_root_only_tree():
+    B, V = 3, 1000
+    rng = np.random.default_rng(1)
+    logits = rng.normal(size=(B, 1, V)).astype(np.float32)
+    for mode in ("greedy", "stochastic"):
+        w = gen.TreeWorkload("root", mode, 1.0, B, 1, V, gen.DT_F32, np.array([-1], np.int32),
+                             np.full((B, 1), -1, np.int32), logits,
+                             gen.uniforms(gen.key(1, 1, 1), B).reshape(B, 1), 0)
+        g, o, _, _ = _check(w)
+        assert np.all(g["accept_len"] == 0)
