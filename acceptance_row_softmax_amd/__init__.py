@@ -53,6 +53,9 @@ def lib():
         L.spec_verify_linear.restype = i32
         L.spec_verify_linear.argtypes = [i32, f32, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, sz, vp]
+        for fn in (L.spec_verify_linear_accept, L.spec_verify_linear_correct):
+            fn.restype = i32
+            fn.argtypes = L.spec_verify_linear.argtypes
         L.spec_verify_tree_workspace.restype = sz
         L.spec_verify_tree_workspace.argtypes = [i64, i64, i64, i32, i32]
         L.spec_verify_tree.restype = i32
@@ -68,7 +71,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_tree_workspace",
+EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_linear_accept",
+            "spec_verify_linear_correct", "spec_verify_tree_workspace",
             "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
             "spec_workspace_clear", "spec_verify_status_string")
 
@@ -145,7 +149,7 @@ _WS = Workspace()
 
 def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic",
                   temperature: float = 1.0, *, with_probs: bool = True, err_flags: bool = True,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, phase: str = "both", out=None):
     """Verify B linear drafts of k tokens.
 
     target [B][k+1][V], draft [B][k][V] (same dtype; draft unused in greedy mode),
@@ -182,23 +186,25 @@ def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic
             raise ValueError("uniforms must be [B][k+1]")
     else:
         uniforms = None
-    acc = torch.empty(B, dtype=torch.int32, device=dev)
-    out = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    pt = torch.empty((B, k), dtype=torch.float32, device=dev) if (stoch and with_probs) else None
-    pd = torch.empty((B, k), dtype=torch.float32, device=dev) if (stoch and with_probs) else None
-    ef = torch.empty(B, dtype=torch.int32, device=dev) if err_flags else None
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+               "err_flags": torch.empty(B, dtype=torch.int32, device=dev) if err_flags else None}
+        if stoch and with_probs:
+            out["p_target"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+            out["p_draft"] = torch.empty((B, k), dtype=torch.float32, device=dev)
     L = lib()
+    fn = {"both": L.spec_verify_linear, "accept": L.spec_verify_linear_accept,
+          "correct": L.spec_verify_linear_correct}[phase]
     mcode = SV_STOCHASTIC if stoch else SV_GREEDY
     nbytes = L.spec_verify_linear_workspace(B, k, V, dt, mcode)
     ws = workspace if workspace is not None else _WS.get(dev, ("linear", B, k, V, dt, mcode), nbytes)
-    st = L.spec_verify_linear(mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft),
-                              _ptr(draft_tokens), _ptr(uniforms), _ptr(acc), _ptr(out), _ptr(pt),
-                              _ptr(pd), _ptr(ef), _ptr(ws), ws.numel(), _stream(stream))
-    _check(st, "spec_verify_linear")
-    res = {"accept_len": acc, "out_tokens": out, "err_flags": ef}
-    if pt is not None:
-        res["p_target"], res["p_draft"] = pt, pd
-    return res
+    st = fn(mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft), _ptr(draft_tokens),
+            _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("p_target")),
+            _ptr(out.get("p_draft")), _ptr(out.get("err_flags")), _ptr(ws), ws.numel(),
+            _stream(stream))
+    _check(st, "spec_verify_linear" + ("" if phase == "both" else "_" + phase))
+    return out
 
 
 def verify_tree(parent, cand_tokens, logits, uniforms, max_depth: int, mode: str = "greedy",

@@ -48,7 +48,7 @@ __device__ RowStat finalize_row(const char* row, int64_t V, const Partial* parts
     float M = -INFINITY;
     int arg = INT_SENTINEL;
     for (int c = c_lo; c < c_hi; ++c) {
-      const Partial p = parts[c];
+      const Partial p = fetch(parts + c);
       argmax_combine(M, arg, p.m, p.idx);
     }
     wave_argmax(M, arg);
@@ -57,7 +57,7 @@ __device__ RowStat finalize_row(const char* row, int64_t V, const Partial* parts
       const double Mc0 = (double)M * (double)c0;
       double local = 0.0;
       for (int c = c_lo; c < c_hi; ++c) {
-        const Partial p = parts[c];
+        const Partial p = fetch(parts + c);
         if (p.m != -INFINITY) local += p.s * exp2((double)chunk_mc0(p.m, c0) - Mc0);
       }
       Z = wave_sum(local);
@@ -78,13 +78,13 @@ __device__ RowStat finalize_row(const char* row, int64_t V, const Partial* parts
       const double Mc0 = (double)st.M * (double)c0;
       if (wave_id() == 0) {
         const ChunkPick pk = pick_chunk(C, (double)u, [&](int c) -> double {
-          const Partial p = parts[c];
+          const Partial p = fetch(parts + c);
           return (p.m == -INFINITY) ? 0.0 : p.s * exp2((double)chunk_mc0(p.m, c0) - Mc0);
         });
         if (lane_id() == 0) {
           sm.result = pk.c;
           if (pk.c >= 0) {
-            const float mc0 = chunk_mc0(parts[pk.c].m, c0);
+            const float mc0 = chunk_mc0(fetch(parts + pk.c).m, c0);
             // threshold in the chunk's own units (weights relative to its mc0)
             sm.theta = pk.fallback ? INFINITY : (pk.theta - pk.before) * exp2(Mc0 - (double)mc0);
           }
@@ -95,7 +95,7 @@ __device__ RowStat finalize_row(const char* row, int64_t V, const Partial* parts
       const double th = sm.theta;
       __syncthreads();
       if (cstar >= 0) {
-        SoftmaxWeights<DT> pol{row, V, row_aligned(row), c0, chunk_mc0(parts[cstar].m, c0)};
+        SoftmaxWeights<DT> pol{row, V, row_aligned(row), c0, chunk_mc0(fetch(parts + cstar).m, c0)};
         st.y = (int)chunk_invcdf<DT>(pol, cstar, th, sm);
       } else {
         st.y = -1;
@@ -146,9 +146,9 @@ __device__ void linear_decide(const LinearParams& P, int64_t b) {
   const int x = has ? P.tokens[b * k + lane] : 0;
   const bool tok_bad = has && (x < 0 || x >= V);
   RowStat ts{}, ds{};
-  if (has) ts = rows[lane];
-  if (STOCH && has) ds = rows[k + 1 + lane];
-  const RowStat tk = rows[k];
+  if (has) ts = fetch(rows + lane);
+  if (STOCH && has) ds = fetch(rows + k + 1 + lane);
+  const RowStat tk = fetch(rows + k);
   const bool row_bad = (has && !ts.ok) || (STOCH && has && !ds.ok) || !tk.ok;
   int err = 0;
   if (__ballot(tok_bad)) err |= SV_ERR_TOKEN;
@@ -224,13 +224,13 @@ __global__ __launch_bounds__(BLOCK) void linear_stats_kernel(LinearParams P) {
 
   const Partial p = chunk_stats<DT, STOCH, !STOCH>(row, P.V, c, P.c0, sm);
   const int64_t rid = b * P.R + r;
-  if (threadIdx.x == 0) P.parts[rid * P.C + c] = p;
+  if (threadIdx.x == 0) publish(P.parts + rid * P.C + c, p);
   if (!arrive_last(&P.row_cnt[rid], (unsigned)P.C, sm)) return;
 
   const bool draw = STOCH && (r == P.k);
   const float u = draw ? P.uniforms[b * (P.k + 1) + P.k] : 0.0f;
   const RowStat st = finalize_row<DT, STOCH>(row, P.V, P.parts + rid * P.C, P.C, P.c0, draw, u, sm, rsh);
-  if (threadIdx.x == 0) P.rows[rid] = st;
+  if (threadIdx.x == 0) publish(P.rows + rid, st);
   if (!arrive_last(&P.seq_cnt[b], (unsigned)P.R, sm)) return;
   if (wave_id() == 0) linear_decide<DT, STOCH>(P, b);
 }
@@ -257,13 +257,13 @@ __global__ __launch_bounds__(BLOCK) void linear_residual_kernel(LinearParams P, 
   ResidualWeights<DT> pol{trow, drow, P.V, row_aligned(trow), row_aligned(drow), c0, mc0t, mc0d, izt, izd};
 
   const double s = chunk_weight_sum<DT>(pol, c, sm);
-  if (threadIdx.x == 0) P.res_part[b * P.C + c] = s;
+  if (threadIdx.x == 0) publish(P.res_part + b * P.C + c, s);
   if (!arrive_last(&P.res_cnt[b], (unsigned)P.C, sm)) return;
 
   const float u = P.uniforms[b * (k + 1) + k];
   const double* rp = P.res_part + b * P.C;
   if (wave_id() == 0) {
-    const ChunkPick pk = pick_chunk(P.C, (double)u, [&](int cc) -> double { return rp[cc]; });
+    const ChunkPick pk = pick_chunk(P.C, (double)u, [&](int cc) -> double { return fetch(rp + cc); });
     if (lane_id() == 0) {
       sm.result = pk.c;
       sm.theta = pk.fallback ? INFINITY : pk.theta - pk.before;
@@ -321,12 +321,12 @@ __device__ void tree_walk(const TreeParams& P, int64_t b, unsigned char* smem, B
     const bool bad = (i == 0) ? (p != -1) : (p < 0 || p >= i);
     par_s[i] = (int16_t)(bad ? 0 : p);
     if (bad) err |= SV_ERR_TREE;
-    if (ny[i] < 0) err |= SV_ERR_ROW;
+    if (fetch(ny + i) < 0) err |= SV_ERR_ROW;
     unsigned char m = 0;
     if (i > 0) {
       const int ci = cand[i];
       if (ci < 0 || ci >= P.V) err |= SV_ERR_TOKEN;
-      if (!bad) m = (ci == ny[p]) ? 1 : 0;
+      if (!bad) m = (ci == fetch(ny + p)) ? 1 : 0;
     }
     match_s[i] = m;
   }
@@ -335,9 +335,11 @@ __device__ void tree_walk(const TreeParams& P, int64_t b, unsigned char* smem, B
   for (int bit = 1; bit <= SV_ERR_TREE; bit <<= 1)
     if (__syncthreads_or(err & bit)) all_err |= bit;
 
+  // Depth check and path search (bad parents were replaced by the root above, so
+  // every chain ends; the depth bound is checked whatever other error was found).
   unsigned long long best_key = 0ull;
   int too_deep = 0;
-  if (all_err == 0) {
+  {
     for (int64_t i = threadIdx.x; i < N; i += BLOCK) {
       int64_t j = i, d = 0;
       int acc = 1;
@@ -394,7 +396,7 @@ __device__ void tree_walk(const TreeParams& P, int64_t b, unsigned char* smem, B
       out[j] = cand[node];
       node = par_s[node];
     }
-    out[L] = ny[best];
+    out[L] = fetch(ny + best);
     P.accept_len[b] = L;
     if (P.err_flags) P.err_flags[b] = 0;
   }
@@ -415,12 +417,12 @@ __global__ __launch_bounds__(BLOCK) void tree_kernel(TreeParams P) {
   const char* row = P.logits + (rid * P.V) * E;
 
   const Partial p = chunk_stats<DT, STOCH, !STOCH>(row, P.V, c, P.c0, sm);
-  if (threadIdx.x == 0) P.parts[rid * P.C + c] = p;
+  if (threadIdx.x == 0) publish(P.parts + rid * P.C + c, p);
   if (!arrive_last(&P.row_cnt[rid], (unsigned)P.C, sm)) return;
 
   const float u = STOCH ? P.uniforms[rid] : 0.0f;
   const RowStat st = finalize_row<DT, STOCH>(row, P.V, P.parts + rid * P.C, P.C, P.c0, STOCH, u, sm, rsh);
-  if (threadIdx.x == 0) P.node_y[rid] = st.ok ? st.y : -1;
+  if (threadIdx.x == 0) publish(P.node_y + rid, (int32_t)(st.ok ? st.y : -1));
   if (!arrive_last(&P.tree_cnt[b], (unsigned)P.N, sm)) return;
   tree_walk(P, b, walk_smem, sm);
 }
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(BLOCK) void row_stats_kernel(RowStatsParams P) {
   const int64_t r = lb / P.C, c = lb % P.C;
   const char* row = P.x + (r * P.V) * E;
   const Partial p = chunk_stats<DT, true, true>(row, P.V, c, P.c0, sm);
-  if (threadIdx.x == 0) P.parts[r * P.C + c] = p;
+  if (threadIdx.x == 0) publish(P.parts + r * P.C + c, p);
   if (!arrive_last(&P.row_cnt[r], (unsigned)P.C, sm)) return;
   // argmax needs the ARG partials, the normaliser the SUM partials: both are kept
   const RowStat st = finalize_row<DT, true>(row, P.V, P.parts + r * P.C, P.C, P.c0, false, 0.0f, sm, rsh);
@@ -537,12 +539,16 @@ sv_status dispatch(sv_dtype dt, bool stoch, Args&&... args) {
   return SV_EDTYPE;
 }
 
+enum LinearPhase { PHASE_ACCEPT = 1, PHASE_CORRECT = 2, PHASE_BOTH = 3 };
+
 template <int DT, bool STOCH>
 struct LinearLauncher {
-  static sv_status run(const LinearParams& P, hipStream_t s) {
-    hipLaunchKernelGGL((linear_stats_kernel<DT, STOCH>), dim3((unsigned)P.nblocks), dim3(BLOCK), 0, s, P);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    if (STOCH && P.k > 0) {
+  static sv_status run(const LinearParams& P, int phases, hipStream_t s) {
+    if (phases & PHASE_ACCEPT) {
+      hipLaunchKernelGGL((linear_stats_kernel<DT, STOCH>), dim3((unsigned)P.nblocks), dim3(BLOCK), 0, s, P);
+      if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    }
+    if ((phases & PHASE_CORRECT) && STOCH && P.k > 0) {
       const int64_t nb = P.B * P.C;
       hipLaunchKernelGGL((linear_residual_kernel<DT>), dim3((unsigned)nb), dim3(BLOCK), 0, s, P, nb);
     }
@@ -593,12 +599,12 @@ size_t spec_verify_linear_workspace(int64_t B, int64_t k, int64_t V, sv_dtype dt
   return linear_layout(B, k, V, dtype, mode).total;
 }
 
-sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
-                             sv_dtype dtype, const void* target_logits, const void* draft_logits,
-                             const int32_t* draft_tokens, const float* uniforms, int32_t* accept_len,
-                             int32_t* out_tokens, float* p_target, float* p_draft,
-                             int32_t* err_flags, void* workspace, size_t workspace_bytes,
-                             sv_stream_t stream) {
+static sv_status linear_entry(int phases, sv_mode mode, float temperature, int64_t B, int64_t k,
+                              int64_t V, sv_dtype dtype, const void* target_logits,
+                              const void* draft_logits, const int32_t* draft_tokens,
+                              const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                              float* p_target, float* p_draft, int32_t* err_flags, void* workspace,
+                              size_t workspace_bytes, sv_stream_t stream) {
   if (!dtype_ok(dtype)) return SV_EDTYPE;
   if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
   const bool stoch = (mode == SV_STOCHASTIC);
@@ -637,7 +643,40 @@ sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
   P.nblocks = B * P.R * P.C;
   if (P.nblocks > MAX_BLOCKS) return SV_ELIMIT;
-  return dispatch<LinearLauncher>(dtype, stoch, P, reinterpret_cast<hipStream_t>(stream));
+  return dispatch<LinearLauncher>(dtype, stoch, P, phases, reinterpret_cast<hipStream_t>(stream));
+}
+
+sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                             sv_dtype dtype, const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const float* uniforms, int32_t* accept_len,
+                             int32_t* out_tokens, float* p_target, float* p_draft,
+                             int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                             sv_stream_t stream) {
+  return linear_entry(PHASE_BOTH, mode, temperature, B, k, V, dtype, target_logits, draft_logits,
+                      draft_tokens, uniforms, accept_len, out_tokens, p_target, p_draft, err_flags,
+                      workspace, workspace_bytes, stream);
+}
+
+sv_status spec_verify_linear_accept(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                    sv_dtype dtype, const void* target_logits,
+                                    const void* draft_logits, const int32_t* draft_tokens,
+                                    const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                                    float* p_target, float* p_draft, int32_t* err_flags,
+                                    void* workspace, size_t workspace_bytes, sv_stream_t stream) {
+  return linear_entry(PHASE_ACCEPT, mode, temperature, B, k, V, dtype, target_logits, draft_logits,
+                      draft_tokens, uniforms, accept_len, out_tokens, p_target, p_draft, err_flags,
+                      workspace, workspace_bytes, stream);
+}
+
+sv_status spec_verify_linear_correct(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                     sv_dtype dtype, const void* target_logits,
+                                     const void* draft_logits, const int32_t* draft_tokens,
+                                     const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                                     float* p_target, float* p_draft, int32_t* err_flags,
+                                     void* workspace, size_t workspace_bytes, sv_stream_t stream) {
+  return linear_entry(PHASE_CORRECT, mode, temperature, B, k, V, dtype, target_logits, draft_logits,
+                      draft_tokens, uniforms, accept_len, out_tokens, p_target, p_draft, err_flags,
+                      workspace, workspace_bytes, stream);
 }
 
 size_t spec_verify_tree_workspace(int64_t B, int64_t n_nodes, int64_t V, sv_dtype dtype, sv_mode mode) {

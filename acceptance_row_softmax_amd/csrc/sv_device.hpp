@@ -242,22 +242,67 @@ __device__ inline void block_scan(double v, double& incl, double& excl, BlockScr
 }
 
 // ------------------------------------------------------------------ cross-block handoff
-// Release this block's global writes, then count the block in. Returns true in
-// every thread of the block that arrives last; that block then sees every write
-// the other blocks released before arriving, and resets the counter to zero.
+// Workgroups hand data to each other inside one launch without device-scope
+// fences: on this chip a device-scope fence writes back and invalidates the
+// whole L2 of the XCD, which serialises badly when every workgroup does it.
+// Instead, the data a workgroup hands over is written by its thread 0 with
+// device-coherent stores (they are not left dirty in a non-coherent L2), the
+// thread waits until those stores have completed, and only then counts itself
+// in with a device-scope atomic. The workgroup that arrives last reads the data
+// back with device-coherent loads (they do not hit stale L1/L2 lines).
+template <class T>
+__device__ inline void publish(T* dst, const T& v) {
+  static_assert(sizeof(T) % 4 == 0, "publish works on 4-byte words");
+  if constexpr (sizeof(T) % 8 == 0) {
+    const uint64_t* s = reinterpret_cast<const uint64_t*>(&v);
+    uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 8; ++i)
+      __hip_atomic_store(d + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(&v);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i)
+      __hip_atomic_store(d + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <class T>
+__device__ inline T fetch(const T* src) {
+  static_assert(sizeof(T) % 4 == 0, "fetch works on 4-byte words");
+  T v;
+  if constexpr (sizeof(T) % 8 == 0) {
+    uint64_t* d = reinterpret_cast<uint64_t*>(&v);
+    const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 8; ++i)
+      d[i] = __hip_atomic_load(s + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    uint32_t* d = reinterpret_cast<uint32_t*>(&v);
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i)
+      d[i] = __hip_atomic_load(s + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return v;
+}
+
+// Counts this workgroup in. Returns true in every thread of the workgroup that
+// arrives last (`expected` arrivals); that workgroup resets the counter to zero.
+// Precondition: the only handed-over data of this workgroup was written by its
+// thread 0 with publish().
 __device__ inline bool arrive_last(unsigned* counter, unsigned expected, BlockScratch& sm) {
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // thread 0's stores have completed
+    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (old + 1 == expected);
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.flag = last ? 1 : 0;
   }
   __syncthreads();
-  const bool last = sm.flag != 0;
-  if (last) __threadfence();
-  return last;
+  return sm.flag != 0;
 }
 
 // Logical block index with consecutive indices placed on the same XCD:

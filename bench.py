@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of speculative-decoding verification on one MI355X.
+
+One step = one full verification of one batch (every row streamed, acceptance
+test, first-reject scan, correction / bonus draw, emission). The default
+workload is the draft-target configuration the headline metric is quoted on:
+B=32 sequences, k=4 draft tokens, V=128256, bf16 logits, stochastic at T=0.7.
+
+Inputs are generated on the host from fixed seeds, copied to HBM, and
+replicated into enough rotating copies (together more than 3x the 256 MB
+Infinity Cache) that every step reads its logits from HBM, not from cache.
+Before timing, the GPU result of one step is checked against the CPU oracle;
+the benchmark refuses to report a number if parity fails.
+
+Prints ONE JSON line (rank 0, N=1). Fields beyond the required ones:
+logit_GBps / hbm_frac (algorithmic bytes of a whole step over its time),
+phase_us (live HIP-event durations of each phase), parity.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec + logit GB/s (% HBM peak), V=128256 k=4"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="c2_linear",
+                    choices=["c1_tiny", "c2_linear", "c3_mtp", "c4_medusa_sparse", "c5_medusa_full"])
+    ap.add_argument("--mode", default=None, help="greedy | stochastic (default: the config's own)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def make_workload(cfg, mode, seed):
+    import gen
+    defaults = {"c1_tiny": "stochastic", "c2_linear": "stochastic", "c3_mtp": "stochastic",
+                "c4_medusa_sparse": "greedy", "c5_medusa_full": "greedy"}
+    mode = mode or defaults[cfg]
+    return gen.CONFIGS[cfg](seed, mode)
+
+
+def describe(w):
+    import gen
+    dt = gen.DTYPE_NAMES[w.dtype]
+    if hasattr(w, "k"):
+        return (f"{w.name}: linear draft verification, B={w.B} k={w.k} V={w.V} {dt} logits, "
+                f"{w.mode}" + (f" T={w.temperature}" if w.mode == "stochastic" else ""))
+    return (f"{w.name}: candidate-tree verification, B={w.B} trees of {w.n_nodes} nodes, V={w.V} "
+            f"{dt} logits, {w.mode}" + (f" T={w.temperature}" if w.mode == "stochastic" else ""))
+
+
+def positions(w):
+    return w.B * w.k if hasattr(w, "k") else w.B * (w.n_nodes - 1)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this verification engine runs on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported. Batches shard by sequence with no "
+              "communication, so N GPUs run N independent copies of this benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import acceptance_row_softmax_amd as sv
+    import gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.time()
+    w = make_workload(args.config, args.mode, args.seed)
+    linear = hasattr(w, "k")
+    stoch = w.mode == "stochastic"
+    alg_bytes = w.algorithmic_bytes()
+    print(f"[bench] {describe(w)}; algorithmic bytes/step {alg_bytes} "
+          f"(generated in {time.time() - t_gen:.1f}s)", file=sys.stderr, flush=True)
+
+    def dev_logits(a):
+        a = np.ascontiguousarray(a)
+        if w.dtype == gen.DT_F32:
+            return torch.from_numpy(a).to(dev)
+        t = torch.from_numpy(a.view(np.int16)).to(dev)
+        return t.view(torch.bfloat16 if w.dtype == gen.DT_BF16 else torch.float16)
+
+    copies = args.copies or max(1, math.ceil(3 * INFINITY_CACHE_BYTES / alg_bytes) + 1)
+    if linear:
+        base = {"t": dev_logits(w.target),
+                "d": dev_logits(w.draft) if (stoch and w.k > 0) else None,
+                "x": torch.from_numpy(w.draft_tokens.astype(np.int32)).to(dev) if w.k > 0 else None,
+                "u": torch.from_numpy(w.uniforms.astype(np.float32)).to(dev)}
+    else:
+        base = {"lg": dev_logits(w.logits),
+                "par": torch.from_numpy(np.asarray(w.parent, np.int32)).to(dev),
+                "cand": torch.from_numpy(w.cand.astype(np.int32)).to(dev),
+                "u": torch.from_numpy(w.uniforms.astype(np.float32)).to(dev)}
+    sets = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
+                     for _ in range(copies - 1)]
+    outs = []
+
+    def call(i, phase="both"):
+        s = sets[i]
+        if linear:
+            if len(outs) <= i:
+                outs.append(sv.verify_linear(s["t"], s["d"], s["x"], s["u"], mode=w.mode,
+                                             temperature=w.temperature, phase=phase))
+                return outs[i]
+            return sv.verify_linear(s["t"], s["d"], s["x"], s["u"], mode=w.mode,
+                                    temperature=w.temperature, phase=phase, out=outs[i])
+        r = sv.verify_tree(s["par"], s["cand"], s["lg"], s["u"], w.max_depth, mode=w.mode,
+                           temperature=w.temperature)
+        return r
+
+    # ---------------------------------------------------------------- parity gate
+    import oracle
+    first = call(0)
+    torch.cuda.synchronize()
+    if linear:
+        o = oracle.verify_linear(w.mode, w.temperature, w.target, w.draft if stoch else None,
+                                 w.draft_tokens, w.uniforms, w.V, w.dtype)
+        g_acc = first["accept_len"].cpu().numpy()
+        g_out = first["out_tokens"].cpu().numpy()
+        differ = (g_acc != o["accept_len"]) | np.any(g_out != o["out_tokens"], axis=1)
+    else:
+        sample = list(range(min(w.B, 2 if w.n_nodes > 1000 else w.B)))
+        o = oracle.verify_tree(w.mode, w.temperature, w.parent, w.cand[sample], w.logits[sample],
+                               w.uniforms[sample], w.V, w.dtype, w.max_depth)
+        g_acc = first["accept_len"].cpu().numpy()[sample]
+        g_out = first["out_tokens"].cpu().numpy()[sample]
+        differ = (g_acc != o["accept_len"]) | np.any(g_out != o["out_tokens"], axis=1)
+    bad = differ & (o["near_tie"] == 0)
+    parity = {"checked": int(len(differ)), "exceptions": int(differ.sum()),
+              "near_tie_sequences": int((o["near_tie"] != 0).sum()), "ok": bool(not bad.any())}
+    if not parity["ok"]:
+        print(f"[bench] PARITY FAILED: {parity}", file=sys.stderr, flush=True)
+        sys.exit(1)
+    print(f"[bench] parity vs oracle ok: {parity}", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- warmup
+    for i in range(args.warmup):
+        call(i % copies)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed region
+    K = max(copies, (args.steps // copies) * copies)
+    stream = torch.cuda.current_stream()
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                call(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = K // copies
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gpu_ms = ev0.elapsed_time(ev1)
+        # graph replays must reproduce the eager result
+        if linear:
+            eager = call(0)
+            torch.cuda.synchronize()
+            assert torch.equal(eager["out_tokens"], outs[0]["out_tokens"])
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            call(i % copies)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gpu_ms = None
+    wall_ms = (t1 - t0) * 1e3
+    ms_per_step = wall_ms / K
+
+    # ---------------------------------------------------------------- per-phase durations (HIP events)
+    # The GPU is held by a spin kernel while the host enqueues the steps, so that the
+    # event pairs measure kernel time rather than host launch gaps.
+    phase_us = {}
+    nprof = min(K, 400)
+    cal0, cal1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cal0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    cal1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(cal0.elapsed_time(cal1), 1e-3)
+    hold = int(cycles_per_ms * max(20.0, nprof * 0.1))   # >= 0.1 ms of host time per step
+    if linear:
+        phases = ["accept", "correct"] if (stoch and w.k > 0) else ["accept"]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+               for _ in range(nprof)]
+        torch.cuda._sleep(hold)
+        for n in range(nprof):
+            e = evs[n]
+            e[0].record(stream)
+            for j, ph in enumerate(phases):
+                call(n % copies, phase=ph)
+                e[j + 1].record(stream)
+        torch.cuda.synchronize()
+        for j, ph in enumerate(phases):
+            phase_us[ph] = 1e3 * float(np.mean([evs[n][j].elapsed_time(evs[n][j + 1])
+                                                for n in range(nprof)]))
+        dominant = "linear_stats_kernel"
+        dom_us = phase_us["accept"]
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nprof)]
+        torch.cuda._sleep(hold)
+        for n in range(nprof):
+            evs[n][0].record(stream)
+            call(n % copies)
+            evs[n][1].record(stream)
+        torch.cuda.synchronize()
+        phase_us["tree"] = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        dominant = "tree_kernel"
+        dom_us = phase_us["tree"]
+
+    npos = positions(w)
+    value = npos / (ms_per_step * 1e-3)
+    step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    dom_gbps = alg_bytes / (dom_us * 1e-6) / 1e9
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_rep, t_c0 = 0, time.perf_counter()
+        while True:
+            if linear:
+                oracle.verify_linear(w.mode, w.temperature, w.target, w.draft if stoch else None,
+                                     w.draft_tokens, w.uniforms, w.V, w.dtype)
+                per = w.B * w.k
+                what = f"the full batch ({w.B} sequences)"
+            else:
+                oracle.verify_tree(w.mode, w.temperature, w.parent, w.cand[:1], w.logits[:1],
+                                   w.uniforms[:1], w.V, w.dtype, w.max_depth)
+                per = w.n_nodes - 1
+                what = "one tree of the batch"
+            n_rep += 1
+            el = time.perf_counter() - t_c0
+            if el > args.cpu_seconds:
+                break
+        cpu = {"value": n_rep * per / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{what} x {n_rep} repetitions, {el:.1f}s, single-threaded double-precision "
+                         f"oracle on {platform.processor() or platform.machine()} "
+                         f"({os.cpu_count()} host cores visible)"}
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {gen.DT_F32: "f32", gen.DT_BF16: "bf16", gen.DT_F16: "f16"}[w.dtype],
+        "data": "synthetic (seeded generator; no dataset)",
+        "config": {"workload": describe(w), "global_batch": w.B,
+                   "positions_per_step": npos, "algorithmic_bytes_per_step": alg_bytes,
+                   "input_copies": copies, "graph": not args.no_graph},
+        "logit_GBps": step_gbps,
+        "hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "phase_us": phase_us,
+        "gpu_ms_timed_region": gpu_ms,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dom_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
+                     "traffic": None, "launch_us": dom_us},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -112,6 +112,31 @@ sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t
                              float* p_draft, int32_t* err_flags, void* workspace,
                              size_t workspace_bytes, sv_stream_t stream);
 
+/* The same verification in two phases, for callers that want the accepted lengths
+ * before the correction token (the accepted count is what the host needs for the
+ * next step's lengths, [S-INF]). Both take exactly the arguments of
+ * spec_verify_linear and must be called in this order with the same arguments and
+ * workspace, on the same stream (or after the first completes):
+ *   _accept   streams every row once; writes accept_len, err_flags, p_target,
+ *             p_draft and out_tokens, except out_tokens[b][L] of stochastic sequences
+ *             that rejected a draft (L < k);
+ *   _correct  draws that token from the residual max(0, p_t,L - p_d,L) ([S-ZE]); it
+ *             re-reads only rows t_L and d_L of those sequences. No-op in greedy mode.
+ */
+sv_status spec_verify_linear_accept(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                    sv_dtype dtype, const void* target_logits,
+                                    const void* draft_logits, const int32_t* draft_tokens,
+                                    const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                                    float* p_target, float* p_draft, int32_t* err_flags,
+                                    void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+sv_status spec_verify_linear_correct(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                     sv_dtype dtype, const void* target_logits,
+                                     const void* draft_logits, const int32_t* draft_tokens,
+                                     const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                                     float* p_target, float* p_draft, int32_t* err_flags,
+                                     void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
 /* ---------------------------------------------------------------- candidate trees
  * [M-3]; "Accelerating Sonar through speculation", section "EAGLE" (keep the longest
  * suitable candidate sequence and append one target token).

@@ -13,6 +13,12 @@ import oracle
 TIE_EPS = 1e-6
 PROB_RTOL = 1e-5
 
+# Running totals over every stochastic parity check in the session: an exception
+# is a sequence or tree whose GPU result differs from the oracle's. Each one must
+# be a near tie (an evaluated uniform within TIE_EPS of its threshold in the
+# oracle's arithmetic); their count must stay under 1e-4 of evaluated draws.
+STATS = {"exceptions": 0, "evaluated": 0, "near_tie_sequences": 0, "sequences": 0}
+
 
 def say(msg: str):
     print(f"[gpu-test] {msg}", flush=True)
@@ -52,17 +58,26 @@ def oracle_linear(w: gen.LinearWorkload, seqs=None):
                                 w.draft_tokens[sl], w.uniforms[sl], w.V, w.dtype, TIE_EPS)
 
 
+def _record(differ, near, n_eval):
+    STATS["exceptions"] += int(np.sum(differ))
+    STATS["evaluated"] += int(np.sum(n_eval))
+    STATS["near_tie_sequences"] += int(np.sum(near != 0))
+    STATS["sequences"] += int(len(near))
+
+
 def compare_linear(g, o, stochastic: bool, seqs=None):
-    """Returns (n_near_tie_sequences, n_evaluated_draws). Asserts parity."""
+    """Asserts parity; returns (exceptions, evaluated draws)."""
     sel = np.arange(len(o["accept_len"])) if seqs is None else np.asarray(seqs)
     acc_g = g["accept_len"][sel]
     out_g = g["out_tokens"][sel]
     np.testing.assert_array_equal(g["err_flags"][sel], o["err_flags"])
-    exact = o["near_tie"] == 0
-    bad = np.nonzero(exact & ((acc_g != o["accept_len"]) | np.any(out_g != o["out_tokens"], axis=1)))[0]
+    differ = (acc_g != o["accept_len"]) | np.any(out_g != o["out_tokens"], axis=1)
+    bad = np.nonzero(differ & (o["near_tie"] == 0))[0]
     assert bad.size == 0, (f"{bad.size} sequences differ, first {bad[:5]}: gpu L={acc_g[bad[:5]]} "
                            f"oracle L={o['accept_len'][bad[:5]]} gpu out={out_g[bad[:3]]} "
                            f"oracle out={o['out_tokens'][bad[:3]]}")
+    if not stochastic:
+        assert not np.any(differ), "greedy results must match exactly"
     if stochastic:
         ok = o["err_flags"] == 0
         pt_o, pd_o = o["p_target"][ok], o["p_draft"][ok]
@@ -72,7 +87,8 @@ def compare_linear(g, o, stochastic: bool, seqs=None):
             tiny = np.abs(b) < 1e-37          # below fp32's normal range
             assert np.all((rel <= PROB_RTOL) | tiny), (name, float(rel.max()))
         assert np.all(np.isnan(g["p_target"][sel][~ok]))
-    return int(np.sum(o["near_tie"])), int(np.sum(o["n_eval"]))
+        _record(differ, o["near_tie"], o["n_eval"])
+    return int(np.sum(differ)), int(np.sum(o["n_eval"]))
 
 
 def run_tree(w: gen.TreeWorkload, max_depth=None, **kw):
@@ -99,10 +115,16 @@ def compare_tree(g, o, trees=None):
     sel = np.arange(len(o["accept_len"])) if trees is None else np.asarray(trees)
     np.testing.assert_array_equal(g["err_flags"][sel], o["err_flags"])
     exact = o["near_tie"] == 0
+    differ = np.zeros(len(sel), bool)
     for key in ("accept_len", "path_nodes", "out_tokens"):
         a = g[key][sel]
         b = o[key]
         diff = a != b if a.ndim == 1 else np.any(a != b, axis=1)
+        differ |= diff
         bad = np.nonzero(exact & diff)[0]
         assert bad.size == 0, (key, bad[:5], a[bad[:3]], b[bad[:3]])
-    return int(np.sum(o["near_tie"])), int(np.sum(o["n_eval"]))
+    if np.any(o["n_eval"] > 0):
+        _record(differ, o["near_tie"], o["n_eval"])
+    else:
+        assert not np.any(differ), "greedy results must match exactly"
+    return int(np.sum(differ)), int(np.sum(o["n_eval"]))

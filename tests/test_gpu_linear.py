@@ -1,10 +1,12 @@
 """GPU parity of linear verification: libspecverify through its C ABI against the
 oracle, element by element, on seeded synthetic inputs.
 
-Bar: accept lengths and tokens bit-exact (greedy: always; stochastic: except
-sequences where an evaluated uniform lies within 1e-6 of its threshold, which
-are counted and must stay below 1e-4 of evaluated draws); p_target / p_draft
-within 1e-5 relative of the oracle's double values."""
+Bar: accept lengths and tokens bit-exact. Greedy: always. Stochastic: a
+sequence may differ only if one of its evaluated uniforms lies within 1e-6 of
+its threshold in the oracle's arithmetic (an exception); exceptions are
+counted over the whole session and must stay below 1e-4 of evaluated draws
+(checked by test_zz_exception_rate in test_gpu_zz_summary.py). p_target /
+p_draft within 1e-5 relative of the oracle's double values."""
 import numpy as np
 import pytest
 
@@ -26,14 +28,14 @@ def _check(w, seqs=None):
 def test_c1_tiny_many_sequences(mode):
     # 20000 independent sequences of the tiny configuration (fp32, V=1000, k=4)
     w = gen.c1_tiny(0, mode, B=20000)
-    g, o, near, n_eval = _check(w)
+    g, o, exc, n_eval = _check(w)
     if mode == "stochastic":
         assert n_eval > 50000
-        assert near / n_eval < 1e-4, (near, n_eval)
+        assert exc / n_eval < 1e-4, (exc, n_eval)
         # the acceptance rate is in the expected regime (1 - total variation ~ 0.8)
         assert 0.6 < np.mean(g["accept_len"] >= 1) < 0.95
     else:
-        assert near == 0
+        assert exc == 0
 
 
 @pytest.mark.parametrize("dtype", [gen.DT_F32, gen.DT_BF16, gen.DT_F16])
@@ -122,3 +124,21 @@ def test_deterministic_and_workspace_reuse():
         if a[key] is not None:
             np.testing.assert_array_equal(a[key], c[key])
     G.compare_linear(b, G.oracle_linear(w2), True)
+
+
+def test_two_phase_calls_equal_one_call():
+    import torch
+    import acceptance_row_softmax_amd as sv
+    w = gen.c2_linear(9, B=16)
+    G.say("two-phase accept/correct vs one call")
+    t, d = G.to_dev(w.target, w.dtype), G.to_dev(w.draft, w.dtype)
+    x, u = G.to_dev(w.draft_tokens), G.to_dev(w.uniforms)
+    one = sv.verify_linear(t, d, x, u, mode="stochastic", temperature=w.temperature)
+    two = sv.verify_linear(t, d, x, u, mode="stochastic", temperature=w.temperature, phase="accept")
+    torch.cuda.synchronize()
+    acc_after_phase1 = two["accept_len"].clone()
+    sv.verify_linear(t, d, x, u, mode="stochastic", temperature=w.temperature, phase="correct", out=two)
+    torch.cuda.synchronize()
+    for key in ("accept_len", "out_tokens", "p_target", "p_draft", "err_flags"):
+        assert torch.equal(one[key], two[key]), key
+    assert torch.equal(acc_after_phase1, one["accept_len"])
