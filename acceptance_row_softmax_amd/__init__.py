@@ -24,7 +24,7 @@ from . import _build
 
 SV_GREEDY, SV_STOCHASTIC = 0, 1
 SV_F32, SV_BF16, SV_F16 = 0, 1, 2
-SV_ERR_TOKEN, SV_ERR_ROW, SV_ERR_TREE = 1, 2, 4
+SV_ERR_TOKEN, SV_ERR_ROW, SV_ERR_TREE, SV_ERR_INTERNAL = 1, 2, 4, 8
 SV_MAX_K, SV_MAX_TREE_NODES = 64, 16384
 
 LIB_PATH = _build.LIB
@@ -53,9 +53,6 @@ def lib():
         L.spec_verify_linear.restype = i32
         L.spec_verify_linear.argtypes = [i32, f32, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, sz, vp]
-        for fn in (L.spec_verify_linear_accept, L.spec_verify_linear_correct):
-            fn.restype = i32
-            fn.argtypes = L.spec_verify_linear.argtypes
         L.spec_verify_tree_workspace.restype = sz
         L.spec_verify_tree_workspace.argtypes = [i64, i64, i64, i32, i32]
         L.spec_verify_tree.restype = i32
@@ -71,8 +68,7 @@ def lib():
     return _lib
 
 
-EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_linear_accept",
-            "spec_verify_linear_correct", "spec_verify_tree_workspace",
+EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_tree_workspace",
             "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
             "spec_workspace_clear", "spec_verify_status_string")
 
@@ -128,15 +124,16 @@ def _stream(stream=None):
 
 
 class Workspace:
-    """Device workspace cache keyed by (device, kind, shape). Buffers are
-    zero-filled at allocation; calls leave their control words zero."""
+    """One zero-filled device workspace per (device, stream), grown on demand.
+    Every call that completes leaves it all zeros, so it serves every entry point
+    and shape; calls on one stream never overlap, calls on two streams get two."""
 
     def __init__(self):
         self._bufs = {}
 
-    def get(self, device, key, nbytes: int):
+    def get(self, device, stream, nbytes: int):
         torch = _torch()
-        k = (str(device), key)
+        k = (str(device), stream.value)
         buf = self._bufs.get(k)
         if buf is None or buf.numel() < nbytes:
             buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -149,13 +146,14 @@ _WS = Workspace()
 
 def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic",
                   temperature: float = 1.0, *, with_probs: bool = True, err_flags: bool = True,
-                  workspace=None, stream=None, phase: str = "both", out=None):
+                  workspace=None, stream=None, out=None):
     """Verify B linear drafts of k tokens.
 
     target [B][k+1][V], draft [B][k][V] (same dtype; draft unused in greedy mode),
     draft_tokens [B][k] int32, uniforms [B][k+1] float32 (stochastic only).
     Returns a dict of device tensors: accept_len [B], out_tokens [B][k+1],
     p_target / p_draft [B][k] (stochastic, if with_probs), err_flags [B].
+    ``out`` may hold preallocated tensors of those names and shapes.
     """
     torch = _torch()
     stoch = mode == "stochastic"
@@ -194,16 +192,14 @@ def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic
             out["p_target"] = torch.empty((B, k), dtype=torch.float32, device=dev)
             out["p_draft"] = torch.empty((B, k), dtype=torch.float32, device=dev)
     L = lib()
-    fn = {"both": L.spec_verify_linear, "accept": L.spec_verify_linear_accept,
-          "correct": L.spec_verify_linear_correct}[phase]
     mcode = SV_STOCHASTIC if stoch else SV_GREEDY
     nbytes = L.spec_verify_linear_workspace(B, k, V, dt, mcode)
-    ws = workspace if workspace is not None else _WS.get(dev, ("linear", B, k, V, dt, mcode), nbytes)
-    st = fn(mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft), _ptr(draft_tokens),
+    s = _stream(stream)
+    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    st = L.spec_verify_linear(mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft), _ptr(draft_tokens),
             _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("p_target")),
-            _ptr(out.get("p_draft")), _ptr(out.get("err_flags")), _ptr(ws), ws.numel(),
-            _stream(stream))
-    _check(st, "spec_verify_linear" + ("" if phase == "both" else "_" + phase))
+            _ptr(out.get("p_draft")), _ptr(out.get("err_flags")), _ptr(ws), ws.numel(), s)
+    _check(st, "spec_verify_linear")
     return out
 
 
@@ -249,11 +245,12 @@ def verify_tree(parent, cand_tokens, logits, uniforms, max_depth: int, mode: str
     L = lib()
     mcode = SV_STOCHASTIC if stoch else SV_GREEDY
     nbytes = L.spec_verify_tree_workspace(B, N, V, dt, mcode)
-    ws = workspace if workspace is not None else _WS.get(dev, ("tree", B, N, V, dt, mcode), nbytes)
+    s = _stream(stream)
+    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
     st = L.spec_verify_tree(mcode, float(temperature), B, N, V, dt, _ptr(parent), stride,
                             _ptr(cand_tokens), _ptr(logits), _ptr(uniforms), int(max_depth),
                             _ptr(acc), _ptr(path) if max_depth > 0 else None, _ptr(out), _ptr(ef),
-                            _ptr(ws), ws.numel(), _stream(stream))
+                            _ptr(ws), ws.numel(), s)
     _check(st, "spec_verify_tree")
     return {"accept_len": acc, "path_nodes": path, "out_tokens": out, "err_flags": ef}
 
@@ -272,8 +269,9 @@ def row_stats(x, temperature: float = 1.0, *, workspace=None, stream=None):
     ef = torch.empty(rows, dtype=torch.int32, device=dev)
     L = lib()
     nbytes = L.spec_row_stats_workspace(rows, V, dt)
-    ws = workspace if workspace is not None else _WS.get(dev, ("rows", rows, V, dt), nbytes)
+    s = _stream(stream)
+    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
     st = L.spec_row_stats(dt, float(temperature), rows, V, _ptr(x), _ptr(m), _ptr(lse), _ptr(am),
-                          _ptr(ef), _ptr(ws), ws.numel(), _stream(stream))
+                          _ptr(ef), _ptr(ws), ws.numel(), s)
     _check(st, "spec_row_stats")
     return {"max": m, "lse": lse, "argmax": am, "err_flags": ef}

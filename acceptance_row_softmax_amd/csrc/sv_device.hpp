@@ -52,13 +52,13 @@ struct RowStat {
 };
 
 // ------------------------------------------------------------------ loads
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ inline float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
-__device__ inline float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 template <int DT>
-__device__ inline float load_elem(const char* row, int64_t i) {
+__device__ __forceinline__ float load_elem(const char* row, int64_t i) {
   if constexpr (DT == DT_F32) {
     return reinterpret_cast<const float*>(row)[i];
   } else if constexpr (DT == DT_BF16) {
@@ -69,7 +69,7 @@ __device__ inline float load_elem(const char* row, int64_t i) {
 }
 
 template <int DT>
-__device__ inline void decode_unit(const uint4 v, float (&x)[DTraits<DT>::W]) {
+__device__ __forceinline__ void decode_unit(const uint4 v, float (&x)[DTraits<DT>::W]) {
   if constexpr (DT == DT_F32) {
     x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
     x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
@@ -84,8 +84,9 @@ __device__ inline void decode_unit(const uint4 v, float (&x)[DTraits<DT>::W]) {
 
 // Load unit `unit` of a row: W consecutive elements starting at unit*W.
 // Elements at or past V read as -inf (zero weight, never a maximum).
+// Used for single units (the scan's final unit); chunks use load_chunk.
 template <int DT>
-__device__ inline void load_unit(const char* row, int64_t V, int64_t unit, bool aligned,
+__device__ __forceinline__ void load_unit(const char* row, int64_t V, int64_t unit, bool aligned,
                                  float (&x)[DTraits<DT>::W]) {
   constexpr int W = DTraits<DT>::W;
   constexpr int E = DTraits<DT>::E;
@@ -99,15 +100,111 @@ __device__ inline void load_unit(const char* row, int64_t V, int64_t unit, bool 
   }
 }
 
-__device__ inline bool row_aligned(const char* row) { return (reinterpret_cast<uintptr_t>(row) & 15u) == 0; }
+// A chunk's raw 16-byte words for one thread (UNROLL units), as loaded.
+struct ChunkRaw {
+  uint4 v[UNROLL];
+};
+
+// Issue this thread's UNROLL vector loads of a chunk (units unit0 + j*BLOCK + tid)
+// without waiting: addresses are clamped to units lying entirely inside the row.
+// Rows that do not start on a 16-byte boundary load nothing here (decode_chunk
+// reads them element by element).
+template <int DT>
+__device__ __forceinline__ void load_chunk_raw(const char* row, int64_t V, int64_t unit0, bool aligned,
+                                               ChunkRaw& raw) {
+  constexpr int W = DTraits<DT>::W;
+  constexpr int E = DTraits<DT>::E;
+  const int64_t nfull = V / W;                 // units lying entirely inside the row
+  if (aligned && nfull > 0) {
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int64_t u = unit0 + j * BLOCK + threadIdx.x;
+      const int64_t uc = (u < nfull) ? u : nfull - 1;
+      raw.v[j] = *reinterpret_cast<const uint4*>(row + uc * (W * E));
+    }
+  }
+}
+
+// Decode a chunk loaded by load_chunk_raw; units (partly) past V and rows that do
+// not start on a 16-byte boundary are read element by element here (entries past
+// V read as -inf).
+template <int DT>
+__device__ __forceinline__ void decode_chunk(const char* row, int64_t V, int64_t unit0, bool aligned,
+                                             const ChunkRaw& raw, float (&x)[UNROLL][DTraits<DT>::W]) {
+  constexpr int W = DTraits<DT>::W;
+  const int64_t nfull = V / W;
+  if (aligned && nfull > 0) {
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      decode_unit<DT>(raw.v[j], x[j]);
+      const int64_t u = unit0 + j * BLOCK + threadIdx.x;
+      if (u >= nfull) {
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+          const int64_t i = u * W + e;
+          x[j][e] = (i < V) ? load_elem<DT>(row, i) : -INFINITY;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int64_t u = unit0 + j * BLOCK + threadIdx.x;
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        const int64_t i = u * W + e;
+        const float v = load_elem<DT>(row, i < V ? i : V - 1);
+        x[j][e] = (i < V) ? v : -INFINITY;
+      }
+    }
+  }
+}
+
+// Decode unit j of this thread from a raw chunk (see decode_chunk).
+template <int DT>
+__device__ __forceinline__ void decode_unit_at(const char* row, int64_t V, int64_t unit0, bool aligned,
+                                               const ChunkRaw& raw, int j, float (&x)[DTraits<DT>::W]) {
+  constexpr int W = DTraits<DT>::W;
+  const int64_t nfull = V / W;
+  const int64_t u = unit0 + j * BLOCK + threadIdx.x;
+  if (aligned && nfull > 0) {
+    decode_unit<DT>(raw.v[j], x);
+    if (u >= nfull) {
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        const int64_t i = u * W + e;
+        x[e] = (i < V) ? load_elem<DT>(row, i) : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      const int64_t i = u * W + e;
+      const float v = load_elem<DT>(row, i < V ? i : V - 1);
+      x[e] = (i < V) ? v : -INFINITY;
+    }
+  }
+}
+
+// Load and decode this thread's UNROLL units of a chunk, every vector load issued
+// before any result is used.
+template <int DT>
+__device__ __forceinline__ void load_chunk(const char* row, int64_t V, int64_t unit0, bool aligned,
+                                           float (&x)[UNROLL][DTraits<DT>::W]) {
+  ChunkRaw raw;
+  load_chunk_raw<DT>(row, V, unit0, aligned, raw);
+  decode_chunk<DT>(row, V, unit0, aligned, raw, x);
+}
+
+__device__ __forceinline__ bool row_aligned(const char* row) { return (reinterpret_cast<uintptr_t>(row) & 15u) == 0; }
 
 // ------------------------------------------------------------------ arithmetic
-__device__ inline float softmax_weight(float x, float c0, float mc0) {
+__device__ __forceinline__ float softmax_weight(float x, float c0, float mc0) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c0, -mc0));
 }
 
 template <int W>
-__device__ inline float pairwise_sum(const float (&w)[W]) {
+__device__ __forceinline__ float pairwise_sum(const float (&w)[W]) {
   if constexpr (W == 8) {
     return ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
   } else {
@@ -117,37 +214,37 @@ __device__ inline float pairwise_sum(const float (&w)[W]) {
 
 // m*c0 in fp32 as used for the chunk's weights; 0 for an empty (-inf) chunk so
 // that its -inf entries weigh exp2(-inf) = 0 instead of NaN.
-__device__ inline float chunk_mc0(float m, float c0) { return (m == -INFINITY) ? 0.0f : m * c0; }
+__device__ __forceinline__ float chunk_mc0(float m, float c0) { return (m == -INFINITY) ? 0.0f : m * c0; }
 
 // ------------------------------------------------------------------ reductions
-__device__ inline int lane_id() { return threadIdx.x & 63; }
-__device__ inline int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-__device__ inline double wave_sum(double v) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ inline float wave_max(float v) {
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
-__device__ inline int wave_max_int(int v) {
+__device__ __forceinline__ int wave_max_int(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
   return v;
 }
-__device__ inline int wave_sum_int(int v) {
+__device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 // (value, index): larger value wins, lower index on equal values.
-__device__ inline void argmax_combine(float& m, int& i, float m2, int i2) {
+__device__ __forceinline__ void argmax_combine(float& m, int& i, float m2, int i2) {
   if (m2 > m || (m2 == m && i2 < i)) { m = m2; i = i2; }
 }
-__device__ inline void wave_argmax(float& m, int& i) {
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(m, o);
@@ -157,7 +254,7 @@ __device__ inline void wave_argmax(float& m, int& i) {
 }
 
 // Inclusive prefix sum over the 64 lanes (lane order), Hillis-Steele.
-__device__ inline double wave_incl_scan(double v) {
+__device__ __forceinline__ double wave_incl_scan(double v) {
   const int lane = lane_id();
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -176,7 +273,7 @@ struct BlockScratch {
   double theta;
 };
 
-__device__ inline double block_sum(double v, BlockScratch& sm) {
+__device__ __forceinline__ double block_sum(double v, BlockScratch& sm) {
   v = wave_sum(v);
   if (lane_id() == 0) sm.d[wave_id()] = v;
   __syncthreads();
@@ -186,7 +283,7 @@ __device__ inline double block_sum(double v, BlockScratch& sm) {
   __syncthreads();
   return r;
 }
-__device__ inline float block_max(float v, BlockScratch& sm) {
+__device__ __forceinline__ float block_max(float v, BlockScratch& sm) {
   v = wave_max(v);
   if (lane_id() == 0) sm.f[wave_id()] = v;
   __syncthreads();
@@ -196,7 +293,7 @@ __device__ inline float block_max(float v, BlockScratch& sm) {
   __syncthreads();
   return r;
 }
-__device__ inline int block_max_int(int v, BlockScratch& sm) {
+__device__ __forceinline__ int block_max_int(int v, BlockScratch& sm) {
   v = wave_max_int(v);
   if (lane_id() == 0) sm.i[wave_id()] = v;
   __syncthreads();
@@ -206,7 +303,7 @@ __device__ inline int block_max_int(int v, BlockScratch& sm) {
   __syncthreads();
   return r;
 }
-__device__ inline int block_sum_int(int v, BlockScratch& sm) {
+__device__ __forceinline__ int block_sum_int(int v, BlockScratch& sm) {
   v = wave_sum_int(v);
   if (lane_id() == 0) sm.i[wave_id()] = v;
   __syncthreads();
@@ -216,7 +313,7 @@ __device__ inline int block_sum_int(int v, BlockScratch& sm) {
   __syncthreads();
   return r;
 }
-__device__ inline void block_argmax(float& m, int& idx, BlockScratch& sm) {
+__device__ __forceinline__ void block_argmax(float& m, int& idx, BlockScratch& sm) {
   wave_argmax(m, idx);
   if (lane_id() == 0) { sm.f[wave_id()] = m; sm.i[wave_id()] = idx; }
   __syncthreads();
@@ -229,7 +326,7 @@ __device__ inline void block_argmax(float& m, int& idx, BlockScratch& sm) {
   idx = ri;
 }
 // Block-wide inclusive and exclusive prefix sums in thread order.
-__device__ inline void block_scan(double v, double& incl, double& excl, BlockScratch& sm) {
+__device__ __forceinline__ void block_scan(double v, double& incl, double& excl, BlockScratch& sm) {
   const double wi = wave_incl_scan(v);
   const double prev = __shfl_up(wi, 1);
   if (lane_id() == 63) sm.d[wave_id()] = wi;
@@ -241,74 +338,70 @@ __device__ inline void block_scan(double v, double& incl, double& excl, BlockScr
   excl = (lane_id() == 0) ? off : off + prev;
 }
 
-// ------------------------------------------------------------------ cross-block handoff
-// Workgroups hand data to each other inside one launch without device-scope
-// fences: on this chip a device-scope fence writes back and invalidates the
-// whole L2 of the XCD, which serialises badly when every workgroup does it.
-// Instead, the data a workgroup hands over is written by its thread 0 with
-// device-coherent stores (they are not left dirty in a non-coherent L2), the
-// thread waits until those stores have completed, and only then counts itself
-// in with a device-scope atomic. The workgroup that arrives last reads the data
-// back with device-coherent loads (they do not hit stale L1/L2 lines).
-template <class T>
-__device__ inline void publish(T* dst, const T& v) {
-  static_assert(sizeof(T) % 4 == 0, "publish works on 4-byte words");
-  if constexpr (sizeof(T) % 8 == 0) {
-    const uint64_t* s = reinterpret_cast<const uint64_t*>(&v);
-    uint64_t* d = reinterpret_cast<uint64_t*>(dst);
-#pragma unroll
-    for (unsigned i = 0; i < sizeof(T) / 8; ++i)
-      __hip_atomic_store(d + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(&v);
-    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
-#pragma unroll
-    for (unsigned i = 0; i < sizeof(T) / 4; ++i)
-      __hip_atomic_store(d + i, s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
+// ------------------------------------------------------------------ cross-workgroup records
+// Workgroups hand data to each other inside one launch without fences and
+// without atomics: a record is an array of 8-byte words, each holding a 32-bit
+// value and the 32-bit tag of the call that wrote it. The writer stores the words
+// with device-coherent 8-byte stores and moves on; the record's one reader polls
+// them with device-coherent loads until every word carries the call's tag, then
+// clears the words (tag 0). A word is written and read whole, so a matching tag
+// means its value is this call's. Every call draws a fresh odd tag, and every
+// record is cleared by its reader, so neither an earlier call's words nor those of
+// an earlier replay of the same captured graph can ever match.
+//
+// A workgroup only ever waits for records of workgroups with a lower dispatch
+// index, which were dispatched before it and are resident or finished; waits are
+// bounded all the same (about 0.2 s), and a timeout is reported as an error.
+constexpr int SPIN_LIMIT = 1 << 18;
 
 template <class T>
-__device__ inline T fetch(const T* src) {
-  static_assert(sizeof(T) % 4 == 0, "fetch works on 4-byte words");
-  T v;
-  if constexpr (sizeof(T) % 8 == 0) {
-    uint64_t* d = reinterpret_cast<uint64_t*>(&v);
-    const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
+struct RecWords {
+  static_assert(sizeof(T) % 4 == 0, "records are made of 4-byte words");
+  static constexpr int N = sizeof(T) / 4;
+};
+
+template <class T>
+__device__ __forceinline__ void put_rec(uint64_t* dst, const T& v, uint32_t tag) {
+  uint32_t w[RecWords<T>::N];
+  __builtin_memcpy(w, &v, sizeof(T));
 #pragma unroll
-    for (unsigned i = 0; i < sizeof(T) / 8; ++i)
-      d[i] = __hip_atomic_load(s + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    uint32_t* d = reinterpret_cast<uint32_t*>(&v);
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
-#pragma unroll
-    for (unsigned i = 0; i < sizeof(T) / 4; ++i)
-      d[i] = __hip_atomic_load(s + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return v;
+  for (int i = 0; i < RecWords<T>::N; ++i)
+    __hip_atomic_store(dst + i, ((uint64_t)tag << 32) | w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Counts this workgroup in. Returns true in every thread of the workgroup that
-// arrives last (`expected` arrivals); that workgroup resets the counter to zero.
-// Precondition: the only handed-over data of this workgroup was written by its
-// thread 0 with publish().
-__device__ inline bool arrive_last(unsigned* counter, unsigned expected, BlockScratch& sm) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // thread 0's stores have completed
-    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = (old + 1 == expected);
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.flag = last ? 1 : 0;
+// Waits until all words of the record carry `tag`; false on timeout (v undefined).
+template <class T>
+__device__ __forceinline__ bool get_rec(const uint64_t* src, T& v, uint32_t tag) {
+  uint32_t w[RecWords<T>::N];
+  for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < RecWords<T>::N; ++i) {
+      const uint64_t x = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && ((uint32_t)(x >> 32) == tag);
+      w[i] = (uint32_t)x;
+    }
+    if (ok) {
+      __builtin_memcpy(&v, w, sizeof(T));
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(2);
   }
-  __syncthreads();
-  return sm.flag != 0;
+  return false;
+}
+
+// Clears a consumed record (its reader does this once it has read it).
+template <class T>
+__device__ __forceinline__ void clear_rec(uint64_t* dst) {
+#pragma unroll
+  for (int i = 0; i < RecWords<T>::N; ++i)
+    __hip_atomic_store(dst + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Logical block index with consecutive indices placed on the same XCD:
 // workgroups are dispatched round-robin over the 8 XCDs, so hardware block b runs
 // on XCD b % 8. This makes the chunks of one row share that XCD's L2.
-__device__ inline int64_t xcd_logical_block(int64_t hw, int64_t nblocks) {
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t hw, int64_t nblocks) {
   constexpr int64_t NX = 8;
   const int64_t xcd = hw % NX, local = hw / NX;
   const int64_t base = nblocks / NX, rem = nblocks % NX;
@@ -316,28 +409,27 @@ __device__ inline int64_t xcd_logical_block(int64_t hw, int64_t nblocks) {
 }
 
 // ------------------------------------------------------------------ chunk statistics
-// Streams chunk `c` of a row and returns (in every thread) its partial:
-// max with lowest index (if ARG), and the weight sum relative to fl32(m*c0) (if SUM).
+// Reduces one chunk, loaded raw by load_chunk_raw, to its partial (same value in
+// every thread): max with lowest index (if ARG), and the weight sum relative to
+// fl32(m*c0) (if SUM). Units are decoded on the fly in each pass, so only the raw
+// words stay live across the block reduction.
 template <int DT, bool SUM, bool ARG>
-__device__ inline Partial chunk_stats(const char* row, int64_t V, int64_t c, float c0, BlockScratch& sm) {
+__device__ __forceinline__ Partial reduce_chunk(const char* row, int64_t V, int64_t unit0, bool aligned,
+                                                const ChunkRaw& raw, float c0, BlockScratch& sm) {
   constexpr int W = DTraits<DT>::W;
   const int tid = threadIdx.x;
-  const bool aligned = row_aligned(row);
-  const int64_t unit0 = c * UNITS_PER_CHUNK;
-  float x[UNROLL][W];
-#pragma unroll
-  for (int j = 0; j < UNROLL; ++j) load_unit<DT>(row, V, unit0 + j * BLOCK + tid, aligned, x[j]);
-
   float best = -INFINITY;
   int pos = INT_SENTINEL;
 #pragma unroll
   for (int j = 0; j < UNROLL; ++j) {
+    float x[W];
+    decode_unit_at<DT>(row, V, unit0, aligned, raw, j, x);
 #pragma unroll
     for (int e = 0; e < W; ++e) {
       if constexpr (ARG) {
-        if (x[j][e] > best) { best = x[j][e]; pos = j * W + e; }
+        if (x[e] > best) { best = x[e]; pos = j * W + e; }
       } else {
-        best = fmaxf(best, x[j][e]);
+        best = fmaxf(best, x[e]);
       }
     }
   }
@@ -360,8 +452,9 @@ __device__ inline Partial chunk_stats(const char* row, int64_t V, int64_t c, flo
 #pragma unroll
     for (int j = 0; j < UNROLL; ++j) {
       float w[W];
+      decode_unit_at<DT>(row, V, unit0, aligned, raw, j, w);
 #pragma unroll
-      for (int e = 0; e < W; ++e) w[e] = softmax_weight(x[j][e], c0, mc0);
+      for (int e = 0; e < W; ++e) w[e] = softmax_weight(w[e], c0, mc0);
       acc += (double)pairwise_sum<W>(w);
     }
     p.s = block_sum(acc, sm);
@@ -383,6 +476,13 @@ struct SoftmaxWeights {
 #pragma unroll
     for (int e = 0; e < DTraits<DT>::W; ++e) w[e] = softmax_weight(x[e], c0, mc0);
   }
+  __device__ void chunk(int64_t unit0, float (&w)[UNROLL][DTraits<DT>::W]) const {
+    load_chunk<DT>(row, V, unit0, aligned, w);
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j)
+#pragma unroll
+      for (int e = 0; e < DTraits<DT>::W; ++e) w[j][e] = softmax_weight(w[j][e], c0, mc0);
+  }
 };
 
 // Weight policy for the residual max(0, p_t - p_d) of a target/draft row pair:
@@ -394,28 +494,37 @@ struct ResidualWeights {
   int64_t V;
   bool taligned, daligned;
   float c0, mc0t, mc0d, izt, izd;
+  __device__ float weight(float xt, float xd) const {
+    const float pt = softmax_weight(xt, c0, mc0t);
+    const float pd = softmax_weight(xd, c0, mc0d) * izd;
+    return fmaxf(0.0f, __builtin_fmaf(pt, izt, -pd));
+  }
   __device__ void unit(int64_t u, float (&w)[DTraits<DT>::W]) const {
     float xt[DTraits<DT>::W], xd[DTraits<DT>::W];
     load_unit<DT>(trow, V, u, taligned, xt);
     load_unit<DT>(drow, V, u, daligned, xd);
 #pragma unroll
-    for (int e = 0; e < DTraits<DT>::W; ++e) {
-      const float pt = softmax_weight(xt[e], c0, mc0t);
-      const float pd = softmax_weight(xd[e], c0, mc0d) * izd;
-      w[e] = fmaxf(0.0f, __builtin_fmaf(pt, izt, -pd));
-    }
+    for (int e = 0; e < DTraits<DT>::W; ++e) w[e] = weight(xt[e], xd[e]);
+  }
+  __device__ void chunk(int64_t unit0, float (&w)[UNROLL][DTraits<DT>::W]) const {
+    float xd[UNROLL][DTraits<DT>::W];
+    load_chunk<DT>(trow, V, unit0, taligned, w);
+    load_chunk<DT>(drow, V, unit0, daligned, xd);
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j)
+#pragma unroll
+      for (int e = 0; e < DTraits<DT>::W; ++e) w[j][e] = weight(w[j][e], xd[j][e]);
   }
 };
 
 // Sum of a policy's weights over chunk c (fixed order, same unit sums as the scan).
 template <int DT, class Policy>
-__device__ inline double chunk_weight_sum(const Policy& pol, int64_t c, BlockScratch& sm) {
+__device__ __forceinline__ double chunk_weight_sum(const Policy& pol, int64_t c, BlockScratch& sm) {
   constexpr int W = DTraits<DT>::W;
   const int64_t unit0 = c * UNITS_PER_CHUNK;
   double acc = 0.0;
   float w[UNROLL][W];
-#pragma unroll
-  for (int j = 0; j < UNROLL; ++j) pol.unit(unit0 + j * BLOCK + threadIdx.x, w[j]);
+  pol.chunk(unit0, w);
 #pragma unroll
   for (int j = 0; j < UNROLL; ++j) acc += (double)pairwise_sum<W>(w[j]);
   return block_sum(acc, sm);
@@ -426,16 +535,16 @@ __device__ inline double chunk_weight_sum(const Policy& pol, int64_t c, BlockScr
 // such element (theta at or past the chunk total), the last element of positive
 // weight. Returns -1 if the chunk has no positive weight. Same value in all threads.
 template <int DT, class Policy>
-__device__ inline int64_t chunk_invcdf(const Policy& pol, int64_t c, double theta, BlockScratch& sm) {
+__device__ __forceinline__ int64_t chunk_invcdf(const Policy& pol, int64_t c, double theta, BlockScratch& sm) {
   constexpr int W = DTraits<DT>::W;
   const int tid = threadIdx.x;
   const int64_t unit0 = c * UNITS_PER_CHUNK;
   float us[UNROLL];
+  {
+    float w[UNROLL][W];
+    pol.chunk(unit0, w);
 #pragma unroll
-  for (int j = 0; j < UNROLL; ++j) {
-    float w[W];
-    pol.unit(unit0 + j * BLOCK + tid, w);
-    us[j] = pairwise_sum<W>(w);
+    for (int j = 0; j < UNROLL; ++j) us[j] = pairwise_sum<W>(w[j]);
   }
 
   // 1) which group of BLOCK consecutive units holds the crossing
@@ -501,6 +610,9 @@ __device__ inline int64_t chunk_invcdf(const Policy& pol, int64_t c, double thet
 }
 
 // ------------------------------------------------------------------ chunk selection (wave 0)
+constexpr int MAX_CHUNKS = 256;            // 4 chunks per lane of wave 0
+constexpr int CHUNKS_PER_LANE = MAX_CHUNKS / 64;
+
 // Given per-chunk weights W_c (c < C) held by lane-contiguous ranges, pick the
 // first chunk whose inclusive prefix exceeds u * total. Runs in wave 0 only;
 // result fields are valid in all lanes of wave 0.
@@ -512,21 +624,21 @@ struct ChunkPick {
   bool fallback;  // no chunk crossed: c is the last chunk of positive weight
 };
 
-constexpr int MAX_CHUNKS = 256;            // 4 chunks per lane of wave 0
-constexpr int CHUNKS_PER_LANE = MAX_CHUNKS / 64;
-
-template <class WeightOf>
-__device__ inline ChunkPick pick_chunk(int C, double u, WeightOf weight_of) {
-  const int lane = lane_id();
+// Each lane of wave 0 holds the weights of chunks c_lo .. c_lo+CHUNKS_PER_LANE-1
+// (c_lo = lane * ceil(C/64); zero past its range), in wl[].
+__device__ __forceinline__ void lane_chunk_range(int C, int& c_lo, int& c_hi) {
   const int per = (C + 63) / 64;
-  const int c_lo = min(C, lane * per), c_hi = min(C, c_lo + per);
-  double wl[CHUNKS_PER_LANE];
+  c_lo = min(C, lane_id() * per);
+  c_hi = min(C, c_lo + per);
+}
+
+__device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&wl)[CHUNKS_PER_LANE]) {
+  const int lane = lane_id();
+  int c_lo, c_hi;
+  lane_chunk_range(C, c_lo, c_hi);
   double local = 0.0;
 #pragma unroll
-  for (int q = 0; q < CHUNKS_PER_LANE; ++q) {
-    wl[q] = (c_lo + q < c_hi) ? weight_of(c_lo + q) : 0.0;
-    local += wl[q];
-  }
+  for (int q = 0; q < CHUNKS_PER_LANE; ++q) local += wl[q];
   const double incl = wave_incl_scan(local);
   const double prev = __shfl_up(incl, 1);
   const double excl = (lane == 0) ? 0.0 : prev;

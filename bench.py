@@ -14,7 +14,7 @@ the benchmark refuses to report a number if parity fails.
 
 Prints ONE JSON line (rank 0, N=1). Fields beyond the required ones:
 logit_GBps / hbm_frac (algorithmic bytes of a whole step over its time),
-phase_us (live HIP-event durations of each phase), parity.
+kernel_us (live HIP-event duration of the step's one kernel launch), parity.
 """
 from __future__ import annotations
 
@@ -121,15 +121,15 @@ def main():
                      for _ in range(copies - 1)]
     outs = []
 
-    def call(i, phase="both"):
+    def call(i):
         s = sets[i]
         if linear:
             if len(outs) <= i:
                 outs.append(sv.verify_linear(s["t"], s["d"], s["x"], s["u"], mode=w.mode,
-                                             temperature=w.temperature, phase=phase))
+                                             temperature=w.temperature))
                 return outs[i]
             return sv.verify_linear(s["t"], s["d"], s["x"], s["u"], mode=w.mode,
-                                    temperature=w.temperature, phase=phase, out=outs[i])
+                                    temperature=w.temperature, out=outs[i])
         r = sv.verify_tree(s["par"], s["cand"], s["lg"], s["u"], w.max_depth, mode=w.mode,
                            temperature=w.temperature)
         return r
@@ -201,10 +201,10 @@ def main():
     wall_ms = (t1 - t0) * 1e3
     ms_per_step = wall_ms / K
 
-    # ---------------------------------------------------------------- per-phase durations (HIP events)
-    # The GPU is held by a spin kernel while the host enqueues the steps, so that the
-    # event pairs measure kernel time rather than host launch gaps.
-    phase_us = {}
+    # ---------------------------------------------------------------- kernel duration (HIP events)
+    # A step is one kernel launch. The GPU is held by a spin kernel while the host
+    # enqueues the steps, so that each event pair brackets the kernel itself rather
+    # than host launch gaps.
     nprof = min(K, 400)
     cal0, cal1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cal0.record(stream)
@@ -213,35 +213,16 @@ def main():
     torch.cuda.synchronize()
     cycles_per_ms = 1_000_000 / max(cal0.elapsed_time(cal1), 1e-3)
     hold = int(cycles_per_ms * max(20.0, nprof * 0.1))   # >= 0.1 ms of host time per step
-    if linear:
-        phases = ["accept", "correct"] if (stoch and w.k > 0) else ["accept"]
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
-               for _ in range(nprof)]
-        torch.cuda._sleep(hold)
-        for n in range(nprof):
-            e = evs[n]
-            e[0].record(stream)
-            for j, ph in enumerate(phases):
-                call(n % copies, phase=ph)
-                e[j + 1].record(stream)
-        torch.cuda.synchronize()
-        for j, ph in enumerate(phases):
-            phase_us[ph] = 1e3 * float(np.mean([evs[n][j].elapsed_time(evs[n][j + 1])
-                                                for n in range(nprof)]))
-        dominant = "linear_stats_kernel"
-        dom_us = phase_us["accept"]
-    else:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(nprof)]
-        torch.cuda._sleep(hold)
-        for n in range(nprof):
-            evs[n][0].record(stream)
-            call(n % copies)
-            evs[n][1].record(stream)
-        torch.cuda.synchronize()
-        phase_us["tree"] = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        dominant = "tree_kernel"
-        dom_us = phase_us["tree"]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nprof)]
+    torch.cuda._sleep(hold)
+    for n in range(nprof):
+        evs[n][0].record(stream)
+        call(n % copies)
+        evs[n][1].record(stream)
+    torch.cuda.synchronize()
+    dom_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    dominant = "linear_kernel" if linear else "tree_kernel"
 
     npos = positions(w)
     value = npos / (ms_per_step * 1e-3)
@@ -290,7 +271,7 @@ def main():
                    "input_copies": copies, "graph": not args.no_graph},
         "logit_GBps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
-        "phase_us": phase_us,
+        "kernel_us": dom_us,
         "gpu_ms_timed_region": gpu_ms,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dom_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,

@@ -45,10 +45,12 @@
  *    once the stream reaches that point. Concurrent calls need distinct workspaces.
  *  - Workspace: device memory of at least the size the *_workspace function
  *    returns, 256-byte aligned, zero-filled before its first use (for instance with
- *    spec_workspace_clear). Every call leaves its control words zero again, so a
- *    workspace can be reused without clearing by calls of the same entry point and
- *    shape (B, k or n_nodes, V, dtype, mode); clear it again before a call of another
- *    shape, since the control words sit at offsets that depend on the shape.
+ *    spec_workspace_clear). Workgroups of one launch pass results to each other
+ *    through records in it; every call tags its records with a fresh value and each
+ *    record is cleared by the workgroup that reads it, so a call that ends without
+ *    SV_ERR_INTERNAL leaves the workspace all zeros again, ready for any entry point
+ *    and shape. One workspace serves one launch at a time; after SV_ERR_INTERNAL,
+ *    clear it again before reuse.
  *  - Errors detectable on the host return a non-zero status before anything is
  *    enqueued. Data errors seen on the device set bits in err_flags (if given) and
  *    give that sequence accept_len = -1 and -1 tokens:
@@ -57,6 +59,10 @@
  *                          non-finite softmax normaliser (NaN or +inf logits)
  *      bit2 SV_ERR_TREE    parent[0] != -1, parent[i] outside [0, i), or a node
  *                          deeper than max_depth
+ *      bit3 SV_ERR_INTERNAL a wait between workgroups of the launch gave up (after
+ *                          2^18 polls, a fraction of a second: only if the GPU did
+ *                          not run the launch's workgroups in dispatch order, or a
+ *                          concurrent call shared the workspace); outputs are not valid
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -82,7 +88,7 @@ typedef enum {
 typedef enum { SV_GREEDY = 0, SV_STOCHASTIC = 1 } sv_mode;
 typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
 
-enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4 };
+enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4, SV_ERR_INTERNAL = 8 };
 
 /* Limits: k <= SV_MAX_K drafts per sequence; n_nodes <= SV_MAX_TREE_NODES; V < 2^31. */
 enum { SV_MAX_K = 64, SV_MAX_TREE_NODES = 16384 };
@@ -102,6 +108,9 @@ enum { SV_MAX_K = 64, SV_MAX_TREE_NODES = 16384 };
  *                               p_d,i(x_i) for every i < k (NaN on a data error)
  *   err_flags      [B]          optional data-error bits (see above)
  * Greedy mode accepts x_i iff x_i = argmax(target row i) and emits argmax(target row L).
+ * One kernel launch; every logit row is read once, and in SV_STOCHASTIC rows t_L and
+ * d_L of sequences that rejected a draft (L < k) are read a second time for the
+ * residual draw ([S-ZE]).
  */
 size_t spec_verify_linear_workspace(int64_t B, int64_t k, int64_t V, sv_dtype dtype, sv_mode mode);
 
@@ -111,31 +120,6 @@ sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t
                              int32_t* accept_len, int32_t* out_tokens, float* p_target,
                              float* p_draft, int32_t* err_flags, void* workspace,
                              size_t workspace_bytes, sv_stream_t stream);
-
-/* The same verification in two phases, for callers that want the accepted lengths
- * before the correction token (the accepted count is what the host needs for the
- * next step's lengths, [S-INF]). Both take exactly the arguments of
- * spec_verify_linear and must be called in this order with the same arguments and
- * workspace, on the same stream (or after the first completes):
- *   _accept   streams every row once; writes accept_len, err_flags, p_target,
- *             p_draft and out_tokens, except out_tokens[b][L] of stochastic sequences
- *             that rejected a draft (L < k);
- *   _correct  draws that token from the residual max(0, p_t,L - p_d,L) ([S-ZE]); it
- *             re-reads only rows t_L and d_L of those sequences. No-op in greedy mode.
- */
-sv_status spec_verify_linear_accept(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
-                                    sv_dtype dtype, const void* target_logits,
-                                    const void* draft_logits, const int32_t* draft_tokens,
-                                    const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
-                                    float* p_target, float* p_draft, int32_t* err_flags,
-                                    void* workspace, size_t workspace_bytes, sv_stream_t stream);
-
-sv_status spec_verify_linear_correct(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
-                                     sv_dtype dtype, const void* target_logits,
-                                     const void* draft_logits, const int32_t* draft_tokens,
-                                     const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
-                                     float* p_target, float* p_draft, int32_t* err_flags,
-                                     void* workspace, size_t workspace_bytes, sv_stream_t stream);
 
 /* ---------------------------------------------------------------- candidate trees
  * [M-3]; "Accelerating Sonar through speculation", section "EAGLE" (keep the longest

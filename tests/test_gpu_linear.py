@@ -126,19 +126,28 @@ def test_deterministic_and_workspace_reuse():
     G.compare_linear(b, G.oracle_linear(w2), True)
 
 
-def test_two_phase_calls_equal_one_call():
+def test_workspace_left_zero_and_shared_across_shapes():
+    """Every record is cleared by its reader: after each call the workspace is all
+    zeros again, so one workspace serves calls of different shapes and modes."""
     import torch
     import acceptance_row_softmax_amd as sv
-    w = gen.c2_linear(9, B=16)
-    G.say("two-phase accept/correct vs one call")
-    t, d = G.to_dev(w.target, w.dtype), G.to_dev(w.draft, w.dtype)
-    x, u = G.to_dev(w.draft_tokens), G.to_dev(w.uniforms)
-    one = sv.verify_linear(t, d, x, u, mode="stochastic", temperature=w.temperature)
-    two = sv.verify_linear(t, d, x, u, mode="stochastic", temperature=w.temperature, phase="accept")
-    torch.cuda.synchronize()
-    acc_after_phase1 = two["accept_len"].clone()
-    sv.verify_linear(t, d, x, u, mode="stochastic", temperature=w.temperature, phase="correct", out=two)
-    torch.cuda.synchronize()
-    for key in ("accept_len", "out_tokens", "p_target", "p_draft", "err_flags"):
-        assert torch.equal(one[key], two[key]), key
-    assert torch.equal(acc_after_phase1, one["accept_len"])
+    G.say("one workspace, several shapes; zero after every call")
+    wa = gen.c2_linear(9, B=16)
+    wb = gen.linear_draft_target(71, 1, 7, 3, 20000, gen.DT_F16, 2.0, 0.5, "greedy", 1.0, "ws-b")
+    wc = gen.linear_draft_target(72, 2, 5, 0, 3000, gen.DT_F32, 2.0, 0.5, "stochastic", 1.3, "ws-c")
+    L = sv.lib()
+    # the generator's dtype codes are the library's
+    need = max(L.spec_verify_linear_workspace(w.B, w.k, w.V, w.dtype,
+                                              sv.SV_STOCHASTIC if w.mode == "stochastic" else sv.SV_GREEDY)
+               for w in (wa, wb, wc))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for w in (wa, wb, wc, wa):
+        t = G.to_dev(w.target, w.dtype)
+        d = G.to_dev(w.draft, w.dtype) if (w.mode == "stochastic" and w.k > 0) else None
+        x = G.to_dev(w.draft_tokens) if w.k > 0 else None
+        u = G.to_dev(w.uniforms)
+        g = sv.verify_linear(t, d, x, u, mode=w.mode, temperature=w.temperature, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, w.name
+        got = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
+        G.compare_linear(got, G.oracle_linear(w), w.mode == "stochastic")
