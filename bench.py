@@ -47,7 +47,56 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device copies of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="print the hash of the kernel sources that measured traffic is keyed on")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources and the header, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("acceptance_row_softmax_amd/csrc/specverify.hip", "acceptance_row_softmax_amd/csrc/sv_device.hpp",
+                "acceptance_row_softmax_amd/_build.py", "include/specverify.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per launch from the committed counter summaries under profiles/
+    (lines "bench-traffic: {json}"), if one was taken on this workload with the
+    current kernel sources; else None."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    src = kernel_source_hash()
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(pdir, name), encoding="utf-8") as f:
+            for ln in f:
+                if not ln.startswith("bench-traffic: "):
+                    continue
+                rec = json.loads(ln[len("bench-traffic: "):])
+                if rec.get("workload") == workload_key and rec.get("source_sha256") == src:
+                    return rec
+    return None
+
+
+def copy_probe(mib: int):
+    """Ten plain device-to-device copies of `mib` MiB: each reads and writes exactly
+    that many bytes, which scales the HBM byte counters of a counter run."""
+    import torch
+    n = mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 10}), flush=True)
 
 
 def make_workload(cfg, mode, seed):
@@ -74,6 +123,9 @@ def positions(w):
 
 def main():
     args = parse()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this verification engine runs on one GPU; --gpus {args.gpus} "
@@ -91,6 +143,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     t_gen = time.time()
     w = make_workload(args.config, args.mode, args.seed)
     linear = hasattr(w, "k")
@@ -191,20 +246,24 @@ def main():
             torch.cuda.synchronize()
             assert torch.equal(eager["out_tokens"], outs[0]["out_tokens"])
     else:
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        ev0.record(stream)
         for i in range(K):
             call(i % copies)
+        ev1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        gpu_ms = None
+        gpu_ms = ev0.elapsed_time(ev1)
     wall_ms = (t1 - t0) * 1e3
     ms_per_step = wall_ms / K
 
     # ---------------------------------------------------------------- kernel duration (HIP events)
-    # A step is one kernel launch. The GPU is held by a spin kernel while the host
-    # enqueues the steps, so that each event pair brackets the kernel itself rather
-    # than host launch gaps.
+    # A step is one kernel launch, so the launch duration is the timed region's
+    # event time over its K launches (launch gaps included: an upper bound).
+    # Second figure: one event pair per launch, with the GPU held by a spin kernel
+    # while the host enqueues, so that host launch gaps stay out of the pairs.
     nprof = min(K, 400)
     cal0, cal1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cal0.record(stream)
@@ -221,13 +280,15 @@ def main():
         call(n % copies)
         evs[n][1].record(stream)
     torch.cuda.synchronize()
-    dom_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    pair_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    dom_us = gpu_ms * 1e3 / K
     dominant = "linear_kernel" if linear else "tree_kernel"
 
     npos = positions(w)
     value = npos / (ms_per_step * 1e-3)
     step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
     dom_gbps = alg_bytes / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(f"{args.config}/{w.mode}/seed{args.seed}")
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
@@ -271,11 +332,13 @@ def main():
                    "input_copies": copies, "graph": not args.no_graph},
         "logit_GBps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
-        "kernel_us": dom_us,
+        "kernel_us": pair_us,
         "gpu_ms_timed_region": gpu_ms,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dom_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
-                     "traffic": None, "launch_us": dom_us},
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "traffic_detail": traffic, "launch_us": dom_us,
+                     "algorithmic_bytes": alg_bytes},
         "cpu_baseline": cpu,
         "parity": parity,
     }
