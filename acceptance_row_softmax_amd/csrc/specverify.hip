@@ -1,25 +1,32 @@
 // libspecverify: speculative-decoding verification kernels for gfx950 and the C ABI
 // declared in include/specverify.h.
 //
-// One launch per call. The grid's workgroups are, in dispatch order:
-//  * streaming workgroups, one per (row, 16 KiB chunk), sequence by sequence:
-//    each streams its chunk once (max / argmax / exp-sum), writes its partial as a
-//    tagged record and is done. The workgroup of a row's last chunk combines the
-//    row (max, normaliser, argmax) and, for the bonus row k in stochastic mode,
-//    draws the extra token; the one finishing a sequence's last row runs the
-//    acceptance test for all k positions at once (one lane per position), the
-//    first-reject scan, and emits the tokens;
-//  * in stochastic mode, one residual workgroup per (sequence, chunk): for
-//    sequences that rejected at L < k it sums max(0, p_t,L - p_d,L) over its chunk;
-//    the sequence's last residual workgroup picks the chunk holding u*S and runs the
-//    LDS block scan there (inverse CDF) for the correction token;
-// Trees and row statistics use the same streaming workgroups; the workgroup
-// finishing a tree's last node runs the accepted-path search in LDS.
+// Linear drafts: one launch per call. Its workgroups hold four independent waves;
+// in dispatch order the waves are
+//  * streaming waves, one per (row, 8 KiB chunk), rows in position order (the
+//    target/draft rows of position 0 of every sequence, then position 1, ...,
+//    the target rows after the last draft at the end). A streaming wave reduces its
+//    chunk to a partial (max, argmax or softmax sum) and writes it as a tagged
+//    record. The last wave to finish a row (an atomic counter per row) combines
+//    the row: max, argmax, normaliser, the probability of the draft token at that
+//    row, and, for the row after the last draft, the bonus draw.
+//  * per sequence, the second row combined of a (target, draft) pair runs that
+//    position's acceptance test and records the outcome in the sequence's state
+//    word; the wave whose update fixes the first rejected position L hands the
+//    rows t_L, d_L to the residual waves (or, if no draft is rejected, releases
+//    the bonus token);
+//  * residual waves (stochastic mode), one per (sequence, chunk), dispatched after
+//    all streaming waves: each sums max(0, p_t,L - p_d,L) over its chunk; the last
+//    of a sequence picks the chunk holding u*S and draws the correction token by
+//    an inverse-CDF scan inside it;
+//  * the last event of a sequence (an atomic counter per sequence) writes all of
+//    its outputs.
+// No wave ever waits for work that is dispatched after it except the residual
+// waves (which wait for the decision of streaming waves dispatched before them).
 //
-// Workgroups hand results to each other through tagged records in the workspace.
-// Every call carries a fresh tag; a record's single reader polls until it sees
-// the call's tag and then clears the record, so a workspace is all zeros again
-// after every call that completed without an internal error.
+// Trees: a streaming launch of the same kind computes every node's token, then one
+// workgroup per tree searches the accepted path in LDS. Row statistics: the
+// streaming launch alone.
 //
 // Sources: "Accelerating Sonar through speculation" (sections "Spekulatives
 // Decoding", "Ziel-Entwurf", "MTP", "EAGLE"); "Speculative-Decoding, LLM推理的加速 /
@@ -40,159 +47,234 @@ namespace {
 constexpr double LN2 = 0.69314718055994530941723212145818;
 constexpr double LOG2E = 1.4426950408889634073599246810019;
 
-// Record slots (8-byte tagged words) per record type.
-constexpr int PART_WORDS = RecWords<Partial>::N;   // 4
+constexpr int PART_WORDS = RecWords<Partial>::N;   // 6
+// Every atomic counter sits on its own 128-byte line: counters that share a line
+// serialise each other's atomics.
+constexpr int64_t CSTRIDE = 32;                     // in 32-bit words
+constexpr int64_t SSTRIDE = 16;                     // in 64-bit words
 constexpr int ROW_WORDS = RecWords<RowStat>::N;    // 8
 
-struct Decision {   // what the residual workgroups of a sequence need
-  int L;            // first rejected position
-  int pending;      // 1 if the correction token is drawn from the residual
-  float Mt, Md;     // row maxima of t_L, d_L
-  double Zt, Zd;    // normalisers of t_L, d_L (relative to M*c0)
+// What the residual waves of a sequence need. kind 0: no draft rejected (the bonus
+// token is final); 1: draw from the residual of rows t_L, d_L; 2: a draft was
+// rejected but its rows are unusable (data error, no draw).
+struct Decision {
+  int L;
+  int kind;
+  float Mt, Md;
+  double Zt, Zd;
 };
-constexpr int DEC_WORDS = RecWords<Decision>::N;    // 8
+constexpr int DEC_WORDS = RecWords<Decision>::N;   // 8
 
 struct ResPart {
   double s;
 };
-constexpr int RES_WORDS = RecWords<ResPart>::N;     // 2
+constexpr int RES_WORDS = RecWords<ResPart>::N;    // 2
 
-// ------------------------------------------------------------------ row finalisation
-// Wave 0 waits for the C tagged partials of one row, clears them and combines them; then,
-// optionally, the whole workgroup draws a token from softmax(row / T) with
-// uniform u. Result valid in all threads; ok = -1 if a wait timed out.
-template <int DT, bool SUM>
-__device__ __forceinline__ RowStat finalize_row(const char* row, int64_t V, const uint64_t* parts, int C,
-                                                float c0, uint32_t tag, bool draw, float u,
-                                                BlockScratch& sm, RowStat& sh) {
-  if (wave_id() == 0) {
-    int c_lo, c_hi;
-    lane_chunk_range(C, c_lo, c_hi);
-    Partial pl[CHUNKS_PER_LANE];
-    bool ok = true;
+struct Token {
+  int y;        // -1 no token (data error), -2 a wait timed out
+};
+
+struct Probs {  // p_t,i(x_i) and p_d,i(x_i) of one position (stochastic)
+  float pt, pd;
+};
+constexpr int PROB_WORDS = RecWords<Probs>::N;    // 2
+
+// Sequence state word: bit i (i < k) position i decided, bit 32+i position i
+// rejected, BONUS_BIT the bonus row has been drawn.
+constexpr uint64_t BONUS_BIT = 1ull << 31;
+
+// First rejected position if the state fixes it, k if every draft is accepted and
+// the bonus row is drawn, else -1.
+__device__ __forceinline__ int settled_L(uint64_t s, int k) {
+  const uint64_t mk = (1ull << k) - 1;
+  const uint64_t dec = s & mk, rej = (s >> 32) & mk;
+  const int fr = rej ? __builtin_ctzll(rej) : k;
+  const uint64_t und = ~dec & mk;
+  const int fu = und ? __builtin_ctzll(und) : k;
+  if (fr < k) return fu > fr ? fr : -1;
+  return (fu == k && (s & BONUS_BIT)) ? k : -1;
+}
+
+template <class T>
+__device__ __forceinline__ T bcast(T v) { return __shfl(v, 0); }
+
+// ------------------------------------------------------------------ row combine
+// Chunk partials of one row, lane-strided (lane l holds chunks l + 64 t).
+struct RowParts {
+  float m[MAX_ROUNDS];
+  int idx[MAX_ROUNDS];
+  double s[MAX_ROUNDS];
+  bool got;    // every partial arrived (same in every lane)
+  bool xin;    // some chunk holds the draft token
+  float xv;    // its logit
+};
+
+// Reads the C partials of a row and clears them.
+__device__ __forceinline__ RowParts read_parts(uint64_t* parts, int C, uint32_t tag) {
+  const int lane = lane_id();
+  RowParts rp;
+  bool got = true;
+  int xin = 0;
+  float xv = 0.0f;
 #pragma unroll
-    for (int q = 0; q < CHUNKS_PER_LANE; ++q) {
-      pl[q].m = -INFINITY;
-      pl[q].idx = INT_SENTINEL;
-      pl[q].s = 0.0;
-      if (c_lo + q < c_hi) ok = get_rec(parts + (int64_t)(c_lo + q) * PART_WORDS, pl[q], tag) && ok;
-    }
-#pragma unroll
-    for (int q = 0; q < CHUNKS_PER_LANE; ++q)
-      if (c_lo + q < c_hi) clear_rec<Partial>(const_cast<uint64_t*>(parts) + (int64_t)(c_lo + q) * PART_WORDS);
-    const bool all_ok = __ballot(!ok) == 0ull;
-    float M = -INFINITY;
-    int arg = INT_SENTINEL;
-#pragma unroll
-    for (int q = 0; q < CHUNKS_PER_LANE; ++q) argmax_combine(M, arg, pl[q].m, pl[q].idx);
-    wave_argmax(M, arg);
-    double Z = 0.0;
-    double wl[CHUNKS_PER_LANE];
-    const double Mc0 = (double)M * (double)c0;
-    if constexpr (SUM) {
-      double local = 0.0;
-#pragma unroll
-      for (int q = 0; q < CHUNKS_PER_LANE; ++q) {
-        wl[q] = (pl[q].m == -INFINITY) ? 0.0 : pl[q].s * exp2((double)chunk_mc0(pl[q].m, c0) - Mc0);
-        local += wl[q];
-      }
-      Z = wave_sum(local);
-    }
-    bool rowok = SUM ? ((M > -INFINITY) && __builtin_isfinite(Z) && Z > 0.0) : (M > -INFINITY);
-    if (lane_id() == 0) {
-      sh.M = M;
-      sh.argmax = (M > -INFINITY && arg != INT_SENTINEL) ? arg : -1;
-      sh.Z = Z;
-      sh.ok = all_ok ? (rowok ? 1 : 0) : -1;
-      sh.y = SUM ? -1 : sh.argmax;
-    }
-    if constexpr (SUM) {
-      if (draw && all_ok && rowok) {
-        const ChunkPick pk = pick_chunk(C, (double)u, wl);
-        // the chosen chunk's max, from the lane holding it
-        float mine = 0.0f;
-#pragma unroll
-        for (int q = 0; q < CHUNKS_PER_LANE; ++q)
-          if (c_lo + q == pk.c) mine = pl[q].m;
-        const int per = (C + 63) / 64;
-        const float mstar = __shfl(mine, (pk.c >= 0 ? pk.c : 0) / per);
-        if (lane_id() == 0) {
-          sm.result = pk.c;
-          const float mc0 = chunk_mc0(mstar, c0);
-          sm.f[0] = mc0;
-          // threshold in the chunk's own units (weights relative to its mc0)
-          sm.theta = (pk.c < 0) ? 0.0 : (pk.fallback ? INFINITY : (pk.theta - pk.before) * exp2(Mc0 - (double)mc0));
-        }
-      } else if (lane_id() == 0) {
-        sm.result = -1;
-      }
-    }
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    Partial p;
+    p.m = -INFINITY;
+    p.idx = INT_SENTINEL;
+    p.s = 0.0;
+    p.xin = 0;
+    p.xv = 0.0f;
+    const int c = t * WAVE + lane;
+    if (c < C) got = get_rec(parts + (int64_t)c * PART_WORDS, p, tag) && got;
+    rp.m[t] = p.m;
+    rp.idx[t] = p.idx;
+    rp.s[t] = p.s;
+    if (p.xin) { xin = 1; xv = p.xv; }
   }
-  __syncthreads();
-  RowStat st = sh;
+  const unsigned long long xm = __ballot(xin != 0);
+  rp.xin = xm != 0ull;
+  rp.xv = __shfl(xv, xm ? first_lane(xm) : 0);
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    const int c = t * WAVE + lane;
+    if (c < C) clear_rec<Partial>(parts + (int64_t)c * PART_WORDS);
+  }
+  rp.got = __ballot(!got) == 0ull;
+  return rp;
+}
+
+struct RowSums {
+  float M;
+  int argmax;   // -1 if no entry exceeds -inf
+  double Z;     // relative to 2^(M*c0); 0 if not computed
+};
+
+// Combines the partials; wl receives each chunk's weight relative to 2^(M*c0).
+template <bool SUM>
+__device__ __forceinline__ RowSums row_sums(const RowParts& rp, float c0, double (&wl)[MAX_ROUNDS]) {
+  float M = -INFINITY;
+  int arg = INT_SENTINEL;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) argmax_combine(M, arg, rp.m[t], rp.idx[t]);
+  wave_argmax(M, arg);
+  RowSums r;
+  r.M = M;
+  r.argmax = (M > -INFINITY && arg != INT_SENTINEL) ? arg : -1;
+  r.Z = 0.0;
   if constexpr (SUM) {
-    if (draw && st.ok == 1) {
-      const int cstar = (int)sm.result;
-      const double th = sm.theta;
-      const float mc0 = sm.f[0];
-      __syncthreads();
-      if (cstar >= 0) {
-        SoftmaxWeights<DT> pol{row, V, row_aligned(row), c0, mc0};
-        st.y = (int)chunk_invcdf<DT>(pol, cstar, th, sm);
-      } else {
-        st.y = -1;
-      }
-    }
-  }
-  __syncthreads();
-  return st;
-}
-
-// Streams one chunk and writes its partial record (thread 0).
-template <int DT, bool SUM, bool ARG>
-__device__ __forceinline__ void stream_chunk(const char* row, int64_t V, int64_t c, float c0,
-                                             uint64_t* part_slot, uint32_t tag, BlockScratch& sm) {
-  const int64_t unit0 = c * UNITS_PER_CHUNK;
-  const bool aligned = row_aligned(row);
-  ChunkRaw raw;
-  load_chunk_raw<DT>(row, V, unit0, aligned, raw);
-  const Partial p = reduce_chunk<DT, SUM, ARG>(row, V, unit0, aligned, raw, c0, sm);
-  if (threadIdx.x == 0) put_rec(part_slot, p, tag);
-}
-
-// Inverse-CDF draw from softmax(row / T) that streams the whole row itself (every
-// chunk's weight sum relative to the row max, then the scan in the chosen chunk).
-// Used only when no partials are at hand (the residual of two rows that are equal
-// up to rounding). LDS: up to MAX_CHUNKS doubles in `wsum`.
-template <int DT>
-__device__ __forceinline__ int draw_row_streamed(const char* row, int64_t V, int C, float M, float c0, float u,
-                                                 double* wsum, BlockScratch& sm) {
-  SoftmaxWeights<DT> pol{row, V, row_aligned(row), c0, M * c0};
-  for (int c = 0; c < C; ++c) {
-    const double w = chunk_weight_sum<DT>(pol, c, sm);
-    if (threadIdx.x == 0) wsum[c] = w;
-  }
-  __syncthreads();
-  if (wave_id() == 0) {
-    int c_lo, c_hi;
-    lane_chunk_range(C, c_lo, c_hi);
-    double wl[CHUNKS_PER_LANE];
+    const double Mc0 = (double)M * (double)c0;
+    double local = 0.0;
 #pragma unroll
-    for (int q = 0; q < CHUNKS_PER_LANE; ++q) wl[q] = (c_lo + q < c_hi) ? wsum[c_lo + q] : 0.0;
-    const ChunkPick pk = pick_chunk(C, (double)u, wl);
-    if (lane_id() == 0) {
-      sm.result = pk.c;
-      sm.theta = pk.fallback ? INFINITY : pk.theta - pk.before;
+    for (int t = 0; t < MAX_ROUNDS; ++t) {
+      wl[t] = (rp.m[t] == -INFINITY) ? 0.0 : rp.s[t] * pow2_neg((double)chunk_mc0(rp.m[t], c0) - Mc0);
+      local += wl[t];
     }
+    r.Z = wave_sum(local);
   }
-  __syncthreads();
-  const int cstar = (int)sm.result;
-  const double th = sm.theta;
-  __syncthreads();
-  return cstar >= 0 ? (int)chunk_invcdf<DT>(pol, cstar, th, sm) : -1;
+  return r;
 }
 
-// ------------------------------------------------------------------ linear
+// Inverse-CDF draw from softmax(row / T) with uniform u, given the row's chunk
+// partials: pick the chunk, then scan inside it. -1 if the row has no weight.
+template <int DT>
+__device__ __forceinline__ int softmax_draw(const char* row, int64_t V, int C, float c0, float u,
+                                            const RowParts& rp, const RowSums& rs, const double (&wl)[MAX_ROUNDS]) {
+  constexpr int W = DTraits<DT>::W;
+  const ChunkPick pk = pick_chunk(C, (double)u, wl);
+  if (pk.c < 0) return -1;
+  const int tc = pk.c / WAVE, lc = pk.c % WAVE;
+  float mm = rp.m[0];
+#pragma unroll
+  for (int t = 1; t < MAX_ROUNDS; ++t) if (t == tc) mm = rp.m[t];
+  const float mstar = __shfl(mm, lc);
+  const float mc0 = chunk_mc0(mstar, c0);
+  // threshold in the chunk's own units (weights relative to its mc0)
+  const double th = pk.fallback ? (double)INFINITY
+                                : (pk.theta - pk.before) * exp2((double)rs.M * (double)c0 - (double)mc0);
+  Raw r;
+  const Chunk k = load_chunk<DT>(row, V, pk.c, r);
+  SoftmaxW sw;
+  sw.c0 = c0;
+  sw.mc0 = mc0;
+  const int64_t y = chunk_invcdf<DT, false>(k, r, r, th, sw);
+  return (int)y;
+}
+
+// The same draw when no partials are at hand: the wave streams the row once to
+// build them (used only for the residual of two rows equal up to rounding).
+template <int DT>
+__device__ __forceinline__ int softmax_draw_streamed(const char* row, int64_t V, int C, float c0, float u) {
+  const int lane = lane_id();
+  RowParts rp;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    rp.m[t] = -INFINITY;
+    rp.idx[t] = INT_SENTINEL;
+    rp.s[t] = 0.0;
+  }
+#pragma unroll 1
+  for (int c = 0; c < C; ++c) {
+    const Partial p = chunk_partial<DT, true, false>(row, V, c, c0);
+    const int t = c / WAVE;
+#pragma unroll
+    for (int q = 0; q < MAX_ROUNDS; ++q)
+      if (q == t && lane == c % WAVE) {
+        rp.m[q] = p.m;
+        rp.s[q] = p.s;
+      }
+  }
+  rp.got = true;
+  double wl[MAX_ROUNDS];
+  const RowSums rs = row_sums<true>(rp, c0, wl);
+  if (!(rs.Z > 0.0) || !__builtin_isfinite(rs.Z)) return -1;
+  return softmax_draw<DT>(row, V, C, c0, u, rp, rs, wl);
+}
+
+__device__ __forceinline__ ResidW make_residw(const Decision& d, float c0) {
+  ResidW rw;
+  rw.c0 = c0;
+  rw.mc0t = d.Mt * c0;
+  rw.mc0d = d.Md * c0;
+  // 1 / sum_v exp2(x_v*c0 - fl32(M*c0)), from Z = sum_v exp2(x_v*c0 - M*c0)
+  rw.izt = (float)(1.0 / (d.Zt * exp2((double)d.Mt * (double)c0 - (double)rw.mc0t)));
+  rw.izd = (float)(1.0 / (d.Zd * exp2((double)d.Md * (double)c0 - (double)rw.mc0d)));
+  return rw;
+}
+
+// Residual sum over chunk c of rows t_L, d_L (same value in every lane).
+template <int DT>
+__device__ __forceinline__ double residual_chunk_sum(const char* trow, const char* drow, int64_t V, int64_t c,
+                                                     const ResidW& rw) {
+  constexpr int W = DTraits<DT>::W;
+  Raw rt, rd;
+  load_chunk<DT>(trow, V, c, rt);
+  load_chunk<DT>(drow, V, c, rd);
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < CU; ++j) {
+    float xt[W], xd[W];
+    unit_values<DT>(rt, j, xt);
+    unit_values<DT>(rd, j, xd);
+#pragma unroll
+    for (int e = 0; e < W; ++e) xt[e] = rw(xt[e], xd[e]);
+    s += (double)pairwise_sum<W>(xt);
+  }
+  return wave_sum(s);
+}
+
+// Inverse CDF of the residual inside chunk c.
+template <int DT>
+__device__ __forceinline__ int residual_chunk_draw(const char* trow, const char* drow, int64_t V, int64_t c,
+                                                   const ResidW& rw, double th) {
+  constexpr int W = DTraits<DT>::W;
+  Raw rt, rd;
+  const Chunk kt = load_chunk<DT>(trow, V, c, rt);
+  load_chunk<DT>(drow, V, c, rd);
+  const int64_t y = chunk_invcdf<DT, true>(kt, rt, rd, th, rw);
+  return (int)y;
+}
+
+// ------------------------------------------------------------------ linear drafts
 struct LinearParams {
   const char* target;
   const char* draft;
@@ -203,259 +285,373 @@ struct LinearParams {
   float* p_target;
   float* p_draft;
   int32_t* err_flags;
-  uint64_t* parts;      // [B][R][C] Partial records
-  uint64_t* rows;       // [B][R]    RowStat records
-  uint64_t* dec;        // [B]       Decision records
-  uint64_t* res;        // [B][C]    ResPart records
+  uint64_t* parts;      // [RQ][C]  Partial records
+  uint64_t* rows;       // [RQ]     RowStat records
+  uint64_t* dec;        // [B]      Decision records
+  uint64_t* res;        // [B][C]   ResPart records
+  uint64_t* tok;        // [B]      Token records
+  uint64_t* prob;       // [B][k]   Probs records (stochastic)
+  uint32_t* row_cnt;    // [RQ]     chunks done per row
+  uint32_t* pair_cnt;   // [B][k]   rows combined per (target, draft) pair
+  uint64_t* state;      // [B]      sequence state words
+  uint32_t* fin;        // [B]      events per sequence
+  uint32_t* res_cnt;    // [B]      residual waves done per sequence
+  uint32_t* errw;       // [B]      error bits per sequence
   int64_t B, k, V;
-  int R, C;
+  int C, CP, R;         // chunks per row, streaming waves per row (C rounded up to 4), rows per sequence
   float c0;
-  uint32_t tag;         // this call's record tag
-  int64_t n_stream;     // streaming workgroups (B * R * C)
-  int64_t n_resid;      // residual workgroups (B * C in stochastic mode, else 0)
+  uint32_t tag;
+  int64_t n_stream;     // streaming waves (RQ * CP)
+  int64_t n_resid;      // residual waves (B * C in stochastic mode with k > 0, else 0)
 };
 
-// Row slots per sequence. Stochastic: slot 0 = target row k (bonus), then the
-// pairs (t_0, d_0), (t_1, d_1), ...; greedy: slot i = target row i.
+// Row order. Stochastic: q = i*2B + 2b + which for i < k (which 0 target, 1
+// draft), q = 2kB + b for target row k. Greedy: q = i*B + b.
+template <bool STOCH>
+__device__ __forceinline__ int64_t row_q(const LinearParams& P, int64_t b, int64_t i, int which) {
+  if (!STOCH) return i * P.B + b;
+  if (i < P.k) return i * 2 * P.B + 2 * b + which;
+  return 2 * P.k * P.B + b;
+}
+
 template <int DT, bool STOCH>
-__device__ __forceinline__ const char* slot_ptr(const LinearParams& P, int64_t b, int slot) {
+__device__ __forceinline__ const char* row_ptr(const LinearParams& P, int64_t b, int64_t i, int which) {
   constexpr int E = DTraits<DT>::E;
-  if (!STOCH) return P.target + ((b * (P.k + 1) + slot) * P.V) * E;
-  if (slot == 0) return P.target + ((b * (P.k + 1) + P.k) * P.V) * E;
-  const int64_t i = (slot - 1) >> 1;
-  if (((slot - 1) & 1) != 0) return P.draft + ((b * P.k + i) * P.V) * E;
+  if (which) return P.draft + ((b * P.k + i) * P.V) * E;
   return P.target + ((b * (P.k + 1) + i) * P.V) * E;
 }
-__device__ __forceinline__ int tslot(bool stoch, int i, int64_t k) { return stoch ? (i == k ? 0 : 1 + 2 * i) : i; }
-__device__ __forceinline__ int dslot(int i) { return 2 + 2 * i; }
 
-// Acceptance test, first-reject scan and emission for sequence b (wave 0).
+// Writes every output of sequence b (its last event): the first rejected
+// position from the state word, the final token from the token record, the
+// error bits, and the accepted drafts.
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_decide(const LinearParams& P, int64_t b, uint32_t tag) {
+__device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b) {
   const int lane = lane_id();
   const int64_t k = P.k, V = P.V;
-  const uint64_t* rows = P.rows + b * P.R * ROW_WORDS;
+  uint64_t s = 0;
+  uint32_t ew = 0;
+  Token t;
+  t.y = -2;
+  bool tg = true;
+  if (lane == 0) s = state_load(P.state + b * SSTRIDE);
+  if (lane == 1) ew = __hip_atomic_load(P.errw + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 2) tg = get_rec(P.tok + b, t, P.tag);
   const bool has = lane < k;
   const int x = has ? P.tokens[b * k + lane] : 0;
-  const bool tok_bad = has && (x < 0 || x >= V);
-  RowStat ts{}, ds{}, tk{};
-  bool got = true;
-  if (has) got = get_rec(rows + (int64_t)tslot(STOCH, lane, k) * ROW_WORDS, ts, tag) && got;
-  if (STOCH && has) got = get_rec(rows + (int64_t)dslot(lane) * ROW_WORDS, ds, tag) && got;
-  got = get_rec(rows + (int64_t)tslot(STOCH, (int)k, k) * ROW_WORDS, tk, tag) && got;
-  // every row record of the sequence has been read: clear them
-  for (int64_t r = lane; r < P.R; r += 64) clear_rec<RowStat>(const_cast<uint64_t*>(rows) + r * ROW_WORDS);
-  const bool row_bad = (has && ts.ok != 1) || (STOCH && has && ds.ok != 1) || tk.ok != 1;
-  const bool internal = (has && (ts.ok < 0 || (STOCH && ds.ok < 0))) || tk.ok < 0 || !got;
-  int err = 0;
-  if (__ballot(tok_bad)) err |= SV_ERR_TOKEN;
-  if (__ballot(row_bad)) err |= SV_ERR_ROW;
-  if (__ballot(internal)) err |= SV_ERR_INTERNAL;
-
-  int32_t* out = P.out_tokens + b * (k + 1);
-  Decision d{};
-  if (err) {
-    for (int64_t j = lane; j <= k; j += 64) out[j] = -1;
-    if (STOCH && has) {
-      if (P.p_target) P.p_target[b * k + lane] = NAN;
-      if (P.p_draft) P.p_draft[b * k + lane] = NAN;
-    }
-    if (lane == 0) {
-      P.accept_len[b] = -1;
-      if (P.err_flags) P.err_flags[b] = err;
-      d.L = -1;
-      d.pending = 0;
-      if (STOCH && P.n_resid > 0) put_rec(P.dec + b * DEC_WORDS, d, tag);
-    }
-    return;
+  Probs pr;
+  pr.pt = pr.pd = NAN;
+  bool pg = true;
+  if (STOCH && has) {
+    pg = get_rec(P.prob + (b * k + lane) * PROB_WORDS, pr, P.tag);
+    clear_rec<Probs>(P.prob + (b * k + lane) * PROB_WORDS);
   }
-  bool acc = false;
-  if constexpr (!STOCH) {
-    acc = has && (x == ts.argmax);
-  } else {
-    if (has) {
-      const double c0d = (double)P.c0;
-      const float tx = load_elem<DT>(P.target + ((b * (k + 1) + lane) * V) * DTraits<DT>::E, x);
-      const float dx = load_elem<DT>(P.draft + ((b * k + lane) * V) * DTraits<DT>::E, x);
-      const double pt = exp2(((double)tx - (double)ts.M) * c0d) / ts.Z;
-      const double pd = exp2(((double)dx - (double)ds.M) * c0d) / ds.Z;
-      double q;
-      if (pd > 0.0) q = pt / pd;
-      else q = (pt > 0.0) ? INFINITY : NAN;
-      acc = (double)P.uniforms[b * (k + 1) + lane] < q;  // NaN ratio rejects
-      if (P.p_target) P.p_target[b * k + lane] = (float)pt;
-      if (P.p_draft) P.p_draft[b * k + lane] = (float)pd;
-    }
+  // leave the sequence's words and records zero for the next call
+  if (lane == 0) counter_reset(P.state + b * SSTRIDE);
+  if (lane == 1) counter_reset(P.errw + b * CSTRIDE);
+  if (lane == 2) clear_rec<Token>(P.tok + b);
+  if (lane < P.R) {
+    const int64_t i = lane <= k ? lane : lane - k - 1;
+    clear_rec<RowStat>(P.rows + row_q<STOCH>(P, b, i, lane <= k ? 0 : 1) * ROW_WORDS);
   }
-  const unsigned long long rej = __ballot(has && !acc);
+  s = __shfl(s, 0);
+  int err = (int)__shfl(ew, 1);
+  const int y = __shfl(tg ? t.y : -2, 2);
+  const uint64_t rej = (s >> 32) & ((1ull << k) - 1);
   const int L = rej ? __builtin_ctzll(rej) : (int)k;
-  bool pending = false;
-  int y;
-  if constexpr (!STOCH) {
-    const int yl = __shfl(ts.argmax, L & 63);
-    y = (L == k) ? tk.argmax : yl;
-  } else {
-    pending = (L < k);
-    y = tk.y;
-    // the residual workgroups need t_L's and d_L's statistics
-    d.L = L;
-    d.pending = pending ? 1 : 0;
-    d.Mt = __shfl(ts.M, L & 63);
-    d.Md = __shfl(ds.M, L & 63);
-    d.Zt = __shfl(ts.Z, L & 63);
-    d.Zd = __shfl(ds.Z, L & 63);
+  if (__ballot(has && (x < 0 || x >= V))) err |= SV_ERR_TOKEN;
+  if (y == -2 || __ballot(!pg)) err |= SV_ERR_INTERNAL;
+  if (STOCH && has) {
+    if (P.p_target) P.p_target[b * k + lane] = err ? NAN : pr.pt;
+    if (P.p_draft) P.p_draft[b * k + lane] = err ? NAN : pr.pd;
   }
-  for (int64_t j = lane; j <= k; j += 64) {
-    if (j < L) out[j] = x;  // j == lane here: lane L-1 < 64 holds x_j
-    else if (j == L) { if (!pending) out[j] = y; }
-    else out[j] = -1;
+  int32_t* out = P.out_tokens + b * (k + 1);
+  for (int64_t j = lane; j <= k; j += WAVE) {
+    int v = -1;
+    if (!err) v = (j < L) ? x : (j == L ? y : -1);
+    out[j] = v;
   }
   if (lane == 0) {
-    P.accept_len[b] = L;
-    if (P.err_flags) P.err_flags[b] = 0;
-    if (STOCH && P.n_resid > 0) put_rec(P.dec + b * DEC_WORDS, d, tag);
+    P.accept_len[b] = err ? -1 : L;
+    if (P.err_flags) P.err_flags[b] = err;
   }
 }
 
+// Counts one event of sequence b (R row combines and the final token); the last
+// one writes the outputs.
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_stream_block(const LinearParams& P, uint32_t item,
-                                                    BlockScratch& sm, RowStat& rsh) {
-  // item < 2^31: 32-bit index arithmetic (64-bit division would be a long scalar loop)
-  const uint32_t C = (uint32_t)P.C, R = (uint32_t)P.R;
-  const uint32_t rid32 = item / C;
-  const int64_t c = item - rid32 * C;
-  const int64_t b = rid32 / R;
-  const int slot = (int)(rid32 - (uint32_t)b * R);
-  const int64_t rid = rid32;
-  const char* row = slot_ptr<DT, STOCH>(P, b, slot);
-  const uint32_t tag = P.tag;
-  stream_chunk<DT, STOCH, !STOCH>(row, P.V, c, P.c0, P.parts + (int64_t)item * PART_WORDS, tag, sm);
-  if (c != P.C - 1) return;
-  // last chunk of the row: combine it (and draw the bonus token from row k)
-  const bool draw = STOCH && slot == 0;
-  const float u = draw ? P.uniforms[b * (P.k + 1) + P.k] : 0.0f;
-  const RowStat st = finalize_row<DT, STOCH>(row, P.V, P.parts + rid * P.C * PART_WORDS, P.C, P.c0, tag,
-                                             draw, u, sm, rsh);
-  if (threadIdx.x == 0) put_rec(P.rows + rid * ROW_WORDS, st, tag);
-  if (slot != P.R - 1) return;
-  // last row of the sequence: decide
-  if (wave_id() == 0) linear_decide<DT, STOCH>(P, b, tag);
+__device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b) {
+  const uint32_t total = (uint32_t)P.R + 1u;
+  uint32_t old = 0;
+  if (lane_id() == 0) old = counter_add(P.fin + b * CSTRIDE, 1u);
+  old = bcast(old);
+  if (old + 1 != total) return;
+  if (lane_id() == 0) counter_reset(P.fin + b * CSTRIDE);
+  linear_emit<DT, STOCH>(P, b);
+}
+
+// Called after the state update old -> now by the wave that combined row
+// (mi, mwhich) with statistics `mine`. If this update settles L: in stochastic
+// mode with L < k, hand rows t_L, d_L to the residual waves; otherwise the final
+// token is known (the bonus draw, or argmax of t_L in greedy mode): record it.
+template <int DT, bool STOCH>
+__device__ __forceinline__ void linear_settle(const LinearParams& P, int64_t b, uint64_t old, uint64_t now,
+                                              const RowStat& mine, int64_t mi, int mwhich) {
+  const int k = (int)P.k;
+  const int Ln = settled_L(now, k);
+  if (Ln < 0 || settled_L(old, k) >= 0) return;
+  RowStat tl = mine;
+  bool got = true;
+  if (!(mi == Ln && mwhich == 0)) {
+    if (lane_id() == 0) got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 0) * ROW_WORDS, tl, P.tag);
+  }
+  if (STOCH && Ln < k) {
+    RowStat dl = mine;
+    if (!(mi == Ln && mwhich == 1)) {
+      if (lane_id() == 0) got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 1) * ROW_WORDS, dl, P.tag) && got;
+    }
+    if (lane_id() == 0) {
+      Decision d;
+      d.L = Ln;
+      d.kind = (got && tl.ok == 1 && dl.ok == 1) ? 1 : 2;
+      d.Mt = tl.M;
+      d.Md = dl.M;
+      d.Zt = tl.Z;
+      d.Zd = dl.Z;
+      put_rec(P.dec + b * DEC_WORDS, d, P.tag);
+    }
+    return;   // the residual waves draw the token
+  }
+  if (lane_id() == 0) {
+    Token t;
+    t.y = !got ? -2 : (tl.ok != 1 ? -1 : (STOCH ? tl.y : tl.argmax));
+    put_rec(P.tok + b, t, P.tag);
+    if (STOCH && k > 0) {
+      Decision d;
+      d.L = Ln;
+      d.kind = 0;
+      d.Mt = d.Md = 0.0f;
+      d.Zt = d.Zd = 0.0;
+      put_rec(P.dec + b * DEC_WORDS, d, P.tag);
+    }
+  }
+  linear_event<DT, STOCH>(P, b);   // the final token
+}
+
+// Combines row q (b, position i, target/draft) once its last chunk is done.
+template <int DT, bool STOCH>
+__device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q, int64_t b, int64_t i, int which) {
+  const int lane = lane_id();
+  const int64_t k = P.k, V = P.V;
+  const char* row = row_ptr<DT, STOCH>(P, b, i, which);
+  // the draft token of this position; its logit in this row comes with the partials
+  const int x = (i < k) ? P.tokens[b * k + i] : -1;
+  const RowParts rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
+  const float xv = rp.xv;
+  double wl[MAX_ROUNDS];
+  const RowSums rs = row_sums<STOCH>(rp, P.c0, wl);
+  RowStat st;
+  st.Z = rs.Z;
+  st.M = rs.M;
+  st.argmax = rs.argmax;
+  st.px = NAN;
+  st.y = -1;
+  const bool usable = STOCH ? (rs.M > -INFINITY && __builtin_isfinite(rs.Z) && rs.Z > 0.0) : (rs.argmax >= 0);
+  st.ok = rp.got ? (usable ? 1 : 0) : -1;
+  if (STOCH && i < k && st.ok == 1 && x >= 0 && x < V && rp.xin)
+    st.px = exp2(((double)xv - (double)rs.M) * (double)P.c0) / rs.Z;
+  if (STOCH && i == k && st.ok == 1) {
+    // the bonus draw, unless an earlier position has already been rejected
+    uint64_t sn = 0;
+    if (lane == 0) sn = state_load(P.state + b * SSTRIDE);
+    sn = bcast(sn);
+    if (settled_L(sn, (int)k) < 0)
+      st.y = softmax_draw<DT>(row, V, P.C, P.c0, P.uniforms[b * (k + 1) + k], rp, rs, wl);
+  }
+  if (lane == 0) {
+    if (st.ok != 1)
+      __hip_atomic_fetch_or(P.errw + b * CSTRIDE, (uint32_t)(st.ok < 0 ? SV_ERR_INTERNAL : SV_ERR_ROW),
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    put_rec(P.rows + q * ROW_WORDS, st, P.tag);
+  }
+
+  uint64_t bits = 0;
+  bool update = true;
+  if (i == k) {
+    bits = BONUS_BIT;   // the row after the last draft is combined (and drawn)
+  } else if constexpr (!STOCH) {
+    const bool acc = st.ok == 1 && x == st.argmax;
+    bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
+  } else {
+    uint32_t old = 0;
+    if (lane == 0) old = counter_add(P.pair_cnt + (b * k + i) * CSTRIDE, 1u);
+    old = bcast(old);
+    update = (old == 1);
+    if (update) {
+      // second row of the pair: the acceptance test of position i
+      RowStat other;
+      bool got = true;
+      if (lane == 0) {
+        counter_reset(P.pair_cnt + (b * k + i) * CSTRIDE);
+        got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);
+        const double pt = which == 0 ? st.px : other.px;
+        const double pd = which == 0 ? other.px : st.px;
+        double qr;
+        if (pd > 0.0) qr = pt / pd;
+        else qr = (pt > 0.0) ? INFINITY : NAN;
+        const bool ok = got && st.ok == 1 && other.ok == 1;
+        const bool acc = ok && (double)P.uniforms[b * (k + 1) + i] < qr;   // NaN ratio rejects
+        bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
+        Probs pr;
+        pr.pt = (float)pt;
+        pr.pd = (float)pd;
+        put_rec(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
+        if (!got)
+          __hip_atomic_fetch_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      }
+      bits = bcast(bits);
+    }
+  }
+  if (update) {
+    uint64_t olds = 0;
+    if (lane == 0) olds = state_or(P.state + b * SSTRIDE, bits);
+    olds = bcast(olds);
+    linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which);
+  }
+  linear_event<DT, STOCH>(P, b);
+}
+
+template <int DT, bool STOCH>
+__device__ __forceinline__ void linear_stream_wave(const LinearParams& P, int64_t w) {
+  uint32_t q32, c32;
+  stream_coords((uint32_t)w, (uint32_t)P.CP, (uint32_t)(P.B * P.R), q32, c32);
+  if (c32 >= (uint32_t)P.C) return;   // padding wave
+  const int64_t q = q32, c = c32;
+  int64_t b, i;
+  int which;
+  if constexpr (STOCH) {
+    const uint32_t twoB = (uint32_t)(2 * P.B);
+    const uint32_t pairs = (uint32_t)(P.k) * twoB;
+    if (q32 < pairs) {
+      i = q32 / twoB;
+      const uint32_t rem = q32 - (uint32_t)i * twoB;
+      b = rem >> 1;
+      which = (int)(rem & 1u);
+    } else {
+      i = P.k;
+      b = q32 - pairs;
+      which = 0;
+    }
+  } else {
+    const uint32_t B32 = (uint32_t)P.B;
+    i = q32 / B32;
+    b = q32 - (uint32_t)i * B32;
+    which = 0;
+  }
+  const char* row = row_ptr<DT, STOCH>(P, b, i, which);
+  const int64_t x = (STOCH && i < P.k) ? (int64_t)P.tokens[b * P.k + i] : -1;
+  const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c, P.c0, x);
+  uint32_t old = 0;
+  if (lane_id() == 0) {
+    put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
+    old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
+  }
+  old = bcast(old);
+  if (old + 1 != (uint32_t)P.C) return;
+  if (lane_id() == 0) counter_reset(P.row_cnt + q * CSTRIDE);
+  linear_combine<DT, STOCH>(P, q, b, i, which);
 }
 
 template <int DT>
-__device__ __forceinline__ void linear_residual_block(const LinearParams& P, int64_t task, BlockScratch& sm,
-                                                      double* wsum) {
-  const uint32_t b32 = (uint32_t)task / (uint32_t)P.C;
+__device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int64_t w) {
+  const int lane = lane_id();
+  const uint32_t C = (uint32_t)P.C;
+  const uint32_t b32 = (uint32_t)w / C;
   const int64_t b = b32;
-  const int64_t c = (uint32_t)task - b32 * (uint32_t)P.C;
+  const int64_t c = (uint32_t)w - b32 * C;
   const int64_t k = P.k;
-  const uint32_t tag = P.tag;
-  if (threadIdx.x == 0) {
-    Decision d{};
-    const bool ok = get_rec(P.dec + b * DEC_WORDS, d, tag);
-    sm.i[0] = ok ? d.pending : 0;
-    sm.i[1] = d.L;
-    sm.i[2] = ok ? 1 : 0;
-    sm.f[0] = d.Mt;
-    sm.f[1] = d.Md;
-    sm.d[0] = d.Zt;
-    sm.d[1] = d.Zd;
+  Decision d;
+  d.L = 0;
+  d.kind = 2;
+  d.Mt = d.Md = 0.0f;
+  d.Zt = d.Zd = 0.0;
+  bool got = true;
+  if (lane == 0) got = poll_rec(P.dec + b * DEC_WORDS, d, P.tag);
+  got = bcast(got ? 1 : 0) != 0;
+  d.L = bcast(d.L);
+  d.kind = got ? bcast(d.kind) : 3;   // 3: the decision never arrived
+  d.Mt = bcast(d.Mt);
+  d.Md = bcast(d.Md);
+  d.Zt = bcast(d.Zt);
+  d.Zd = bcast(d.Zd);
+  const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
+  const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
+  const ResidW rw = make_residw(d, P.c0);
+  if (d.kind == 1) {
+    ResPart r;
+    r.s = residual_chunk_sum<DT>(trow, drow, P.V, c, rw);
+    if (lane == 0) put_rec(P.res + (b * P.C + c) * RES_WORDS, r, P.tag);
   }
-  __syncthreads();
-  const int pending = sm.i[0];
-  const int L = sm.i[1];
-  const bool got_decision = sm.i[2] != 0;
-  const float Mt = sm.f[0], Md = sm.f[1];
-  const double Zt = sm.d[0], Zd = sm.d[1];
-  __syncthreads();
-  constexpr int E = DTraits<DT>::E;
-  const char* trow = P.target + ((b * (k + 1) + (pending ? L : 0)) * P.V) * E;
-  const char* drow = P.draft + ((b * k + (pending ? L : 0)) * P.V) * E;
-  const float c0 = P.c0;
-  const float mc0t = Mt * c0, mc0d = Md * c0;
-  // 1 / sum_v exp2(x_v*c0 - fl32(M*c0)) from Z = sum_v exp2(x_v*c0 - M*c0)
-  const float izt = pending ? (float)(1.0 / (Zt * exp2((double)Mt * (double)c0 - (double)mc0t))) : 0.0f;
-  const float izd = pending ? (float)(1.0 / (Zd * exp2((double)Md * (double)c0 - (double)mc0d))) : 0.0f;
-  ResidualWeights<DT> pol{trow, drow, P.V, row_aligned(trow), row_aligned(drow), c0, mc0t, mc0d, izt, izd};
-
-  // every residual workgroup answers (0 when there is nothing to draw), so the
-  // sequence's last one knows when the decision record may be cleared
-  ResPart mine;
-  mine.s = pending ? chunk_weight_sum<DT>(pol, c, sm) : 0.0;
-  if (c != P.C - 1) {
-    if (threadIdx.x == 0) put_rec(P.res + task * RES_WORDS, mine, tag);
-    return;
+  uint32_t old = 0;
+  if (lane == 0) old = counter_add(P.res_cnt + b * CSTRIDE, 1u);
+  old = bcast(old);
+  if (old + 1 != C) return;
+  // last residual wave of the sequence: draw the correction token
+  if (lane == 0) {
+    counter_reset(P.res_cnt + b * CSTRIDE);
+    clear_rec<Decision>(P.dec + b * DEC_WORDS);
   }
-
-  // last chunk of the sequence's residual: pick the chunk holding u*S, scan it
-  const float u = pending ? P.uniforms[b * (k + 1) + k] : 0.0f;
-  if (wave_id() == 0) {
-    int c_lo, c_hi;
-    lane_chunk_range(P.C, c_lo, c_hi);
-    double wl[CHUNKS_PER_LANE];
+  if (d.kind == 0) return;   // no draft rejected: the bonus token is recorded already
+  int y = (d.kind == 3) ? -2 : -1;
+  if (d.kind == 1) {
+    double wl[MAX_ROUNDS];
     bool ok = true;
 #pragma unroll
-    for (int q = 0; q < CHUNKS_PER_LANE; ++q) {
-      wl[q] = 0.0;
-      ResPart r{};
-      const int cc = c_lo + q;
-      if (cc >= c_hi) continue;
-      if (cc < P.C - 1) {
-        const bool g = get_rec(P.res + (b * P.C + cc) * RES_WORDS, r, tag);
+    for (int t = 0; t < MAX_ROUNDS; ++t) {
+      wl[t] = 0.0;
+      const int cc = t * WAVE + lane;
+      if (cc < P.C) {
+        ResPart r;
+        uint64_t* rec = P.res + (b * P.C + cc) * RES_WORDS;
+        const bool g = get_rec(rec, r, P.tag);
         ok = ok && g;
-        wl[q] = g ? r.s : 0.0;
-        clear_rec<ResPart>(P.res + (b * P.C + cc) * RES_WORDS);
-      } else {
-        wl[q] = mine.s;
+        wl[t] = g ? r.s : 0.0;
+        clear_rec<ResPart>(rec);
       }
     }
-    if (lane_id() == 0) clear_rec<Decision>(P.dec + b * DEC_WORDS);
-    const bool all_ok = __ballot(!ok) == 0ull;
-    const ChunkPick pk = pick_chunk(P.C, (double)u, wl);
-    if (lane_id() == 0) {
-      sm.result = (all_ok && got_decision) ? pk.c : -2;
-      sm.theta = pk.fallback ? INFINITY : pk.theta - pk.before;
+    const float u = P.uniforms[b * (k + 1) + k];
+    if (__ballot(!ok)) {
+      y = -2;
+    } else {
+      double tot = 0.0;
+#pragma unroll
+      for (int t = 0; t < MAX_ROUNDS; ++t) tot += wl[t];
+      tot = wave_sum(tot);
+      const ChunkPick pk = pick_chunk(P.C, (double)u, wl);
+      if (pk.c >= 0) {
+        const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
+        y = residual_chunk_draw<DT>(trow, drow, P.V, pk.c, rw, th);
+      } else if (tot == 0.0) {
+        // no residual mass (rows equal up to rounding): draw from p_t,L instead
+        y = softmax_draw_streamed<DT>(trow, P.V, P.C, P.c0, u);
+      }
     }
   }
-  __syncthreads();
-  const int cstar = (int)sm.result;
-  const double th = sm.theta;
-  __syncthreads();
-  if (!pending) {
-    if (!got_decision && threadIdx.x == 0) {   // the decision never arrived: flag the sequence
-      P.accept_len[b] = -1;
-      if (P.err_flags) P.err_flags[b] = SV_ERR_INTERNAL;
-    }
-    return;
+  if (lane == 0) {
+    Token t;
+    t.y = y;
+    put_rec(P.tok + b, t, P.tag);
   }
-  int y;
-  if (cstar >= 0) {
-    y = (int)chunk_invcdf<DT>(pol, cstar, th, sm);
-  } else if (cstar == -1) {
-    // no residual mass (equal rows up to rounding): draw from p_t,L instead
-    y = draw_row_streamed<DT>(trow, P.V, P.C, Mt, c0, u, wsum, sm);
-  } else {
-    y = -1;
-    if (threadIdx.x == 0) {
-      P.accept_len[b] = -1;
-      if (P.err_flags) P.err_flags[b] = SV_ERR_INTERNAL;
-    }
-  }
-  if (threadIdx.x == 0) P.out_tokens[b * (k + 1) + L] = y;
+  linear_event<DT, true>(P, b);
 }
 
 template <int DT, bool STOCH>
-__global__ __launch_bounds__(BLOCK) void linear_kernel(LinearParams P) {
-  __shared__ BlockScratch sm;
-  __shared__ RowStat rsh;
-  const int64_t hw = blockIdx.x;
-  if (hw < P.n_stream) {
-    linear_stream_block<DT, STOCH>(P, (uint32_t)xcd_logical_block(hw, P.n_stream), sm, rsh);
-  } else {
-    if constexpr (STOCH) {
-      __shared__ double wsum[MAX_CHUNKS];
-      linear_residual_block<DT>(P, hw - P.n_stream, sm, wsum);
-    }
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void linear_kernel(LinearParams P) {
+  const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
+  if (w < P.n_stream) {
+    linear_stream_wave<DT, STOCH>(P, w);
+  } else if (w < P.n_stream + P.n_resid) {
+    if constexpr (STOCH) linear_residual_wave<DT>(P, w - P.n_stream);
   }
 }
 
@@ -470,29 +666,75 @@ struct TreeParams {
   int32_t* path_nodes;
   int32_t* out_tokens;
   int32_t* err_flags;
-  uint64_t* parts;      // [B][N][C] Partial records
-  uint64_t* node_y;     // [B][N]    token chosen at each node (-1: unusable row, -2: timeout)
+  uint64_t* parts;      // [B*N][C] Partial records
+  uint32_t* row_cnt;    // [B*N]
+  int32_t* node_y;      // [B][N] token of each node (-1 unusable row, -2 a wait timed out)
   int64_t B, N, V, max_depth;
-  int C;
+  int C, CP;
   float c0;
   uint32_t tag;
   int64_t n_stream;
 };
 
-// Accepted-path search for tree b (whole workgroup). LDS: parent (int16) and
-// match flag (uint8) of every node.
-__device__ __forceinline__ void tree_walk(const TreeParams& P, int64_t b, uint32_t tag, unsigned char* smem,
-                                          BlockScratch& sm) {
+template <int DT, bool STOCH>
+__global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
+  constexpr int E = DTraits<DT>::E;
+  const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
+  if (w >= P.n_stream) return;
+  const uint32_t C = (uint32_t)P.C;
+  uint32_t q32, c32;
+  stream_coords((uint32_t)w, (uint32_t)P.CP, (uint32_t)(P.B * P.N), q32, c32);
+  if (c32 >= C) return;   // padding wave
+  const int64_t q = q32, c = c32;
+  const char* row = P.logits + (q * P.V) * E;
+  const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c, P.c0);
+  uint32_t old = 0;
+  if (lane_id() == 0) {
+    put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
+    old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
+  }
+  old = bcast(old);
+  if (old + 1 != C) return;
+  if (lane_id() == 0) counter_reset(P.row_cnt + q * CSTRIDE);
+  const RowParts rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
+  double wl[MAX_ROUNDS];
+  const RowSums rs = row_sums<STOCH>(rp, P.c0, wl);
+  int y;
+  if (!rp.got) {
+    y = -2;
+  } else if constexpr (STOCH) {
+    const bool usable = rs.M > -INFINITY && __builtin_isfinite(rs.Z) && rs.Z > 0.0;
+    y = usable ? softmax_draw<DT>(row, P.V, P.C, P.c0, P.uniforms[q], rp, rs, wl) : -1;
+  } else {
+    y = rs.argmax;
+  }
+  if (lane_id() == 0) P.node_y[q] = y;
+}
+
+__device__ __forceinline__ int block_or(int v, int* sh) {
+  // OR over the workgroup (each bit through __syncthreads_or)
+  int r = 0;
+  for (int bit = 1; bit <= SV_ERR_INTERNAL; bit <<= 1)
+    if (__syncthreads_or(v & bit)) r |= bit;
+  (void)sh;
+  return r;
+}
+
+// Accepted-path search of tree b (one workgroup). LDS: parent (int16) and match
+// flag (uint8) of every node.
+__global__ __launch_bounds__(BLOCK) void tree_walk_kernel(TreeParams P) {
+  extern __shared__ unsigned char smem[];
+  __shared__ unsigned long long best_sh[BLOCK / WAVE];
+  const int64_t b = blockIdx.x;
   const int64_t N = P.N;
   int16_t* par_s = reinterpret_cast<int16_t*>(smem);
   unsigned char* match_s = smem + 2 * N;
   const int32_t* par = P.parent + b * P.parent_stride;
   const int32_t* cand = P.cand + b * N;
-  const uint64_t* ny = P.node_y + b * N;
+  int32_t* ny = P.node_y + b * N;
   int err = 0;
   for (int64_t i = threadIdx.x; i < N; i += BLOCK) {
-    int32_t y;
-    if (!get_rec(ny + i, y, tag)) y = -2;
+    const int y = ny[i];
     if (y == -1) err |= SV_ERR_ROW;
     if (y == -2) err |= SV_ERR_INTERNAL;
     const int p = par[i];
@@ -503,21 +745,13 @@ __device__ __forceinline__ void tree_walk(const TreeParams& P, int64_t b, uint32
     if (i > 0) {
       const int ci = cand[i];
       if (ci < 0 || ci >= P.V) err |= SV_ERR_TOKEN;
-      if (!bad) {
-        int32_t yp;
-        if (!get_rec(ny + p, yp, tag)) { yp = -2; err |= SV_ERR_INTERNAL; }
-        m = (ci == yp) ? 1 : 0;
-      }
+      if (!bad) m = (ci == ny[p]) ? 1 : 0;
     }
     match_s[i] = m;
   }
-  // OR of the error bits over the workgroup (each bit separately)
-  int all_err = 0;
-  for (int bit = 1; bit <= SV_ERR_INTERNAL; bit <<= 1)
-    if (__syncthreads_or(err & bit)) all_err |= bit;
-
-  // Depth check and path search (bad parents were replaced by the root above, so
-  // every chain ends; the depth bound is checked whatever other error was found).
+  int all_err = block_or(err, nullptr);
+  // depth check and path search (bad parents were replaced by the root, so every
+  // chain ends; the depth bound is checked whatever other error was found)
   unsigned long long best_key = 0ull;
   int too_deep = 0;
   for (int64_t i = threadIdx.x; i < N; i += BLOCK) {
@@ -544,78 +778,36 @@ __device__ __forceinline__ void tree_walk(const TreeParams& P, int64_t b, uint32
       P.accept_len[b] = -1;
       if (P.err_flags) P.err_flags[b] = all_err;
     }
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < N; i += BLOCK) clear_rec<int32_t>(const_cast<uint64_t*>(ny) + i);
-    return;
-  }
-  // workgroup max of the (depth, -index) key
-  {
-    unsigned long long v = best_key;
+  } else {
+    // workgroup max of the (depth, -index) key
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long t = __shfl_xor(v, o);
-      v = t > v ? t : v;
+      const unsigned long long t = __shfl_xor(best_key, o);
+      best_key = t > best_key ? t : best_key;
     }
-    if (lane_id() == 0) sm.d[wave_id()] = __longlong_as_double((long long)v);
+    if (lane_id() == 0) best_sh[wave_in_block()] = best_key;
     __syncthreads();
     unsigned long long r = 0ull;
-    for (int w = 0; w < NWAVES; ++w) {
-      const unsigned long long t = (unsigned long long)__double_as_longlong(sm.d[w]);
-      r = t > r ? t : r;
-    }
-    __syncthreads();
-    best_key = r;
-  }
-  const int L = (int)(best_key >> 32);
-  const int best = (int)(0xffffffffull - (best_key & 0xffffffffull));
-  for (int64_t j = L + threadIdx.x; j < P.max_depth; j += BLOCK) path[j] = -1;
-  for (int64_t j = L + 1 + threadIdx.x; j <= P.max_depth; j += BLOCK) out[j] = -1;
-  if (threadIdx.x == 0) {
-    int node = best;
-    for (int j = L - 1; j >= 0; --j) {
-      path[j] = node;
-      out[j] = cand[node];
-      node = par_s[node];
-    }
-    int32_t yb;
-    out[L] = get_rec(ny + best, yb, tag) ? yb : -1;
-    P.accept_len[b] = L;
-    if (P.err_flags) P.err_flags[b] = 0;
-  }
-  // every node record of the tree has been read: clear them
-  __syncthreads();
-  for (int64_t i = threadIdx.x; i < N; i += BLOCK) clear_rec<int32_t>(const_cast<uint64_t*>(ny) + i);
-}
-
-template <int DT, bool STOCH>
-__global__ __launch_bounds__(BLOCK) void tree_kernel(TreeParams P) {
-  __shared__ BlockScratch sm;
-  __shared__ RowStat rsh;
-  extern __shared__ unsigned char walk_smem[];
-  constexpr int E = DTraits<DT>::E;
-  const int64_t hw = blockIdx.x;
-  if (hw < P.n_stream) {
-    const uint32_t item = (uint32_t)xcd_logical_block(hw, P.n_stream);
-    const uint32_t rid32 = item / (uint32_t)P.C;
-    const int64_t rid = rid32;
-    const int64_t c = item - rid32 * (uint32_t)P.C;
-    const uint32_t b32 = rid32 / (uint32_t)P.N;
-    const int64_t b = b32;
-    const int64_t n = rid32 - b32 * (uint32_t)P.N;
-    const char* row = P.logits + (rid * P.V) * E;
-    const uint32_t tag = P.tag;
-    stream_chunk<DT, STOCH, !STOCH>(row, P.V, c, P.c0, P.parts + (int64_t)item * PART_WORDS, tag, sm);
-    if (c == P.C - 1) {
-      const float u = STOCH ? P.uniforms[rid] : 0.0f;
-      const RowStat st = finalize_row<DT, STOCH>(row, P.V, P.parts + rid * P.C * PART_WORDS, P.C, P.c0,
-                                                 tag, STOCH, u, sm, rsh);
-      if (threadIdx.x == 0) {
-        const int32_t y = st.ok == 1 ? st.y : (st.ok < 0 ? -2 : -1);
-        put_rec(P.node_y + rid, y, tag);
+    for (int wv = 0; wv < BLOCK / WAVE; ++wv) r = best_sh[wv] > r ? best_sh[wv] : r;
+    const int L = (int)(r >> 32);
+    const int best = (int)(0xffffffffull - (r & 0xffffffffull));
+    for (int64_t j = L + threadIdx.x; j < P.max_depth; j += BLOCK) path[j] = -1;
+    for (int64_t j = L + 1 + threadIdx.x; j <= P.max_depth; j += BLOCK) out[j] = -1;
+    if (threadIdx.x == 0) {
+      int node = best;
+      for (int j = L - 1; j >= 0; --j) {
+        path[j] = node;
+        out[j] = cand[node];
+        node = par_s[node];
       }
-      if (n == P.N - 1) tree_walk(P, b, tag, walk_smem, sm);
+      out[L] = ny[best];
+      P.accept_len[b] = L;
+      if (P.err_flags) P.err_flags[b] = 0;
     }
   }
+  // leave the node tokens zero, as the workspace was
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < N; i += BLOCK) ny[i] = 0;
 }
 
 // ------------------------------------------------------------------ row statistics
@@ -626,8 +818,9 @@ struct RowStatsParams {
   int32_t* row_argmax;
   int32_t* err_flags;
   uint64_t* parts;
+  uint32_t* row_cnt;
   int64_t rows, V;
-  int C;
+  int C, CP;
   float c0;
   uint32_t tag;
   int64_t n_stream;
@@ -635,29 +828,33 @@ struct RowStatsParams {
 
 template <int DT>
 __global__ __launch_bounds__(BLOCK) void row_stats_kernel(RowStatsParams P) {
-  __shared__ BlockScratch sm;
-  __shared__ RowStat rsh;
   constexpr int E = DTraits<DT>::E;
-  const int64_t hw = blockIdx.x;
-  if (hw < P.n_stream) {
-    const uint32_t item = (uint32_t)xcd_logical_block(hw, P.n_stream);
-    const uint32_t r32 = item / (uint32_t)P.C;
-    const int64_t r = r32, c = item - r32 * (uint32_t)P.C;
-    const char* row = P.x + (r * P.V) * E;
-    const uint32_t tag = P.tag;
-    stream_chunk<DT, true, true>(row, P.V, c, P.c0, P.parts + (int64_t)item * PART_WORDS, tag, sm);
-    if (c == P.C - 1) {
-      // argmax needs the ARG partials, the normaliser the SUM partials: both are kept
-      const RowStat st = finalize_row<DT, true>(row, P.V, P.parts + r * P.C * PART_WORDS, P.C, P.c0, tag,
-                                                false, 0.0f, sm, rsh);
-      if (threadIdx.x == 0) {
-        const bool ok = st.ok == 1 && st.argmax >= 0;
-        if (P.row_max) P.row_max[r] = st.M;
-        if (P.row_argmax) P.row_argmax[r] = st.argmax;
-        if (P.row_lse) P.row_lse[r] = ok ? (float)((double)st.M * (double)P.c0 * LN2 + log(st.Z)) : NAN;
-        if (P.err_flags) P.err_flags[r] = ok ? 0 : (st.ok < 0 ? SV_ERR_INTERNAL : SV_ERR_ROW);
-      }
-    }
+  const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
+  if (w >= P.n_stream) return;
+  const uint32_t C = (uint32_t)P.C;
+  uint32_t r32, c32;
+  stream_coords((uint32_t)w, (uint32_t)P.CP, (uint32_t)P.rows, r32, c32);
+  if (c32 >= C) return;   // padding wave
+  const int64_t r = r32, c = c32;
+  const char* row = P.x + (r * P.V) * E;
+  const Partial p = chunk_partial<DT, true, true>(row, P.V, c, P.c0);
+  uint32_t old = 0;
+  if (lane_id() == 0) {
+    put_rec(P.parts + (r * P.C + c) * PART_WORDS, p, P.tag);
+    old = counter_add(P.row_cnt + r * CSTRIDE, 1u);
+  }
+  old = bcast(old);
+  if (old + 1 != C) return;
+  if (lane_id() == 0) counter_reset(P.row_cnt + r * CSTRIDE);
+  const RowParts rp = read_parts(P.parts + r * P.C * PART_WORDS, P.C, P.tag);
+  double wl[MAX_ROUNDS];
+  const RowSums rs = row_sums<true>(rp, P.c0, wl);
+  if (lane_id() == 0) {
+    const bool ok = rp.got && rs.argmax >= 0 && __builtin_isfinite(rs.Z) && rs.Z > 0.0;
+    if (P.row_max) P.row_max[r] = rs.M;
+    if (P.row_argmax) P.row_argmax[r] = rs.argmax;
+    if (P.row_lse) P.row_lse[r] = ok ? (float)((double)rs.M * (double)P.c0 * LN2 + log(rs.Z)) : NAN;
+    if (P.err_flags) P.err_flags[r] = ok ? 0 : (!rp.got ? SV_ERR_INTERNAL : SV_ERR_ROW);
   }
 }
 
@@ -676,17 +873,17 @@ bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_BF16 || dt == SV_F16; }
 int64_t chunks_per_row(int64_t V, sv_dtype dt) {
   const int64_t W = 16 / elem_bytes(dt);
   const int64_t units = (V + W - 1) / W;
-  return (units + UNITS_PER_CHUNK - 1) / UNITS_PER_CHUNK;
+  return (units + CHUNK_UNITS - 1) / CHUNK_UNITS;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t off[8];
+  size_t off[12];
   size_t total;
 };
 
-// Record regions back to back, each 256-byte aligned.
+// Regions back to back, each 256-byte aligned.
 Layout make_layout(std::initializer_list<size_t> sizes) {
   Layout L{};
   size_t o = 0;
@@ -701,19 +898,22 @@ Layout make_layout(std::initializer_list<size_t> sizes) {
 
 Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
   const int64_t R = (mode == SV_STOCHASTIC) ? 2 * k + 1 : k + 1;
+  const int64_t RQ = B * R;
   const int64_t C = chunks_per_row(V, dt);
-  return make_layout({(size_t)(B * R * C) * PART_WORDS * 8, (size_t)(B * R) * ROW_WORDS * 8,
-                      (size_t)B * DEC_WORDS * 8, (size_t)(B * C) * RES_WORDS * 8});
+  return make_layout({(size_t)(RQ * C) * PART_WORDS * 8, (size_t)RQ * ROW_WORDS * 8, (size_t)B * DEC_WORDS * 8,
+                      (size_t)(B * C) * RES_WORDS * 8, (size_t)B * 8, (size_t)(RQ * CSTRIDE) * 4,
+                      (size_t)(B * k * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
+                      (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8});
 }
 
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
   const int64_t C = chunks_per_row(V, dt);
-  return make_layout({(size_t)(B * N * C) * PART_WORDS * 8, (size_t)(B * N) * 8});
+  return make_layout({(size_t)(B * N * C) * PART_WORDS * 8, (size_t)(B * N * CSTRIDE) * 4, (size_t)(B * N) * 4});
 }
 
 Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
   const int64_t C = chunks_per_row(V, dt);
-  return make_layout({(size_t)(rows * C) * PART_WORDS * 8});
+  return make_layout({(size_t)(rows * C) * PART_WORDS * 8, (size_t)(rows * CSTRIDE) * 4});
 }
 
 bool temperature_ok(float T) { return std::isfinite(T) && T > 0.0f; }
@@ -729,6 +929,8 @@ sv_status launch_status() {
 std::atomic<uint32_t> g_tag{0};
 uint32_t next_tag() { return (g_tag.fetch_add(1, std::memory_order_relaxed) << 1) | 1u; }
 
+unsigned blocks_for(int64_t waves) { return (unsigned)((waves + WPB - 1) / WPB); }
+
 template <template <int, bool> class Launcher, class... Args>
 sv_status dispatch(sv_dtype dt, bool stoch, Args&&... args) {
   switch (dt) {
@@ -742,8 +944,7 @@ sv_status dispatch(sv_dtype dt, bool stoch, Args&&... args) {
 template <int DT, bool STOCH>
 struct LinearLauncher {
   static sv_status run(const LinearParams& P, hipStream_t s) {
-    const int64_t G = P.n_stream + P.n_resid;
-    hipLaunchKernelGGL((linear_kernel<DT, STOCH>), dim3((unsigned)G), dim3(BLOCK), 0, s, P);
+    hipLaunchKernelGGL((linear_kernel<DT, STOCH>), dim3(blocks_for(P.n_stream + P.n_resid)), dim3(BLOCK), 0, s, P);
     return launch_status();
   }
 };
@@ -751,7 +952,9 @@ struct LinearLauncher {
 template <int DT, bool STOCH>
 struct TreeLauncher {
   static sv_status run(const TreeParams& P, size_t smem, hipStream_t s) {
-    hipLaunchKernelGGL((tree_kernel<DT, STOCH>), dim3((unsigned)P.n_stream), dim3(BLOCK), smem, s, P);
+    hipLaunchKernelGGL((tree_stream_kernel<DT, STOCH>), dim3(blocks_for(P.n_stream)), dim3(BLOCK), 0, s, P);
+    if (launch_status() != SV_OK) return SV_EHIP;
+    hipLaunchKernelGGL(tree_walk_kernel, dim3((unsigned)P.B), dim3(BLOCK), smem, s, P);
     return launch_status();
   }
 };
@@ -759,7 +962,7 @@ struct TreeLauncher {
 template <int DT, bool UNUSED>
 struct RowStatsLauncher {
   static sv_status run(const RowStatsParams& P, hipStream_t s) {
-    hipLaunchKernelGGL((row_stats_kernel<DT>), dim3((unsigned)P.n_stream), dim3(BLOCK), 0, s, P);
+    hipLaunchKernelGGL((row_stats_kernel<DT>), dim3(blocks_for(P.n_stream)), dim3(BLOCK), 0, s, P);
     return launch_status();
   }
 };
@@ -768,51 +971,11 @@ bool ws_ok(const void* ws, size_t have, size_t need) {
   return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0 && have >= need;
 }
 
-constexpr int64_t MAX_BLOCKS = 0x7fffffff - 1;
+// Waves of one launch, and rows x chunks as 32-bit indices.
+constexpr int64_t MAX_WAVES = 0x7fffffffLL;
 
-sv_status linear_entry(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
-                       sv_dtype dtype, const void* target_logits, const void* draft_logits,
-                       const int32_t* draft_tokens, const float* uniforms, int32_t* accept_len,
-                       int32_t* out_tokens, float* p_target, float* p_draft, int32_t* err_flags,
-                       void* workspace, size_t workspace_bytes, sv_stream_t stream) {
-  if (!dtype_ok(dtype)) return SV_EDTYPE;
-  if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
-  const bool stoch = (mode == SV_STOCHASTIC);
-  if (B < 0 || k < 0 || V < 1) return SV_EINVAL;
-  if (k > SV_MAX_K || V > 0x7fffffffLL - 16) return SV_ELIMIT;
-  if (chunks_per_row(V, dtype) > MAX_CHUNKS) return SV_ELIMIT;
-  if (B == 0) return SV_OK;
-  if (!target_logits || !accept_len || !out_tokens || (k > 0 && !draft_tokens)) return SV_EINVAL;
-  if (stoch && (!temperature_ok(temperature) || !uniforms || (k > 0 && !draft_logits))) return SV_EINVAL;
-  const Layout lay = linear_layout(B, k, V, dtype, mode);
-  if (!ws_ok(workspace, workspace_bytes, lay.total)) return SV_EWORKSPACE;
-
-  LinearParams P{};
-  P.target = static_cast<const char*>(target_logits);
-  P.draft = static_cast<const char*>(draft_logits);
-  P.tokens = draft_tokens;
-  P.uniforms = uniforms;
-  P.accept_len = accept_len;
-  P.out_tokens = out_tokens;
-  P.p_target = stoch ? p_target : nullptr;
-  P.p_draft = stoch ? p_draft : nullptr;
-  P.err_flags = err_flags;
-  char* ws = static_cast<char*>(workspace);
-  P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
-  P.rows = reinterpret_cast<uint64_t*>(ws + lay.off[1]);
-  P.dec = reinterpret_cast<uint64_t*>(ws + lay.off[2]);
-  P.res = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
-  P.B = B;
-  P.k = k;
-  P.V = V;
-  P.R = (int)(stoch ? 2 * k + 1 : k + 1);
-  P.C = (int)chunks_per_row(V, dtype);
-  P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  P.n_stream = B * P.R * P.C;
-  P.n_resid = (stoch && k > 0) ? B * P.C : 0;
-  if (P.n_stream + P.n_resid > MAX_BLOCKS) return SV_ELIMIT;
-  P.tag = next_tag();
-  return dispatch<LinearLauncher>(dtype, stoch, P, reinterpret_cast<hipStream_t>(stream));
+bool shape_ok(int64_t V, sv_dtype dt) {
+  return V <= 0x7fffffffLL - 16 && chunks_per_row(V, dt) <= MAX_CHUNKS;
 }
 
 }  // namespace
@@ -842,9 +1005,52 @@ sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t
                              int32_t* out_tokens, float* p_target, float* p_draft,
                              int32_t* err_flags, void* workspace, size_t workspace_bytes,
                              sv_stream_t stream) {
-  return linear_entry(mode, temperature, B, k, V, dtype, target_logits, draft_logits,
-                      draft_tokens, uniforms, accept_len, out_tokens, p_target, p_draft, err_flags,
-                      workspace, workspace_bytes, stream);
+  if (!dtype_ok(dtype)) return SV_EDTYPE;
+  if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
+  const bool stoch = (mode == SV_STOCHASTIC);
+  if (B < 0 || k < 0 || V < 1) return SV_EINVAL;
+  if (k > SV_MAX_K || !shape_ok(V, dtype)) return SV_ELIMIT;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !accept_len || !out_tokens || (k > 0 && !draft_tokens)) return SV_EINVAL;
+  if (stoch && (!temperature_ok(temperature) || !uniforms || (k > 0 && !draft_logits))) return SV_EINVAL;
+  const Layout lay = linear_layout(B, k, V, dtype, mode);
+  if (!ws_ok(workspace, workspace_bytes, lay.total)) return SV_EWORKSPACE;
+
+  LinearParams P{};
+  P.target = static_cast<const char*>(target_logits);
+  P.draft = static_cast<const char*>(draft_logits);
+  P.tokens = draft_tokens;
+  P.uniforms = uniforms;
+  P.accept_len = accept_len;
+  P.out_tokens = out_tokens;
+  P.p_target = stoch ? p_target : nullptr;
+  P.p_draft = stoch ? p_draft : nullptr;
+  P.err_flags = err_flags;
+  char* ws = static_cast<char*>(workspace);
+  P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
+  P.rows = reinterpret_cast<uint64_t*>(ws + lay.off[1]);
+  P.dec = reinterpret_cast<uint64_t*>(ws + lay.off[2]);
+  P.res = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
+  P.tok = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
+  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[5]);
+  P.pair_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[6]);
+  P.state = reinterpret_cast<uint64_t*>(ws + lay.off[7]);
+  P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
+  P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
+  P.errw = reinterpret_cast<uint32_t*>(ws + lay.off[10]);
+  P.prob = reinterpret_cast<uint64_t*>(ws + lay.off[11]);
+  P.B = B;
+  P.k = k;
+  P.V = V;
+  P.R = (int)(stoch ? 2 * k + 1 : k + 1);
+  P.C = (int)chunks_per_row(V, dtype);
+  P.CP = (P.C + WPB - 1) / WPB * WPB;
+  P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
+  P.n_stream = B * P.R * P.CP;
+  P.n_resid = (stoch && k > 0) ? B * P.C : 0;
+  if (P.n_stream + P.n_resid > MAX_WAVES) return SV_ELIMIT;
+  P.tag = next_tag();
+  return dispatch<LinearLauncher>(dtype, stoch, P, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t spec_verify_tree_workspace(int64_t B, int64_t n_nodes, int64_t V, sv_dtype dtype, sv_mode mode) {
@@ -863,8 +1069,7 @@ sv_status spec_verify_tree(sv_mode mode, float temperature, int64_t B, int64_t n
   if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
   const bool stoch = (mode == SV_STOCHASTIC);
   if (B < 0 || n_nodes < 1 || V < 1 || max_depth < 0 || parent_batch_stride < 0) return SV_EINVAL;
-  if (n_nodes > SV_MAX_TREE_NODES || V > 0x7fffffffLL - 16) return SV_ELIMIT;
-  if (chunks_per_row(V, dtype) > MAX_CHUNKS) return SV_ELIMIT;
+  if (n_nodes > SV_MAX_TREE_NODES || !shape_ok(V, dtype)) return SV_ELIMIT;
   if (B == 0) return SV_OK;
   if (!parent || !cand_tokens || !target_logits || !accept_len || !out_tokens) return SV_EINVAL;
   if (max_depth > 0 && !path_nodes) return SV_EINVAL;
@@ -884,15 +1089,17 @@ sv_status spec_verify_tree(sv_mode mode, float temperature, int64_t B, int64_t n
   P.err_flags = err_flags;
   char* ws = static_cast<char*>(workspace);
   P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
-  P.node_y = reinterpret_cast<uint64_t*>(ws + lay.off[1]);
+  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[1]);
+  P.node_y = reinterpret_cast<int32_t*>(ws + lay.off[2]);
   P.B = B;
   P.N = n_nodes;
   P.V = V;
   P.max_depth = max_depth;
   P.C = (int)chunks_per_row(V, dtype);
+  P.CP = (P.C + WPB - 1) / WPB * WPB;
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  P.n_stream = B * n_nodes * P.C;
-  if (P.n_stream > MAX_BLOCKS) return SV_ELIMIT;
+  P.n_stream = B * n_nodes * P.CP;
+  if (P.n_stream > MAX_WAVES || B > 0x7fffffffLL) return SV_ELIMIT;
   P.tag = next_tag();
   // LDS of the path search: parent (2 B) + match flag (1 B) per node
   const size_t smem = (size_t)((3 * n_nodes + 15) & ~(int64_t)15);
@@ -909,7 +1116,7 @@ sv_status spec_row_stats(sv_dtype dtype, float temperature, int64_t rows, int64_
                          void* workspace, size_t workspace_bytes, sv_stream_t stream) {
   if (!dtype_ok(dtype)) return SV_EDTYPE;
   if (rows < 0 || V < 1 || !temperature_ok(temperature)) return SV_EINVAL;
-  if (V > 0x7fffffffLL - 16 || chunks_per_row(V, dtype) > MAX_CHUNKS) return SV_ELIMIT;
+  if (!shape_ok(V, dtype)) return SV_ELIMIT;
   if (rows == 0) return SV_OK;
   if (!x) return SV_EINVAL;
   const Layout lay = rowstats_layout(rows, V, dtype);
@@ -922,12 +1129,14 @@ sv_status spec_row_stats(sv_dtype dtype, float temperature, int64_t rows, int64_
   P.err_flags = err_flags;
   char* ws = static_cast<char*>(workspace);
   P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
+  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[1]);
   P.rows = rows;
   P.V = V;
   P.C = (int)chunks_per_row(V, dtype);
+  P.CP = (P.C + WPB - 1) / WPB * WPB;
   P.c0 = temperature_c0(temperature);
-  P.n_stream = rows * P.C;
-  if (P.n_stream > MAX_BLOCKS) return SV_ELIMIT;
+  P.n_stream = rows * P.CP;
+  if (P.n_stream > MAX_WAVES) return SV_ELIMIT;
   P.tag = next_tag();
   return dispatch<RowStatsLauncher>(dtype, false, P, reinterpret_cast<hipStream_t>(stream));
 }

@@ -1,30 +1,34 @@
 // Device building blocks for libspecverify (gfx950, wave64).
 //
-// Data path: logits rows are streamed in 16-byte units (8 bf16/fp16 or 4 fp32
-// values per lane per load). A "chunk" is BLOCK * UNROLL units (16 KiB) handled
-// by one 256-thread workgroup; thread t owns units unit0 + j*BLOCK + t, j < UNROLL,
-// so every load instruction of a wave reads 1 KiB of contiguous memory.
+// Work is split into waves, not workgroups: a 256-thread workgroup holds four
+// wave64s that never synchronise with each other, so one wave's arithmetic
+// overlaps the others' memory traffic. A wave streams one chunk of one row: lane l
+// owns the 16-byte units u0 + j*64 + l (j < CU), so every load instruction reads
+// 1 KiB of contiguous memory and a chunk is CU KiB (8 KiB: 4096 bf16/fp16 or 2048
+// fp32 logits).
 //
-// Arithmetic (all of it the row softmax at temperature T, computed in base 2):
+// Arithmetic (the row softmax at temperature T, in base 2):
 //   c0 = log2(e)/T (fp32).  Chunk max m_c; mc0 = fl32(m_c * c0).
 //   element weight  w = exp2(fma(x, c0, -mc0))            (fp32, v_exp_f32)
 //   unit sum        pairwise fp32 sum of the unit's W weights
-//   chunk sum s_c   per-thread fp64 sum of its unit sums, then a fixed-order
-//                   fp64 butterfly across the wave and the 4 waves.
+//   chunk sum s_c   per-lane fp64 sum of its unit sums, then a fixed fp64
+//                   butterfly across the wave
 //   row normaliser  Z = sum_c s_c * 2^(mc0_c - M*c0)       (fp64, M = row max)
 // Every reduction has a fixed order, so results are bit-identical run to run, and
-// any code that recomputes a weight uses the same expression as the pass that
-// summed it (the inverse-CDF scan relies on that).
+// code that recomputes a weight uses the same expression as the pass that summed it.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace sv {
 
+constexpr int WAVE = 64;
 constexpr int BLOCK = 256;
-constexpr int NWAVES = BLOCK / 64;
-constexpr int UNROLL = 4;
-constexpr int UNITS_PER_CHUNK = BLOCK * UNROLL;
+constexpr int WPB = BLOCK / WAVE;               // independent waves per workgroup
+constexpr int CU = 8;                           // 16-byte units per lane per chunk
+constexpr int CHUNK_UNITS = WAVE * CU;          // 512 units = 8 KiB
+constexpr int MAX_ROUNDS = 4;                   // chunks per lane in a row combine
+constexpr int MAX_CHUNKS = WAVE * MAX_ROUNDS;   // chunks per row
 constexpr int INT_SENTINEL = 0x7fffffff;
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -37,21 +41,66 @@ template <> struct DTraits<DT_F16>  { static constexpr int W = 8; static constex
 // Per-(row, chunk) partial statistics.
 struct Partial {
   float m;     // chunk max (-inf if no entry above -inf)
-  int idx;     // lowest row index holding m (INT_SENTINEL if none)
-  double s;    // sum of exp2(fma(x, c0, -fl32(m*c0))) over the chunk (stochastic only)
+  int idx;     // lowest row index holding m (INT_SENTINEL if none; argmax mode only)
+  double s;    // sum of exp2(fma(x, c0, -fl32(m*c0))) over the chunk (softmax mode only)
+  float xv;    // the logit at the row's draft token, if this chunk holds it
+  int xin;     // 1 if this chunk holds the draft token
 };
 
-// Per-row statistics written by the last chunk block of the row.
+// Per-row statistics, written by the wave that combines the row.
 struct RowStat {
   double Z;    // sum_v 2^(x_v*c0 - M*c0), M*c0 in fp64
+  double px;   // softmax probability of the row's draft token (draft/target pair rows)
   float M;     // row max
   int argmax;  // lowest index of M, -1 if none
-  int ok;      // 1 if the row is usable in the current mode
-  int y;       // token chosen at this row (argmax, or an inverse-CDF draw), -1 if none
-  int pad0, pad1;
+  int ok;      // 1 usable, 0 data error, -1 a wait timed out
+  int y;       // token drawn at this row (bonus row, tree nodes), -1 if none
 };
 
-// ------------------------------------------------------------------ loads
+// ------------------------------------------------------------------ lanes and waves
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+__device__ __forceinline__ int wave_in_block() { return threadIdx.x / WAVE; }
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+// (value, index): larger value wins, lower index on equal values.
+__device__ __forceinline__ void argmax_combine(float& m, int& i, float m2, int i2) {
+  if (m2 > m || (m2 == m && i2 < i)) { m = m2; i = i2; }
+}
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int i2 = __shfl_xor(i, o);
+    argmax_combine(m, i, m2, i2);
+  }
+}
+// Inclusive prefix sum over the 64 lanes in lane order (Hillis-Steele).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const double t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ int first_lane(unsigned long long mask) { return mask ? __builtin_ctzll(mask) : -1; }
+
+// ------------------------------------------------------------------ element decoding
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
@@ -82,120 +131,6 @@ __device__ __forceinline__ void decode_unit(const uint4 v, float (&x)[DTraits<DT
   }
 }
 
-// Load unit `unit` of a row: W consecutive elements starting at unit*W.
-// Elements at or past V read as -inf (zero weight, never a maximum).
-// Used for single units (the scan's final unit); chunks use load_chunk.
-template <int DT>
-__device__ __forceinline__ void load_unit(const char* row, int64_t V, int64_t unit, bool aligned,
-                                 float (&x)[DTraits<DT>::W]) {
-  constexpr int W = DTraits<DT>::W;
-  constexpr int E = DTraits<DT>::E;
-  const int64_t e0 = unit * W;
-  if (aligned && e0 + W <= V) {
-    const uint4 v = *reinterpret_cast<const uint4*>(row + e0 * E);
-    decode_unit<DT>(v, x);
-  } else {
-#pragma unroll
-    for (int e = 0; e < W; ++e) x[e] = (e0 + e < V) ? load_elem<DT>(row, e0 + e) : -INFINITY;
-  }
-}
-
-// A chunk's raw 16-byte words for one thread (UNROLL units), as loaded.
-struct ChunkRaw {
-  uint4 v[UNROLL];
-};
-
-// Issue this thread's UNROLL vector loads of a chunk (units unit0 + j*BLOCK + tid)
-// without waiting: addresses are clamped to units lying entirely inside the row.
-// Rows that do not start on a 16-byte boundary load nothing here (decode_chunk
-// reads them element by element).
-template <int DT>
-__device__ __forceinline__ void load_chunk_raw(const char* row, int64_t V, int64_t unit0, bool aligned,
-                                               ChunkRaw& raw) {
-  constexpr int W = DTraits<DT>::W;
-  constexpr int E = DTraits<DT>::E;
-  const int64_t nfull = V / W;                 // units lying entirely inside the row
-  if (aligned && nfull > 0) {
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      const int64_t u = unit0 + j * BLOCK + threadIdx.x;
-      const int64_t uc = (u < nfull) ? u : nfull - 1;
-      raw.v[j] = *reinterpret_cast<const uint4*>(row + uc * (W * E));
-    }
-  }
-}
-
-// Decode a chunk loaded by load_chunk_raw; units (partly) past V and rows that do
-// not start on a 16-byte boundary are read element by element here (entries past
-// V read as -inf).
-template <int DT>
-__device__ __forceinline__ void decode_chunk(const char* row, int64_t V, int64_t unit0, bool aligned,
-                                             const ChunkRaw& raw, float (&x)[UNROLL][DTraits<DT>::W]) {
-  constexpr int W = DTraits<DT>::W;
-  const int64_t nfull = V / W;
-  if (aligned && nfull > 0) {
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      decode_unit<DT>(raw.v[j], x[j]);
-      const int64_t u = unit0 + j * BLOCK + threadIdx.x;
-      if (u >= nfull) {
-#pragma unroll
-        for (int e = 0; e < W; ++e) {
-          const int64_t i = u * W + e;
-          x[j][e] = (i < V) ? load_elem<DT>(row, i) : -INFINITY;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      const int64_t u = unit0 + j * BLOCK + threadIdx.x;
-#pragma unroll
-      for (int e = 0; e < W; ++e) {
-        const int64_t i = u * W + e;
-        const float v = load_elem<DT>(row, i < V ? i : V - 1);
-        x[j][e] = (i < V) ? v : -INFINITY;
-      }
-    }
-  }
-}
-
-// Decode unit j of this thread from a raw chunk (see decode_chunk).
-template <int DT>
-__device__ __forceinline__ void decode_unit_at(const char* row, int64_t V, int64_t unit0, bool aligned,
-                                               const ChunkRaw& raw, int j, float (&x)[DTraits<DT>::W]) {
-  constexpr int W = DTraits<DT>::W;
-  const int64_t nfull = V / W;
-  const int64_t u = unit0 + j * BLOCK + threadIdx.x;
-  if (aligned && nfull > 0) {
-    decode_unit<DT>(raw.v[j], x);
-    if (u >= nfull) {
-#pragma unroll
-      for (int e = 0; e < W; ++e) {
-        const int64_t i = u * W + e;
-        x[e] = (i < V) ? load_elem<DT>(row, i) : -INFINITY;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      const int64_t i = u * W + e;
-      const float v = load_elem<DT>(row, i < V ? i : V - 1);
-      x[e] = (i < V) ? v : -INFINITY;
-    }
-  }
-}
-
-// Load and decode this thread's UNROLL units of a chunk, every vector load issued
-// before any result is used.
-template <int DT>
-__device__ __forceinline__ void load_chunk(const char* row, int64_t V, int64_t unit0, bool aligned,
-                                           float (&x)[UNROLL][DTraits<DT>::W]) {
-  ChunkRaw raw;
-  load_chunk_raw<DT>(row, V, unit0, aligned, raw);
-  decode_chunk<DT>(row, V, unit0, aligned, raw, x);
-}
-
 __device__ __forceinline__ bool row_aligned(const char* row) { return (reinterpret_cast<uintptr_t>(row) & 15u) == 0; }
 
 // ------------------------------------------------------------------ arithmetic
@@ -212,146 +147,389 @@ __device__ __forceinline__ float pairwise_sum(const float (&w)[W]) {
   }
 }
 
+template <int W>
+__device__ __forceinline__ float max_of(const float (&x)[W]) {
+  if constexpr (W == 8) {
+    return fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  } else {
+    return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  }
+}
+
 // m*c0 in fp32 as used for the chunk's weights; 0 for an empty (-inf) chunk so
 // that its -inf entries weigh exp2(-inf) = 0 instead of NaN.
 __device__ __forceinline__ float chunk_mc0(float m, float c0) { return (m == -INFINITY) ? 0.0f : m * c0; }
 
-// ------------------------------------------------------------------ reductions
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
-
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-// (value, index): larger value wins, lower index on equal values.
-__device__ __forceinline__ void argmax_combine(float& m, int& i, float m2, int i2) {
-  if (m2 > m || (m2 == m && i2 < i)) { m = m2; i = i2; }
-}
-__device__ __forceinline__ void wave_argmax(float& m, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o);
-    const int i2 = __shfl_xor(i, o);
-    argmax_combine(m, i, m2, i2);
-  }
-}
-
-// Inclusive prefix sum over the 64 lanes (lane order), Hillis-Steele.
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-struct BlockScratch {
-  double d[NWAVES];
-  float f[NWAVES];
-  int i[NWAVES];
-  int flag;
-  int64_t result;
-  double theta;
+// ------------------------------------------------------------------ chunks
+// Chunk c of a row: units [c*CHUNK_UNITS, (c+1)*CHUNK_UNITS). Every chunk is
+// brought into the same register layout, a lane's CU units as packed 16-byte
+// words: units inside the row of a 16-byte aligned row are vector loads; the unit
+// that straddles the row end, and every unit of a row that does not start on a
+// 16-byte boundary, are assembled element by element; entries at or past V hold
+// -inf (no weight, never a maximum).
+struct Chunk {
+  const char* row;
+  int64_t V;
+  int64_t u0;
 };
 
-__device__ __forceinline__ double block_sum(double v, BlockScratch& sm) {
-  v = wave_sum(v);
-  if (lane_id() == 0) sm.d[wave_id()] = v;
-  __syncthreads();
-  double r = sm.d[0];
-#pragma unroll
-  for (int w = 1; w < NWAVES; ++w) r += sm.d[w];
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ float block_max(float v, BlockScratch& sm) {
-  v = wave_max(v);
-  if (lane_id() == 0) sm.f[wave_id()] = v;
-  __syncthreads();
-  float r = sm.f[0];
-#pragma unroll
-  for (int w = 1; w < NWAVES; ++w) r = fmaxf(r, sm.f[w]);
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ int block_max_int(int v, BlockScratch& sm) {
-  v = wave_max_int(v);
-  if (lane_id() == 0) sm.i[wave_id()] = v;
-  __syncthreads();
-  int r = sm.i[0];
-#pragma unroll
-  for (int w = 1; w < NWAVES; ++w) r = max(r, sm.i[w]);
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ int block_sum_int(int v, BlockScratch& sm) {
-  v = wave_sum_int(v);
-  if (lane_id() == 0) sm.i[wave_id()] = v;
-  __syncthreads();
-  int r = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVES; ++w) r += sm.i[w];
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ void block_argmax(float& m, int& idx, BlockScratch& sm) {
-  wave_argmax(m, idx);
-  if (lane_id() == 0) { sm.f[wave_id()] = m; sm.i[wave_id()] = idx; }
-  __syncthreads();
-  float rm = sm.f[0];
-  int ri = sm.i[0];
-#pragma unroll
-  for (int w = 1; w < NWAVES; ++w) argmax_combine(rm, ri, sm.f[w], sm.i[w]);
-  __syncthreads();
-  m = rm;
-  idx = ri;
-}
-// Block-wide inclusive and exclusive prefix sums in thread order.
-__device__ __forceinline__ void block_scan(double v, double& incl, double& excl, BlockScratch& sm) {
-  const double wi = wave_incl_scan(v);
-  const double prev = __shfl_up(wi, 1);
-  if (lane_id() == 63) sm.d[wave_id()] = wi;
-  __syncthreads();
-  double off = 0.0;
-  for (int w = 0; w < wave_id(); ++w) off += sm.d[w];
-  __syncthreads();
-  incl = off + wi;
-  excl = (lane_id() == 0) ? off : off + prev;
+struct Raw {
+  uint4 v[CU];
+};
+
+template <int DT>
+__device__ __forceinline__ uint32_t neg_inf_bits() {
+  if constexpr (DT == DT_F32) return 0xff800000u;
+  else if constexpr (DT == DT_BF16) return 0xff80ff80u;
+  else return 0xfc00fc00u;
 }
 
-// ------------------------------------------------------------------ cross-workgroup records
-// Workgroups hand data to each other inside one launch without fences and
-// without atomics: a record is an array of 8-byte words, each holding a 32-bit
-// value and the 32-bit tag of the call that wrote it. The writer stores the words
-// with device-coherent 8-byte stores and moves on; the record's one reader polls
-// them with device-coherent loads until every word carries the call's tag, then
-// clears the words (tag 0). A word is written and read whole, so a matching tag
-// means its value is this call's. Every call draws a fresh odd tag, and every
-// record is cleared by its reader, so neither an earlier call's words nor those of
-// an earlier replay of the same captured graph can ever match.
+// Unit u assembled element by element (entries past V are -inf).
+template <int DT>
+__device__ __forceinline__ uint4 unit_by_elements(const char* row, int64_t V, int64_t u) {
+  constexpr int W = DTraits<DT>::W;
+  const uint32_t ninf = neg_inf_bits<DT>();
+  uint32_t w[4] = {ninf, ninf, ninf, ninf};
+  const int64_t e0 = u * W;
+  if constexpr (DT == DT_F32) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(row);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e0 + e < V) w[e] = p[e0 + e];
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(row);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e0 + e < V) {
+        const uint32_t h = p[e0 + e];
+        w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000ffffu) | (h << 16)) : ((w[e >> 1] & 0xffff0000u) | h);
+      }
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Loads this lane's CU units of chunk c.
+template <int DT>
+__device__ __forceinline__ Chunk load_chunk(const char* row, int64_t V, int64_t c, Raw& r) {
+  constexpr int W = DTraits<DT>::W;
+  Chunk k;
+  k.row = row;
+  k.V = V;
+  k.u0 = c * CHUNK_UNITS;
+  const int lane = lane_id();
+  const bool aligned = row_aligned(row);
+  if (aligned && (k.u0 + CHUNK_UNITS) * W <= V) {
+    // the common case: the whole chunk is inside an aligned row
+    const uint4* p = reinterpret_cast<const uint4*>(row) + k.u0 + lane;
+#pragma unroll
+    for (int j = 0; j < CU; ++j) r.v[j] = p[j * WAVE];
+  } else {
+    const uint32_t ninf = neg_inf_bits<DT>();
+#pragma unroll
+    for (int j = 0; j < CU; ++j) {
+      const int64_t u = k.u0 + j * WAVE + lane;
+      if (aligned && (u + 1) * W <= V) {
+        r.v[j] = reinterpret_cast<const uint4*>(row)[u];
+      } else if (u * W < V) {
+        r.v[j] = unit_by_elements<DT>(row, V, u);
+      } else {
+        r.v[j] = make_uint4(ninf, ninf, ninf, ninf);
+      }
+    }
+  }
+  return k;
+}
+
+// The W values of this lane's unit j.
+template <int DT>
+__device__ __forceinline__ void unit_values(const Raw& r, int j, float (&x)[DTraits<DT>::W]) {
+  decode_unit<DT>(r.v[j], x);
+}
+
+// Partial of a chunk (same value in every lane): max, with the lowest index
+// holding it if ARG (NaN never chosen), if SUM the weight sum relative to
+// fl32(max*c0), and the logit at row index x if the chunk holds it (x < 0: none).
+template <int DT, bool SUM, bool ARG>
+__device__ __forceinline__ Partial chunk_reduce(const Chunk& k, const Raw& r, float c0, int64_t x) {
+  constexpr int W = DTraits<DT>::W;
+  float best = -INFINITY;
+  int pos = INT_SENTINEL;
+#pragma unroll
+  for (int j = 0; j < CU; ++j) {
+    float x[W];
+    unit_values<DT>(r, j, x);
+    if constexpr (ARG) {
+      const int base = (int)((k.u0 + j * WAVE + lane_id()) * W);
+#pragma unroll
+      for (int e = 0; e < W; ++e)
+        if (x[e] > best) { best = x[e]; pos = base + e; }
+    } else {
+      best = fmaxf(best, max_of<W>(x));
+    }
+  }
+  Partial p;
+  if constexpr (ARG) {
+    wave_argmax(best, pos);
+    p.m = best;
+    p.idx = pos;
+  } else {
+    p.m = wave_max(best);
+    p.idx = INT_SENTINEL;
+  }
+  p.s = 0.0;
+  if constexpr (SUM) {
+    const float mc0 = chunk_mc0(p.m, c0);
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < CU; ++j) {
+      float w[W];
+      unit_values<DT>(r, j, w);
+#pragma unroll
+      for (int e = 0; e < W; ++e) w[e] = softmax_weight(w[e], c0, mc0);
+      s += (double)pairwise_sum<W>(w);
+    }
+    p.s = wave_sum(s);
+  }
+  p.xv = 0.0f;
+  p.xin = 0;
+  const int64_t ux = x >= 0 ? x / W - k.u0 : -1;   // the unit holding x, relative to the chunk
+  if (ux >= 0 && ux < CHUNK_UNITS && x < k.V) {
+    const int jx = (int)(ux / WAVE), lx = (int)(ux % WAVE), ex = (int)(x % W);
+    float v = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CU; ++j) {
+      if (j == jx) {
+        float xs[W];
+        unit_values<DT>(r, j, xs);
+#pragma unroll
+        for (int e = 0; e < W; ++e) if (e == ex) v = xs[e];
+      }
+    }
+    p.xv = __shfl(v, lx);
+    p.xin = 1;
+  }
+  return p;
+}
+
+// Loads chunk c of a row and reduces it.
+template <int DT, bool SUM, bool ARG>
+__device__ __forceinline__ Partial chunk_partial(const char* row, int64_t V, int64_t c, float c0, int64_t x = -1) {
+  Raw r;
+  const Chunk k = load_chunk<DT>(row, V, c, r);
+  return chunk_reduce<DT, SUM, ARG>(k, r, c0, x);
+}
+
+// 2^d for d <= 0 (fp64), as 2^floor(d) * exp2f(frac(d)): relative error ~1e-7.
+__device__ __forceinline__ double pow2_neg(double d) {
+  if (!(d > -1000.0)) return (d != d) ? d : 0.0;   // NaN stays NaN; far below: 0
+  const double di = floor(d);
+  return ldexp((double)__builtin_amdgcn_exp2f((float)(d - di)), (int)di);
+}
+
+// Streaming waves of one launch: rows are processed in groups of 8 consecutive
+// rows, and every chunk of a row runs on the same XCD (workgroups are dispatched
+// round-robin over the 8 XCDs): row q on XCD q % 8. The chunks of a row are
+// padded to a multiple of 4 waves (CP) so that no workgroup spans two rows;
+// padding waves have c >= C and do nothing. RQ rows.
+__device__ __forceinline__ void stream_coords(uint32_t w, uint32_t CP, uint32_t RQ, uint32_t& q, uint32_t& c) {
+  const uint32_t bpr = CP / WPB;           // workgroups per row
+  const uint32_t h = w / WPB, lw = w % WPB;
+  const uint32_t G = 8 * bpr;              // workgroups per group of 8 rows
+  const uint32_t g = h / G, hb = h - g * G;
+  const uint32_t rows = min(8u, RQ - 8 * g);
+  uint32_t r, jb;
+  if (rows == 8) {
+    r = hb % 8;
+    jb = hb / 8;
+  } else {
+    r = hb / bpr;
+    jb = hb - r * bpr;
+  }
+  q = 8 * g + r;
+  c = jb * WPB + lw;
+}
+
+// ------------------------------------------------------------------ inverse CDF inside one chunk
+// Weight functors: softmax weights of one row, or the residual max(0, p_t - p_d)
+// of a (target, draft) row pair.
+struct SoftmaxW {
+  float c0, mc0;
+  __device__ __forceinline__ float operator()(float x, float) const { return softmax_weight(x, c0, mc0); }
+};
+struct ResidW {
+  float c0, mc0t, mc0d, izt, izd;
+  __device__ __forceinline__ float operator()(float xt, float xd) const {
+    const float pt = softmax_weight(xt, c0, mc0t) * izt;
+    const float pd = softmax_weight(xd, c0, mc0d) * izd;
+    return fmaxf(pt - pd, 0.0f);
+  }
+};
+
+// Weights of this lane's unit j (j a compile-time constant after unrolling).
+template <int DT, bool PAIR, class WT>
+__device__ __forceinline__ void unit_weights(const Raw& ra, const Raw& rb, int j, const WT& wt,
+                                             float (&w)[DTraits<DT>::W]) {
+  constexpr int W = DTraits<DT>::W;
+  float xa[W], xb[W];
+  decode_unit<DT>(ra.v[j], xa);
+  if constexpr (PAIR) decode_unit<DT>(rb.v[j], xb);
+#pragma unroll
+  for (int e = 0; e < W; ++e) w[e] = wt(xa[e], PAIR ? xb[e] : 0.0f);
+}
+
+// The row index of the first element of the chunk (in row order) whose
+// cumulative weight exceeds th, or, if rounding leaves none, of the last element
+// of positive weight; -1 if the chunk has no positive weight. Same value in
+// every lane. PAIR: weights of the element pairs of ra (target) and rb (draft).
 //
-// A workgroup only ever waits for records of workgroups with a lower dispatch
-// index, which were dispatched before it and are resident or finished; waits are
-// bounded all the same (about 0.2 s), and a timeout is reported as an error.
+// Units in row order are j-major, lane-minor. The search first finds the unit row
+// j whose running total crosses th (fp64 wave totals), then the lane inside it
+// (one fp64 prefix scan), then the element inside that unit.
+template <int DT, bool PAIR, class WT>
+__device__ __forceinline__ int64_t chunk_invcdf(const Chunk& k, const Raw& ra, const Raw& rb, double th,
+                                                const WT& wt) {
+  constexpr int W = DTraits<DT>::W;
+  const int lane = lane_id();
+  float us[CU];
+#pragma unroll
+  for (int j = 0; j < CU; ++j) {
+    float w[W];
+    unit_weights<DT, PAIR>(ra, rb, j, wt, w);
+    us[j] = pairwise_sum<W>(w);
+  }
+  double off = 0.0, offj = 0.0;
+  int hj = -1;
+#pragma unroll
+  for (int j = 0; j < CU; ++j) {
+    const double t = wave_sum((double)us[j]);
+    if (hj < 0 && off + t > th) { hj = j; offj = off; }
+    off += t;
+  }
+  int key = -1;     // (unit row, lane) of the unit holding the answer
+  bool scan = false;
+  double hexcl = 0.0;
+  if (hj >= 0) {
+    float uj = us[0];
+#pragma unroll
+    for (int j = 1; j < CU; ++j) if (j == hj) uj = us[j];
+    const double incl = wave_incl_scan((double)uj);
+    const unsigned long long hit = __ballot(offj + incl > th);
+    if (hit) {
+      const int hl = first_lane(hit);
+      key = hj * WAVE + hl;
+      hexcl = offj + __shfl(incl, hl) - (double)__shfl(uj, hl);
+      scan = true;
+    } else {
+      // rounding between the two sums: the last positive unit of that row
+      key = wave_max_int(uj > 0.0f ? hj * WAVE + lane : -1);
+    }
+  }
+  if (key < 0) {
+    // no crossing: the last unit of positive weight in the chunk
+#pragma unroll
+    for (int j = 0; j < CU; ++j) if (us[j] > 0.0f) key = j * WAVE + lane;
+    key = wave_max_int(key);
+    if (key < 0) return -1;
+  }
+  const int kj = key / WAVE, kl = key % WAVE;
+  // the unit's weights, selected by a branch per unit row (wave-uniform) so that
+  // the register array is never indexed at run time
+  float w[W];
+#pragma unroll
+  for (int e = 0; e < W; ++e) w[e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CU; ++j)
+    if (j == kj) unit_weights<DT, PAIR>(ra, rb, j, wt, w);
+  int pick = -1;
+  if (lane == kl) {
+    if (scan) {
+      double cum = hexcl;
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        cum += (double)w[e];
+        if (pick < 0 && cum > th) pick = e;
+      }
+    }
+    if (pick < 0) {   // rounding inside the unit, or no crossing: its last positive element
+#pragma unroll
+      for (int e = 0; e < W; ++e) if (w[e] > 0.0f) pick = e;
+    }
+  }
+  pick = __shfl(pick, kl);
+  return (k.u0 + kj * WAVE + kl) * W + pick;
+}
+
+// ------------------------------------------------------------------ chunk selection over a row
+// Chunk weights held lane-strided: lane l holds chunks l + 64*t (t < MAX_ROUNDS),
+// zero past C. Picks the first chunk (row order) whose inclusive prefix exceeds
+// u * total.
+struct ChunkPick {
+  int c;          // chosen chunk; -1 if the total is not a positive finite number
+  double before;  // sum of the weights of the chunks before c
+  double theta;   // u * total
+  bool fallback;  // rounding left no crossing: c is the last chunk of positive weight
+};
+
+__device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&wl)[MAX_ROUNDS]) {
+  const int lane = lane_id();
+  ChunkPick r;
+  r.c = -1;
+  r.before = 0.0;
+  r.theta = 0.0;
+  r.fallback = false;
+  double tr[MAX_ROUNDS];
+  double tot = 0.0;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    tr[t] = (t * WAVE < C) ? wave_sum(wl[t]) : 0.0;
+    tot += tr[t];
+  }
+  if (!(tot > 0.0) || !__builtin_isfinite(tot)) return r;
+  const double theta = u * tot;
+  r.theta = theta;
+  double off = 0.0, offt = 0.0;
+  int ht = -1;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    if (ht < 0 && off + tr[t] > theta) { ht = t; offt = off; }
+    off += tr[t];
+  }
+  if (ht >= 0) {
+    double wt = wl[0];
+#pragma unroll
+    for (int t = 1; t < MAX_ROUNDS; ++t) if (t == ht) wt = wl[t];
+    const double incl = wave_incl_scan(wt);
+    const unsigned long long hit = __ballot(offt + incl > theta && ht * WAVE + lane < C);
+    if (hit) {
+      const int l = first_lane(hit);
+      r.c = ht * WAVE + l;
+      r.before = offt + __shfl(incl, l) - __shfl(wt, l);
+      return r;
+    }
+  }
+  int last = -1;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t)
+    if (t * WAVE + lane < C && wl[t] > 0.0) last = t * WAVE + lane;
+  r.c = wave_max_int(last);
+  r.fallback = true;
+  return r;
+}
+
+// ------------------------------------------------------------------ cross-wave records
+// Waves hand data to each other inside one launch without fences: a record is an
+// array of 8-byte words, each holding a 32-bit value and the 32-bit tag of the
+// call that wrote it. The writer stores the words with device-coherent 8-byte
+// stores; a reader polls them with device-coherent loads until every word carries
+// the call's tag. A word is written and read whole, so a matching tag means its
+// value is this call's. Every record is cleared (tag 0) by the last wave that
+// reads it, so records of an earlier call, or of an earlier replay of a captured
+// graph that carries the same tag, never match.
+//
+// Which wave is "last" is decided by device-scope atomic counters in the same
+// workspace; each is reset to zero by the wave that sees it reach its final count.
+// Waits are bounded; a timeout is reported as an error, never a hang.
 constexpr int SPIN_LIMIT = 1 << 18;
 
 template <class T>
@@ -390,7 +568,18 @@ __device__ __forceinline__ bool get_rec(const uint64_t* src, T& v, uint32_t tag)
   return false;
 }
 
-// Clears a consumed record (its reader does this once it has read it).
+// Polls only the record's first word, with a longer pause between polls, then
+// reads the whole record: for waits that may last a while.
+template <class T>
+__device__ __forceinline__ bool poll_rec(const uint64_t* src, T& v, uint32_t tag) {
+  for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
+    const uint64_t x = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(x >> 32) == tag) return get_rec(src, v, tag);
+    __builtin_amdgcn_s_sleep(8);
+  }
+  return false;
+}
+
 template <class T>
 __device__ __forceinline__ void clear_rec(uint64_t* dst) {
 #pragma unroll
@@ -398,289 +587,18 @@ __device__ __forceinline__ void clear_rec(uint64_t* dst) {
     __hip_atomic_store(dst + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Logical block index with consecutive indices placed on the same XCD:
-// workgroups are dispatched round-robin over the 8 XCDs, so hardware block b runs
-// on XCD b % 8. This makes the chunks of one row share that XCD's L2.
-__device__ __forceinline__ int64_t xcd_logical_block(int64_t hw, int64_t nblocks) {
-  constexpr int64_t NX = 8;
-  const int64_t xcd = hw % NX, local = hw / NX;
-  const int64_t base = nblocks / NX, rem = nblocks % NX;
-  return xcd * base + (xcd < rem ? xcd : rem) + local;
+__device__ __forceinline__ uint32_t counter_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// ------------------------------------------------------------------ chunk statistics
-// Reduces one chunk, loaded raw by load_chunk_raw, to its partial (same value in
-// every thread): max with lowest index (if ARG), and the weight sum relative to
-// fl32(m*c0) (if SUM). Units are decoded on the fly in each pass, so only the raw
-// words stay live across the block reduction.
-template <int DT, bool SUM, bool ARG>
-__device__ __forceinline__ Partial reduce_chunk(const char* row, int64_t V, int64_t unit0, bool aligned,
-                                                const ChunkRaw& raw, float c0, BlockScratch& sm) {
-  constexpr int W = DTraits<DT>::W;
-  const int tid = threadIdx.x;
-  float best = -INFINITY;
-  int pos = INT_SENTINEL;
-#pragma unroll
-  for (int j = 0; j < UNROLL; ++j) {
-    float x[W];
-    decode_unit_at<DT>(row, V, unit0, aligned, raw, j, x);
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      if constexpr (ARG) {
-        if (x[e] > best) { best = x[e]; pos = j * W + e; }
-      } else {
-        best = fmaxf(best, x[e]);
-      }
-    }
-  }
-  Partial p;
-  p.s = 0.0;
-  if constexpr (ARG) {
-    int gidx = INT_SENTINEL;
-    if (pos != INT_SENTINEL)
-      gidx = (int)((unit0 + (int64_t)(pos / W) * BLOCK + tid) * W + (pos % W));
-    block_argmax(best, gidx, sm);
-    p.m = best;
-    p.idx = gidx;
-  } else {
-    p.m = block_max(best, sm);
-    p.idx = INT_SENTINEL;
-  }
-  if constexpr (SUM) {
-    const float mc0 = chunk_mc0(p.m, c0);
-    double acc = 0.0;
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      float w[W];
-      decode_unit_at<DT>(row, V, unit0, aligned, raw, j, w);
-#pragma unroll
-      for (int e = 0; e < W; ++e) w[e] = softmax_weight(w[e], c0, mc0);
-      acc += (double)pairwise_sum<W>(w);
-    }
-    p.s = block_sum(acc, sm);
-  }
-  return p;
+__device__ __forceinline__ uint64_t state_or(uint64_t* p, uint64_t v) {
+  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// ------------------------------------------------------------------ inverse-CDF scan in one chunk
-// Weight policy for one softmax row: w = exp2(fma(x, c0, -mc0)).
-template <int DT>
-struct SoftmaxWeights {
-  const char* row;
-  int64_t V;
-  bool aligned;
-  float c0, mc0;
-  __device__ void unit(int64_t u, float (&w)[DTraits<DT>::W]) const {
-    float x[DTraits<DT>::W];
-    load_unit<DT>(row, V, u, aligned, x);
-#pragma unroll
-    for (int e = 0; e < DTraits<DT>::W; ++e) w[e] = softmax_weight(x[e], c0, mc0);
-  }
-  __device__ void chunk(int64_t unit0, float (&w)[UNROLL][DTraits<DT>::W]) const {
-    load_chunk<DT>(row, V, unit0, aligned, w);
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j)
-#pragma unroll
-      for (int e = 0; e < DTraits<DT>::W; ++e) w[j][e] = softmax_weight(w[j][e], c0, mc0);
-  }
-};
-
-// Weight policy for the residual max(0, p_t - p_d) of a target/draft row pair:
-// p = exp2(fma(x, c0, -mc0)) * invZ with invZ = 1 / sum_v exp2(x_v*c0 - mc0).
-template <int DT>
-struct ResidualWeights {
-  const char* trow;
-  const char* drow;
-  int64_t V;
-  bool taligned, daligned;
-  float c0, mc0t, mc0d, izt, izd;
-  __device__ float weight(float xt, float xd) const {
-    const float pt = softmax_weight(xt, c0, mc0t);
-    const float pd = softmax_weight(xd, c0, mc0d) * izd;
-    return fmaxf(0.0f, __builtin_fmaf(pt, izt, -pd));
-  }
-  __device__ void unit(int64_t u, float (&w)[DTraits<DT>::W]) const {
-    float xt[DTraits<DT>::W], xd[DTraits<DT>::W];
-    load_unit<DT>(trow, V, u, taligned, xt);
-    load_unit<DT>(drow, V, u, daligned, xd);
-#pragma unroll
-    for (int e = 0; e < DTraits<DT>::W; ++e) w[e] = weight(xt[e], xd[e]);
-  }
-  __device__ void chunk(int64_t unit0, float (&w)[UNROLL][DTraits<DT>::W]) const {
-    float xd[UNROLL][DTraits<DT>::W];
-    load_chunk<DT>(trow, V, unit0, taligned, w);
-    load_chunk<DT>(drow, V, unit0, daligned, xd);
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j)
-#pragma unroll
-      for (int e = 0; e < DTraits<DT>::W; ++e) w[j][e] = weight(w[j][e], xd[j][e]);
-  }
-};
-
-// Sum of a policy's weights over chunk c (fixed order, same unit sums as the scan).
-template <int DT, class Policy>
-__device__ __forceinline__ double chunk_weight_sum(const Policy& pol, int64_t c, BlockScratch& sm) {
-  constexpr int W = DTraits<DT>::W;
-  const int64_t unit0 = c * UNITS_PER_CHUNK;
-  double acc = 0.0;
-  float w[UNROLL][W];
-  pol.chunk(unit0, w);
-#pragma unroll
-  for (int j = 0; j < UNROLL; ++j) acc += (double)pairwise_sum<W>(w[j]);
-  return block_sum(acc, sm);
+__device__ __forceinline__ uint64_t state_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Inverse CDF inside chunk c: the row index of the first element whose cumulative
-// weight (element order within the chunk) exceeds theta. If rounding leaves no
-// such element (theta at or past the chunk total), the last element of positive
-// weight. Returns -1 if the chunk has no positive weight. Same value in all threads.
-template <int DT, class Policy>
-__device__ __forceinline__ int64_t chunk_invcdf(const Policy& pol, int64_t c, double theta, BlockScratch& sm) {
-  constexpr int W = DTraits<DT>::W;
-  const int tid = threadIdx.x;
-  const int64_t unit0 = c * UNITS_PER_CHUNK;
-  float us[UNROLL];
-  {
-    float w[UNROLL][W];
-    pol.chunk(unit0, w);
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) us[j] = pairwise_sum<W>(w[j]);
-  }
-
-  // 1) which group of BLOCK consecutive units holds the crossing
-  double tot[UNROLL];
-#pragma unroll
-  for (int j = 0; j < UNROLL; ++j) tot[j] = block_sum((double)us[j], sm);
-  int js = -1;
-  double before = 0.0;
-  bool fallback = false;
-  {
-    double cum = 0.0;
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      if (js < 0 && cum + tot[j] > theta) { js = j; before = cum; }
-      cum += tot[j];
-    }
-    if (js < 0) {
-      fallback = true;
-#pragma unroll
-      for (int j = 0; j < UNROLL; ++j)
-        if (tot[j] > 0.0) js = j;
-      if (js < 0) return -1;
-    }
-  }
-  // 2) which unit (thread) of that group
-  float my = 0.0f;
-#pragma unroll
-  for (int j = 0; j < UNROLL; ++j) if (j == js) my = us[j];
-  double incl, excl;
-  block_scan((double)my, incl, excl, sm);
-  int tstar = 0;
-  const double th = theta - before;
-  if (!fallback) {
-    const int below = block_sum_int((incl > th) ? 0 : 1, sm);   // incl is non-decreasing
-    if (below >= BLOCK) fallback = true;
-    tstar = below;
-  }
-  if (fallback) tstar = block_max_int(my > 0.0f ? tid : -1, sm);
-  // 3) which element of that unit: recompute its weights (same expression as above)
-  if (tid == tstar) {
-    const int64_t u = unit0 + (int64_t)js * BLOCK + tid;
-    float w[W];
-    pol.unit(u, w);
-    int pick = -1;
-    if (!fallback) {
-      double cum = excl;
-#pragma unroll
-      for (int e = 0; e < W; ++e) {
-        cum += (double)w[e];
-        if (pick < 0 && cum > th) pick = e;
-      }
-    }
-    if (pick < 0) {
-#pragma unroll
-      for (int e = 0; e < W; ++e) if (w[e] > 0.0f) pick = e;
-    }
-    sm.result = u * W + pick;
-  }
-  __syncthreads();
-  const int64_t r = sm.result;
-  __syncthreads();
-  return r;
-}
-
-// ------------------------------------------------------------------ chunk selection (wave 0)
-constexpr int MAX_CHUNKS = 256;            // 4 chunks per lane of wave 0
-constexpr int CHUNKS_PER_LANE = MAX_CHUNKS / 64;
-
-// Given per-chunk weights W_c (c < C) held by lane-contiguous ranges, pick the
-// first chunk whose inclusive prefix exceeds u * total. Runs in wave 0 only;
-// result fields are valid in all lanes of wave 0.
-struct ChunkPick {
-  int c;          // chosen chunk, -1 if the total is not a positive finite number
-  double before;  // sum of weights of the chunks before c
-  double total;   // sum of all chunk weights (scan order)
-  double theta;   // u * total
-  bool fallback;  // no chunk crossed: c is the last chunk of positive weight
-};
-
-// Each lane of wave 0 holds the weights of chunks c_lo .. c_lo+CHUNKS_PER_LANE-1
-// (c_lo = lane * ceil(C/64); zero past its range), in wl[].
-__device__ __forceinline__ void lane_chunk_range(int C, int& c_lo, int& c_hi) {
-  const int per = (C + 63) / 64;
-  c_lo = min(C, lane_id() * per);
-  c_hi = min(C, c_lo + per);
-}
-
-__device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&wl)[CHUNKS_PER_LANE]) {
-  const int lane = lane_id();
-  int c_lo, c_hi;
-  lane_chunk_range(C, c_lo, c_hi);
-  double local = 0.0;
-#pragma unroll
-  for (int q = 0; q < CHUNKS_PER_LANE; ++q) local += wl[q];
-  const double incl = wave_incl_scan(local);
-  const double prev = __shfl_up(incl, 1);
-  const double excl = (lane == 0) ? 0.0 : prev;
-  const double total = __shfl(incl, 63);
-  ChunkPick r;
-  r.total = total;
-  r.theta = 0.0;
-  r.c = -1;
-  r.before = 0.0;
-  r.fallback = false;
-  if (!(total > 0.0) || !__builtin_isfinite(total)) return r;
-  const double theta = u * total;
-  r.theta = theta;
-  int hit = INT_SENTINEL;
-  double hit_before = 0.0;
-  {
-    double cum = excl;
-#pragma unroll
-    for (int q = 0; q < CHUNKS_PER_LANE; ++q) {
-      if (hit == INT_SENTINEL && c_lo + q < c_hi) {
-        if (cum + wl[q] > theta) { hit = c_lo + q; hit_before = cum; }
-        cum += wl[q];
-      }
-    }
-  }
-  // first lane with a hit (hits are monotone in lane order)
-  const unsigned long long mask = __ballot(hit != INT_SENTINEL);
-  if (mask != 0ull) {
-    const int src = __builtin_ctzll(mask);
-    r.c = __shfl(hit, src);
-    r.before = __shfl(hit_before, src);
-    return r;
-  }
-  // rounding left no crossing: the last chunk with positive weight
-  int last = -1;
-#pragma unroll
-  for (int q = 0; q < CHUNKS_PER_LANE; ++q)
-    if (c_lo + q < c_hi && wl[q] > 0.0) last = c_lo + q;
-  last = wave_max_int(last);
-  r.c = last;
-  r.fallback = true;
-  return r;
+template <class T>
+__device__ __forceinline__ void counter_reset(T* p) {
+  __hip_atomic_store(p, (T)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace sv

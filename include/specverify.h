@@ -91,7 +91,7 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
 enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4, SV_ERR_INTERNAL = 8 };
 
 /* Limits: k <= SV_MAX_K drafts per sequence; n_nodes <= SV_MAX_TREE_NODES; V < 2^31. */
-enum { SV_MAX_K = 64, SV_MAX_TREE_NODES = 16384 };
+enum { SV_MAX_K = 31, SV_MAX_TREE_NODES = 16384 };
 
 /* ---------------------------------------------------------------- linear drafts
  * [S-SD], [S-ZE], [S-MTP]. B sequences, k draft tokens each (k = 0 is plain

@@ -58,7 +58,7 @@ def test_linear_validation(L):
     assert _lin(L, T=-1.0) == 1
     assert _lin(L, B=-1) == 1
     assert _lin(L, V=0) == 1
-    assert _lin(L, k=65) == 5                      # SV_ELIMIT
+    assert _lin(L, k=32) == 5                      # SV_ELIMIT (k <= 31)
     assert _lin(L, V=3_000_000) == 5               # more than 256 chunks per row
     assert _lin(L, tgt=None) == 1
     assert _lin(L, tok=None) == 1

@@ -70,7 +70,7 @@ def test_identity_accepts_all_plus_bonus():
     np.testing.assert_array_equal(g["p_target"], g["p_draft"])
 
 
-@pytest.mark.parametrize("k", [0, 1, 8, 64])
+@pytest.mark.parametrize("k", [0, 1, 8, 31])
 @pytest.mark.parametrize("mode", ["stochastic", "greedy"])
 def test_draft_lengths(k, mode):
     w = gen.linear_draft_target(80, k, 6, k, 3000, gen.DT_BF16, 1.0, 0.3, mode, 1.0, f"k{k}")
@@ -78,12 +78,14 @@ def test_draft_lengths(k, mode):
 
 
 def test_argmax_ties_across_chunks():
-    # bf16 rows of V=20000 (chunks of 8192): equal maxima placed on both sides of
-    # chunk boundaries and in the tail; the lowest index must win
+    # bf16 rows of V=20000 (a wave's chunk holds 4096 bf16 logits): equal maxima
+    # placed on both sides of chunk boundaries and in the tail; the lowest index
+    # must win
     B, k, V = 6, 2, 20000
     rng = np.random.default_rng(3)
     x = np.round(rng.normal(0, 1, size=(B, k + 1, V)) * 8) / 8
-    spots = [(8191, 8192), (8192, 19999), (0, 16384), (16383, 16384), (5, 6), (19998, 19999)]
+    spots = [(8191, 8192), (8192, 19999), (0, 16384), (16383, 16384), (5, 6), (19998, 19999),
+             (4095, 4096), (12287, 16384), (4096, 19999), (19968, 19999)]
     for b in range(B):
         for r in range(k + 1):
             for s in spots[(b + r) % len(spots)]:
