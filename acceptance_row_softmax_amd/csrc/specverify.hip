@@ -301,8 +301,7 @@ struct LinearParams {
   int C, CP, R;         // chunks per row, streaming waves per row (C rounded up to 4), rows per sequence
   float c0;
   uint32_t tag;
-  int64_t n_stream;     // streaming waves (RQ * CP)
-  int64_t n_resid;      // residual waves (B * C in stochastic mode with k > 0, else 0)
+  int64_t n_waves;      // waves of the launch (see linear_role)
 };
 
 // Row order. Stochastic: q = i*2B + 2b + which for i < k (which 0 target, 1
@@ -324,8 +323,10 @@ __device__ __forceinline__ const char* row_ptr(const LinearParams& P, int64_t b,
 // Writes every output of sequence b (its last event): the first rejected
 // position from the state word, the final token from the token record, the
 // error bits, and the accepted drafts.
+constexpr int TOKEN_UNKNOWN = INT_SENTINEL;
+
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b) {
+__device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b, int known_y) {
   const int lane = lane_id();
   const int64_t k = P.k, V = P.V;
   uint64_t s = 0;
@@ -335,7 +336,7 @@ __device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b) {
   bool tg = true;
   if (lane == 0) s = state_load(P.state + b * SSTRIDE);
   if (lane == 1) ew = __hip_atomic_load(P.errw + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane == 2) tg = get_rec(P.tok + b, t, P.tag);
+  if (lane == 2 && known_y == TOKEN_UNKNOWN) tg = get_rec(P.tok + b, t, P.tag);
   const bool has = lane < k;
   const int x = has ? P.tokens[b * k + lane] : 0;
   Probs pr;
@@ -348,14 +349,14 @@ __device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b) {
   // leave the sequence's words and records zero for the next call
   if (lane == 0) counter_reset(P.state + b * SSTRIDE);
   if (lane == 1) counter_reset(P.errw + b * CSTRIDE);
-  if (lane == 2) clear_rec<Token>(P.tok + b);
+  if (lane == 2 && known_y == TOKEN_UNKNOWN) clear_rec<Token>(P.tok + b);
   if (lane < P.R) {
     const int64_t i = lane <= k ? lane : lane - k - 1;
     clear_rec<RowStat>(P.rows + row_q<STOCH>(P, b, i, lane <= k ? 0 : 1) * ROW_WORDS);
   }
   s = __shfl(s, 0);
   int err = (int)__shfl(ew, 1);
-  const int y = __shfl(tg ? t.y : -2, 2);
+  const int y = known_y != TOKEN_UNKNOWN ? known_y : __shfl(tg ? t.y : -2, 2);
   const uint64_t rej = (s >> 32) & ((1ull << k) - 1);
   const int L = rej ? __builtin_ctzll(rej) : (int)k;
   if (__ballot(has && (x < 0 || x >= V))) err |= SV_ERR_TOKEN;
@@ -377,16 +378,24 @@ __device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b) {
 }
 
 // Counts one event of sequence b (R row combines and the final token); the last
-// one writes the outputs.
+// one writes the outputs. The token event carries the token: if it is not the
+// last event, the token goes to the token record for the wave that will be.
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b) {
+__device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, bool token = false, int y = 0) {
   const uint32_t total = (uint32_t)P.R + 1u;
   uint32_t old = 0;
   if (lane_id() == 0) old = counter_add(P.fin + b * CSTRIDE, 1u);
   old = bcast(old);
-  if (old + 1 != total) return;
+  if (old + 1 != total) {
+    if (token && lane_id() == 0) {
+      Token t;
+      t.y = y;
+      put_rec(P.tok + b, t, P.tag);
+    }
+    return;
+  }
   if (lane_id() == 0) counter_reset(P.fin + b * CSTRIDE);
-  linear_emit<DT, STOCH>(P, b);
+  linear_emit<DT, STOCH>(P, b, token ? y : TOKEN_UNKNOWN);
 }
 
 // Called after the state update old -> now by the wave that combined row
@@ -421,10 +430,9 @@ __device__ __forceinline__ void linear_settle(const LinearParams& P, int64_t b, 
     }
     return;   // the residual waves draw the token
   }
+  int y = 0;
   if (lane_id() == 0) {
-    Token t;
-    t.y = !got ? -2 : (tl.ok != 1 ? -1 : (STOCH ? tl.y : tl.argmax));
-    put_rec(P.tok + b, t, P.tag);
+    y = !got ? -2 : (tl.ok != 1 ? -1 : (STOCH ? tl.y : tl.argmax));
     if (STOCH && k > 0) {
       Decision d;
       d.L = Ln;
@@ -434,7 +442,7 @@ __device__ __forceinline__ void linear_settle(const LinearParams& P, int64_t b, 
       put_rec(P.dec + b * DEC_WORDS, d, P.tag);
     }
   }
-  linear_event<DT, STOCH>(P, b);   // the final token
+  linear_event<DT, STOCH>(P, b, true, bcast(y));   // the final token
 }
 
 // Combines row q (b, position i, target/draft) once its last chunk is done.
@@ -522,10 +530,7 @@ __device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q,
 }
 
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_stream_wave(const LinearParams& P, int64_t w) {
-  uint32_t q32, c32;
-  stream_coords((uint32_t)w, (uint32_t)P.CP, (uint32_t)(P.B * P.R), q32, c32);
-  if (c32 >= (uint32_t)P.C) return;   // padding wave
+__device__ __forceinline__ void linear_stream_wave(const LinearParams& P, uint32_t q32, uint32_t c32) {
   const int64_t q = q32, c = c32;
   int64_t b, i;
   int which;
@@ -562,13 +567,14 @@ __device__ __forceinline__ void linear_stream_wave(const LinearParams& P, int64_
   linear_combine<DT, STOCH>(P, q, b, i, which);
 }
 
+// Residual wave (b, c), dispatched after every streaming wave: waits for the
+// decision of sequence b; if a draft was rejected, sums the residual over chunk c
+// of rows t_L, d_L. The sequence's last residual wave picks the chunk holding u*S,
+// scans it and records the token.
 template <int DT>
-__device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int64_t w) {
+__device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int64_t b, int64_t c) {
   const int lane = lane_id();
   const uint32_t C = (uint32_t)P.C;
-  const uint32_t b32 = (uint32_t)w / C;
-  const int64_t b = b32;
-  const int64_t c = (uint32_t)w - b32 * C;
   const int64_t k = P.k;
   Decision d;
   d.L = 0;
@@ -637,21 +643,46 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
       }
     }
   }
-  if (lane == 0) {
-    Token t;
-    t.y = y;
-    put_rec(P.tok + b, t, P.tag);
+  linear_event<DT, true>(P, b, true, y);
+}
+
+// Wave roles of a linear launch: the streaming waves (rows in order, see
+// stream_coords), then in stochastic mode with k > 0 one residual wave per
+// (sequence, chunk).
+struct Role {
+  int kind;       // 0 idle, 1 streaming (q, c), 2 residual (b, c)
+  uint32_t q, b, c;
+};
+
+template <bool STOCH>
+__device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
+  Role r;
+  r.kind = 0;
+  r.q = r.b = r.c = 0;
+  const uint32_t CP = (uint32_t)P.CP;
+  const uint32_t C = (uint32_t)P.C;
+  const uint32_t RQ = (uint32_t)(P.B * P.R);
+  if (w < RQ * CP) {
+    stream_coords(w, CP, RQ, r.q, r.c);
+    r.kind = r.c < C ? 1 : 0;
+  } else {
+    const uint32_t v = w - RQ * CP;
+    r.b = v / C;
+    r.c = v - r.b * C;
+    r.kind = 2;
   }
-  linear_event<DT, true>(P, b);
+  return r;
 }
 
 template <int DT, bool STOCH>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void linear_kernel(LinearParams P) {
   const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
-  if (w < P.n_stream) {
-    linear_stream_wave<DT, STOCH>(P, w);
-  } else if (w < P.n_stream + P.n_resid) {
-    if constexpr (STOCH) linear_residual_wave<DT>(P, w - P.n_stream);
+  if (w >= P.n_waves) return;
+  const Role r = linear_role<STOCH>(P, (uint32_t)w);
+  if (r.kind == 1) {
+    linear_stream_wave<DT, STOCH>(P, r.q, r.c);
+  } else if (r.kind == 2) {
+    if constexpr (STOCH) linear_residual_wave<DT>(P, r.b, r.c);
   }
 }
 
@@ -879,7 +910,7 @@ int64_t chunks_per_row(int64_t V, sv_dtype dt) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t off[12];
+  size_t off[14];
   size_t total;
 };
 
@@ -944,7 +975,7 @@ sv_status dispatch(sv_dtype dt, bool stoch, Args&&... args) {
 template <int DT, bool STOCH>
 struct LinearLauncher {
   static sv_status run(const LinearParams& P, hipStream_t s) {
-    hipLaunchKernelGGL((linear_kernel<DT, STOCH>), dim3(blocks_for(P.n_stream + P.n_resid)), dim3(BLOCK), 0, s, P);
+    hipLaunchKernelGGL((linear_kernel<DT, STOCH>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
     return launch_status();
   }
 };
@@ -1046,9 +1077,8 @@ sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t
   P.C = (int)chunks_per_row(V, dtype);
   P.CP = (P.C + WPB - 1) / WPB * WPB;
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  P.n_stream = B * P.R * P.CP;
-  P.n_resid = (stoch && k > 0) ? B * P.C : 0;
-  if (P.n_stream + P.n_resid > MAX_WAVES) return SV_ELIMIT;
+  P.n_waves = B * P.R * P.CP + ((stoch && k > 0) ? B * P.C : 0);
+  if (P.n_waves > MAX_WAVES) return SV_ELIMIT;
   P.tag = next_tag();
   return dispatch<LinearLauncher>(dtype, stoch, P, reinterpret_cast<hipStream_t>(stream));
 }
