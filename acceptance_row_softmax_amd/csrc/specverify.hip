@@ -648,7 +648,7 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
 
 // Wave roles of a linear launch: the streaming waves (rows in order, see
 // stream_coords), then in stochastic mode with k > 0 one residual wave per
-// (sequence, chunk).
+// (sequence, chunk). Residual waves follow every row their decision depends on.
 struct Role {
   int kind;       // 0 idle, 1 streaming (q, c), 2 residual (b, c)
   uint32_t q, b, c;

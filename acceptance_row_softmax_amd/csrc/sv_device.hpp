@@ -25,7 +25,10 @@ namespace sv {
 constexpr int WAVE = 64;
 constexpr int BLOCK = 256;
 constexpr int WPB = BLOCK / WAVE;               // independent waves per workgroup
-constexpr int CU = 8;                           // 16-byte units per lane per chunk
+#ifndef SV_CU
+#define SV_CU 8
+#endif
+constexpr int CU = SV_CU;                       // 16-byte units per lane per chunk
 constexpr int CHUNK_UNITS = WAVE * CU;          // 512 units = 8 KiB
 constexpr int MAX_ROUNDS = 4;                   // chunks per lane in a row combine
 constexpr int MAX_CHUNKS = WAVE * MAX_ROUNDS;   // chunks per row
@@ -61,41 +64,100 @@ struct RowStat {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 __device__ __forceinline__ int wave_in_block() { return threadIdx.x / WAVE; }
 
+// Cross-lane steps use DPP row operations (inside rows of 16 lanes: swap
+// neighbours, swap pairs, mirror halves, mirror the row), after which every lane
+// of a row holds the row's result; the four row results are then combined in
+// lane order from lanes 0, 16, 32 and 48. Both orders are fixed, so every lane
+// gets the same bits, run after run.
+enum : int {
+  DPP_XOR1 = 0xB1,          // quad_perm [1,0,3,2]
+  DPP_XOR2 = 0x4E,          // quad_perm [2,3,0,1]
+  DPP_HALF_MIRROR = 0x141,  // lane i <-> 7-i within 8
+  DPP_MIRROR = 0x140,       // lane i <-> 15-i within 16
+  DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118,
+  DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143
+};
+
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ int dpp_i(int v, int old = 0) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ float dpp_f(float v, float old = 0.0f) {
+  return __int_as_float(dpp_i<CTRL, ROW_MASK, BOUND_ZERO>(__float_as_int(v), __float_as_int(old)));
+}
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ double dpp_d(double v, double old = 0.0) {
+  const long long x = __double_as_longlong(v), o = __double_as_longlong(old);
+  const int lo = dpp_i<CTRL, ROW_MASK, BOUND_ZERO>((int)(x & 0xffffffffll), (int)(o & 0xffffffffll));
+  const int hi = dpp_i<CTRL, ROW_MASK, BOUND_ZERO>((int)(x >> 32), (int)(o >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(x & 0xffffffffll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_d<DPP_XOR1>(v);
+  v += dpp_d<DPP_XOR2>(v);
+  v += dpp_d<DPP_HALF_MIRROR>(v);
+  v += dpp_d<DPP_MIRROR>(v);
+  return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 __device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+  v = max(v, dpp_i<DPP_XOR1>(v));
+  v = max(v, dpp_i<DPP_XOR2>(v));
+  v = max(v, dpp_i<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_i<DPP_MIRROR>(v));
+  return max(max(readlane_i(v, 0), readlane_i(v, 16)), max(readlane_i(v, 32), readlane_i(v, 48)));
 }
 // (value, index): larger value wins, lower index on equal values.
 __device__ __forceinline__ void argmax_combine(float& m, int& i, float m2, int i2) {
   if (m2 > m || (m2 == m && i2 < i)) { m = m2; i = i2; }
 }
-__device__ __forceinline__ void wave_argmax(float& m, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o);
-    const int i2 = __shfl_xor(i, o);
-    argmax_combine(m, i, m2, i2);
-  }
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& m, int& i) {
+  const float m2 = dpp_f<CTRL>(m);
+  const int i2 = dpp_i<CTRL>(i);
+  argmax_combine(m, i, m2, i2);
 }
-// Inclusive prefix sum over the 64 lanes in lane order (Hillis-Steele).
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+  argmax_step<DPP_XOR1>(m, i);
+  argmax_step<DPP_XOR2>(m, i);
+  argmax_step<DPP_HALF_MIRROR>(m, i);
+  argmax_step<DPP_MIRROR>(m, i);
+  float rm = readlane_f(m, 0);
+  int ri = readlane_i(i, 0);
+  argmax_combine(rm, ri, readlane_f(m, 16), readlane_i(i, 16));
+  argmax_combine(rm, ri, readlane_f(m, 32), readlane_i(i, 32));
+  argmax_combine(rm, ri, readlane_f(m, 48), readlane_i(i, 48));
+  m = rm;
+  i = ri;
+}
+// Inclusive prefix sum over the 64 lanes in lane order: shifts by 1, 2, 4, 8
+// inside each row, then the totals of rows 0 and 2 into rows 1 and 3, then the
+// total of rows 0-1 into rows 2-3.
 __device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v += dpp_d<DPP_SHR1, 0xF, true>(v);
+  v += dpp_d<DPP_SHR2, 0xF, true>(v);
+  v += dpp_d<DPP_SHR4, 0xF, true>(v);
+  v += dpp_d<DPP_SHR8, 0xF, true>(v);
+  v += dpp_d<DPP_BCAST15, 0xA, false>(v, 0.0);
+  v += dpp_d<DPP_BCAST31, 0xC, false>(v, 0.0);
   return v;
 }
 __device__ __forceinline__ int first_lane(unsigned long long mask) { return mask ? __builtin_ctzll(mask) : -1; }
