@@ -25,7 +25,7 @@ from . import _build
 SV_GREEDY, SV_STOCHASTIC = 0, 1
 SV_F32, SV_BF16, SV_F16 = 0, 1, 2
 SV_ERR_TOKEN, SV_ERR_ROW, SV_ERR_TREE, SV_ERR_INTERNAL = 1, 2, 4, 8
-SV_MAX_K, SV_MAX_TREE_NODES = 64, 16384
+SV_MAX_K, SV_MAX_TREE_NODES, SV_MAX_ROW_BYTES = 31, 16384, 2097152
 
 LIB_PATH = _build.LIB
 _lib = None

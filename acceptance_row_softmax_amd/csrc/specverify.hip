@@ -1005,6 +1005,8 @@ bool ws_ok(const void* ws, size_t have, size_t need) {
 // Waves of one launch, and rows x chunks as 32-bit indices.
 constexpr int64_t MAX_WAVES = 0x7fffffffLL;
 
+static_assert((int64_t)MAX_CHUNKS * CHUNK_UNITS * 16 == SV_MAX_ROW_BYTES, "row limit of the header");
+
 bool shape_ok(int64_t V, sv_dtype dt) {
   return V <= 0x7fffffffLL - 16 && chunks_per_row(V, dt) <= MAX_CHUNKS;
 }

@@ -45,12 +45,13 @@
  *    once the stream reaches that point. Concurrent calls need distinct workspaces.
  *  - Workspace: device memory of at least the size the *_workspace function
  *    returns, 256-byte aligned, zero-filled before its first use (for instance with
- *    spec_workspace_clear). Workgroups of one launch pass results to each other
- *    through records in it; every call tags its records with a fresh value and each
- *    record is cleared by the workgroup that reads it, so a call that ends without
- *    SV_ERR_INTERNAL leaves the workspace all zeros again, ready for any entry point
- *    and shape. One workspace serves one launch at a time; after SV_ERR_INTERNAL,
- *    clear it again before reuse.
+ *    spec_workspace_clear). The waves of one launch pass results to each other
+ *    through records and atomic arrival counters in it; every call tags its
+ *    records with a fresh value, each record is cleared by the wave that reads it
+ *    last and each counter by the wave that completes it, so a call that ends
+ *    without SV_ERR_INTERNAL leaves the workspace all zeros again, ready for any
+ *    entry point and shape. One workspace serves one launch at a time; after
+ *    SV_ERR_INTERNAL, clear it again before reuse.
  *  - Errors detectable on the host return a non-zero status before anything is
  *    enqueued. Data errors seen on the device set bits in err_flags (if given) and
  *    give that sequence accept_len = -1 and -1 tokens:
@@ -90,8 +91,10 @@ typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
 
 enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4, SV_ERR_INTERNAL = 8 };
 
-/* Limits: k <= SV_MAX_K drafts per sequence; n_nodes <= SV_MAX_TREE_NODES; V < 2^31. */
-enum { SV_MAX_K = 31, SV_MAX_TREE_NODES = 16384 };
+/* Limits: k <= SV_MAX_K drafts per sequence; n_nodes <= SV_MAX_TREE_NODES; a row
+ * holds at most SV_MAX_ROW_BYTES of logits (V <= 1048576 for bf16/fp16, 524288 for
+ * fp32). Larger shapes return SV_ELIMIT. */
+enum { SV_MAX_K = 31, SV_MAX_TREE_NODES = 16384, SV_MAX_ROW_BYTES = 2097152 };
 
 /* ---------------------------------------------------------------- linear drafts
  * [S-SD], [S-ZE], [S-MTP]. B sequences, k draft tokens each (k = 0 is plain

@@ -60,6 +60,11 @@ def test_linear_validation(L):
     assert _lin(L, V=0) == 1
     assert _lin(L, k=32) == 5                      # SV_ELIMIT (k <= 31)
     assert _lin(L, V=3_000_000) == 5               # more than 256 chunks per row
+    # SV_MAX_ROW_BYTES: 2 MiB of logits per row; at the limit validation goes on
+    assert _lin(L, V=sv.SV_MAX_ROW_BYTES // 2 + 1) == 5
+    assert _lin(L, V=sv.SV_MAX_ROW_BYTES // 2, ws=None) == 3
+    assert _lin(L, V=sv.SV_MAX_ROW_BYTES // 4 + 1, dt=0) == 5
+    assert _lin(L, V=sv.SV_MAX_ROW_BYTES // 4, dt=0, ws=None) == 3
     assert _lin(L, tgt=None) == 1
     assert _lin(L, tok=None) == 1
     assert _lin(L, u=None) == 1
