@@ -707,9 +707,18 @@ struct TreeParams {
   int64_t n_stream;
 };
 
-template <int DT, bool STOCH>
+// How the token of a node is chosen. Greedy: its argmax, while streaming.
+// Stochastic: an inverse-CDF draw with the node's uniform, either while streaming
+// at every node (EAGER: the draws overlap the stream, best for few rows) or by
+// the walk at the accepted nodes only (LAZY: the only draws the result depends
+// on, best for many rows).
+enum TreeDraw { TD_ARGMAX = 0, TD_EAGER = 1, TD_LAZY = 2 };
+constexpr int64_t TREE_EAGER_ROWS = 4096;   // at most this many rows (B * n_nodes) draw eagerly
+
+template <int DT, int TD>
 __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
   constexpr int E = DTraits<DT>::E;
+  constexpr bool STOCH = TD != TD_ARGMAX;
   const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
   if (w >= P.n_stream) return;
   const uint32_t C = (uint32_t)P.C;
@@ -730,101 +739,243 @@ __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
   const RowParts rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
   double wl[MAX_ROUNDS];
   const RowSums rs = row_sums<STOCH>(rp, P.c0, wl);
+  // the node's token (TD_LAZY: 0 for a usable row); -1 an unusable row, -2 a
+  // wait timed out
   int y;
   if (!rp.got) {
     y = -2;
   } else if constexpr (STOCH) {
     const bool usable = rs.M > -INFINITY && __builtin_isfinite(rs.Z) && rs.Z > 0.0;
-    y = usable ? softmax_draw<DT>(row, P.V, P.C, P.c0, P.uniforms[q], rp, rs, wl) : -1;
+    if constexpr (TD == TD_EAGER)
+      y = usable ? softmax_draw<DT>(row, P.V, P.C, P.c0, P.uniforms[q], rp, rs, wl) : -1;
+    else
+      y = usable ? 0 : -1;
   } else {
     y = rs.argmax;
   }
   if (lane_id() == 0) P.node_y[q] = y;
 }
 
-__device__ __forceinline__ int block_or(int v, int* sh) {
+// node indices and depths fit the 15-bit fields of the walk's search keys
+static_assert(SV_MAX_TREE_NODES <= 16384, "tree walk keys");
+constexpr int WALK_BATCH = 8;   // nodes per thread whose loads are in flight together
+
+__device__ __forceinline__ int block_or(int v) {
   // OR over the workgroup (each bit through __syncthreads_or)
   int r = 0;
   for (int bit = 1; bit <= SV_ERR_INTERNAL; bit <<= 1)
     if (__syncthreads_or(v & bit)) r |= bit;
-  (void)sh;
   return r;
 }
 
-// Accepted-path search of tree b (one workgroup). LDS: parent (int16) and match
-// flag (uint8) of every node.
-__global__ __launch_bounds__(BLOCK) void tree_walk_kernel(TreeParams P) {
+// Largest v over the workgroup (sh: one int per wave).
+template <int NT>
+__device__ __forceinline__ int block_max_int(int v, int* sh) {
+  v = wave_max_int(v);
+  if (lane_id() == 0) sh[wave_in_block()] = v;
+  __syncthreads();
+  int r = sh[0];
+  for (int wv = 1; wv < NT / WAVE; ++wv) r = sh[wv] > r ? sh[wv] : r;
+  __syncthreads();
+  return r;
+}
+
+// Inverse-CDF draw from softmax(row / T) with uniform u by the whole workgroup:
+// the waves reduce the chunks (the same partials the streaming pass forms), then
+// wave 0 picks the chunk and scans it. The token is valid in wave 0.
+template <int DT, int NT>
+__device__ __forceinline__ int walk_draw(const char* row, int64_t V, int C, float c0, float u,
+                                         float* pm, double* ps) {
+  const int wv = wave_in_block(), lane = lane_id();
+  for (int c = wv; c < C; c += NT / WAVE) {
+    const Partial p = chunk_partial<DT, true, false>(row, V, c, c0);
+    if (lane == 0) {
+      pm[c] = p.m;
+      ps[c] = p.s;
+    }
+  }
+  __syncthreads();
+  int y = -1;
+  if (wv == 0) {
+    RowParts rp;
+#pragma unroll
+    for (int t = 0; t < MAX_ROUNDS; ++t) {
+      const int c = t * WAVE + lane;
+      rp.m[t] = c < C ? pm[c] : -INFINITY;
+      rp.idx[t] = INT_SENTINEL;
+      rp.s[t] = c < C ? ps[c] : 0.0;
+    }
+    rp.got = true;
+    rp.xin = false;
+    rp.xv = 0.0f;
+    double wl[MAX_ROUNDS];
+    const RowSums rs = row_sums<true>(rp, c0, wl);
+    if (rs.Z > 0.0 && __builtin_isfinite(rs.Z)) y = softmax_draw<DT>(row, V, C, c0, u, rp, rs, wl);
+  }
+  __syncthreads();   // the partial arrays are reused by the next draw
+  return y;
+}
+
+// Accepted-path search of tree b (one workgroup of NT threads). LDS: parent
+// (int16) and one state byte per node. With the node tokens known (greedy, or
+// drawn while streaming) a node is accepted when every node on its path matches
+// its parent's token. LAZY: the walk goes level by level from the root, drawing
+// the token of each accepted node and accepting the children whose candidate
+// equals it.
+template <int DT, bool LAZY, int NT>
+__global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
+  constexpr int E = DTraits<DT>::E;
   extern __shared__ unsigned char smem[];
-  __shared__ unsigned long long best_sh[BLOCK / WAVE];
+  __shared__ int red_sh[NT / WAVE];
+  __shared__ float pm_sh[LAZY ? MAX_CHUNKS : 1];
+  __shared__ double ps_sh[LAZY ? MAX_CHUNKS : 1];
   const int64_t b = blockIdx.x;
   const int64_t N = P.N;
   int16_t* par_s = reinterpret_cast<int16_t*>(smem);
-  unsigned char* match_s = smem + 2 * N;
+  unsigned char* st_s = smem + 2 * N;   // tokens known: match flag; LAZY: 0 / 1 accepted / 2 drawn
   const int32_t* par = P.parent + b * P.parent_stride;
   const int32_t* cand = P.cand + b * N;
   int32_t* ny = P.node_y + b * N;
+  const int tid = threadIdx.x;
   int err = 0;
-  for (int64_t i = threadIdx.x; i < N; i += BLOCK) {
-    const int y = ny[i];
-    if (y == -1) err |= SV_ERR_ROW;
-    if (y == -2) err |= SV_ERR_INTERNAL;
-    const int p = par[i];
-    const bool bad = (i == 0) ? (p != -1) : (p < 0 || p >= i);
-    par_s[i] = (int16_t)(bad ? 0 : p);
-    if (bad) err |= SV_ERR_TREE;
-    unsigned char m = 0;
-    if (i > 0) {
-      const int ci = cand[i];
-      if (ci < 0 || ci >= P.V) err |= SV_ERR_TOKEN;
-      if (!bad) m = (ci == ny[p]) ? 1 : 0;
+  // validation (and the match flags), WALK_BATCH nodes per thread at a time
+  for (int64_t base = 0; base < N; base += (int64_t)NT * WALK_BATCH) {
+    int yv[WALK_BATCH], pv[WALK_BATCH], cv[WALK_BATCH], yp[WALK_BATCH];
+#pragma unroll
+    for (int j = 0; j < WALK_BATCH; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      yv[j] = 0;
+      pv[j] = -1;
+      cv[j] = 0;
+      if (i < N) {
+        yv[j] = ny[i];
+        pv[j] = par[i];
+        cv[j] = cand[i];
+      }
     }
-    match_s[i] = m;
+#pragma unroll
+    for (int j = 0; j < WALK_BATCH; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      const bool ok = i > 0 && i < N && pv[j] >= 0 && pv[j] < i;
+      yp[j] = -1;
+      if (!LAZY && ok) yp[j] = ny[pv[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < WALK_BATCH; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      if (i >= N) continue;
+      if (yv[j] == -1) err |= SV_ERR_ROW;
+      if (yv[j] == -2) err |= SV_ERR_INTERNAL;
+      const bool bad = (i == 0) ? (pv[j] != -1) : (pv[j] < 0 || pv[j] >= i);
+      par_s[i] = (int16_t)(bad ? 0 : pv[j]);
+      if (bad) err |= SV_ERR_TREE;
+      unsigned char m = 0;
+      if (i > 0) {
+        if (cv[j] < 0 || cv[j] >= P.V) err |= SV_ERR_TOKEN;
+        if (!LAZY && !bad) m = (cv[j] == yp[j]) ? 1 : 0;
+      }
+      st_s[i] = LAZY ? (unsigned char)(i == 0 ? 1 : 0) : m;
+    }
   }
-  int all_err = block_or(err, nullptr);
-  // depth check and path search (bad parents were replaced by the root, so every
-  // chain ends; the depth bound is checked whatever other error was found)
-  unsigned long long best_key = 0ull;
+  int all_err = block_or(err);
+  // depth check (bad parents were replaced by the root, so every chain ends; the
+  // bound is checked whatever other error was found) and, tokens known, the path
+  // search; WALK_BATCH chains per thread advance together
+  int best_key = -1;   // depth * 2^15 + (2^15 - 1 - index): deepest, then lowest index
   int too_deep = 0;
-  for (int64_t i = threadIdx.x; i < N; i += BLOCK) {
-    int64_t j = i, d = 0;
-    int acc = 1;
-    while (j != 0) {
-      if (d >= P.max_depth) { too_deep = 1; break; }
-      acc &= match_s[j];
-      j = par_s[j];
-      ++d;
+  for (int64_t base = 0; base < N; base += (int64_t)NT * WALK_BATCH) {
+    int cur[WALK_BATCH], d[WALK_BATCH], acc[WALK_BATCH];
+#pragma unroll
+    for (int j = 0; j < WALK_BATCH; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      cur[j] = i < N ? (int)i : 0;
+      d[j] = 0;
+      acc[j] = i < N ? 1 : 0;
     }
-    if (acc && !too_deep) {
-      const unsigned long long key = ((unsigned long long)d << 32) | (0xffffffffull - (unsigned long long)i);
-      if (key > best_key) best_key = key;
+    for (;;) {
+      int moving = 0;
+#pragma unroll
+      for (int j = 0; j < WALK_BATCH; ++j) {
+        if (cur[j] == 0) continue;
+        if (d[j] >= P.max_depth) {
+          too_deep = 1;
+          cur[j] = 0;
+          acc[j] = 0;
+          continue;
+        }
+        if (!LAZY) acc[j] &= st_s[cur[j]];
+        cur[j] = par_s[cur[j]];
+        ++d[j];
+        moving = 1;
+      }
+      if (!moving) break;
+    }
+    if (!LAZY) {
+#pragma unroll
+      for (int j = 0; j < WALK_BATCH; ++j) {
+        const int64_t i = base + (int64_t)j * NT + tid;
+        if (acc[j]) {
+          const int key = (d[j] << 15) | (int)(32767 - i);
+          best_key = key > best_key ? key : best_key;
+        }
+      }
     }
   }
   if (__syncthreads_or(too_deep)) all_err |= SV_ERR_TREE;
   int32_t* path = P.path_nodes + b * P.max_depth;
   int32_t* out = P.out_tokens + b * (P.max_depth + 1);
   if (all_err) {
-    for (int64_t j = threadIdx.x; j < P.max_depth; j += BLOCK) path[j] = -1;
-    for (int64_t j = threadIdx.x; j <= P.max_depth; j += BLOCK) out[j] = -1;
-    if (threadIdx.x == 0) {
+    for (int64_t j = tid; j < P.max_depth; j += NT) path[j] = -1;
+    for (int64_t j = tid; j <= P.max_depth; j += NT) out[j] = -1;
+    if (tid == 0) {
       P.accept_len[b] = -1;
       if (P.err_flags) P.err_flags[b] = all_err;
     }
   } else {
-    // workgroup max of the (depth, -index) key
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long t = __shfl_xor(best_key, o);
-      best_key = t > best_key ? t : best_key;
+    int L = 0, best = 0;
+    if constexpr (LAZY) {
+      for (int level = 0;; ++level) {
+        // draw the accepted nodes of this level, lowest index first
+        int first = -1;
+        for (;;) {
+          int key = -1;   // 2^15 - 1 - index of an accepted node still to draw
+          for (int64_t i = tid; i < N; i += NT)
+            if (st_s[i] == 1) key = (int)(32767 - i) > key ? (int)(32767 - i) : key;
+          key = block_max_int<NT>(key, red_sh);
+          if (key < 0) break;
+          const int f = 32767 - key;
+          if (first < 0) first = f;
+          const char* row = P.logits + ((b * N + f) * P.V) * E;
+          const int y = walk_draw<DT, NT>(row, P.V, P.C, P.c0, P.uniforms[b * N + f], pm_sh, ps_sh);
+          if (tid == 0) {
+            ny[f] = y;
+            st_s[f] = 2;
+          }
+          __syncthreads();
+        }
+        L = level;
+        best = first;
+        // accept the children whose candidate is their parent's drawn token
+        int any = 0;
+        for (int64_t i = 1 + tid; i < N; i += NT) {
+          const int pi = par_s[i];
+          // the drawn token was stored by thread 0 after this thread's first read of ny
+          if (st_s[i] == 0 && st_s[pi] == 2 &&
+              cand[i] == __hip_atomic_load(ny + pi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            st_s[i] = 1;
+            any = 1;
+          }
+        }
+        if (!__syncthreads_or(any)) break;
+      }
+    } else {
+      const int r = block_max_int<NT>(best_key, red_sh);
+      L = r >> 15;
+      best = 32767 - (r & 32767);
     }
-    if (lane_id() == 0) best_sh[wave_in_block()] = best_key;
-    __syncthreads();
-    unsigned long long r = 0ull;
-    for (int wv = 0; wv < BLOCK / WAVE; ++wv) r = best_sh[wv] > r ? best_sh[wv] : r;
-    const int L = (int)(r >> 32);
-    const int best = (int)(0xffffffffull - (r & 0xffffffffull));
-    for (int64_t j = L + threadIdx.x; j < P.max_depth; j += BLOCK) path[j] = -1;
-    for (int64_t j = L + 1 + threadIdx.x; j <= P.max_depth; j += BLOCK) out[j] = -1;
-    if (threadIdx.x == 0) {
+    for (int64_t j = L + tid; j < P.max_depth; j += NT) path[j] = -1;
+    for (int64_t j = L + 1 + tid; j <= P.max_depth; j += NT) out[j] = -1;
+    if (tid == 0) {
       int node = best;
       for (int j = L - 1; j >= 0; --j) {
         path[j] = node;
@@ -838,7 +989,7 @@ __global__ __launch_bounds__(BLOCK) void tree_walk_kernel(TreeParams P) {
   }
   // leave the node tokens zero, as the workspace was
   __syncthreads();
-  for (int64_t i = threadIdx.x; i < N; i += BLOCK) ny[i] = 0;
+  for (int64_t i = tid; i < N; i += NT) ny[i] = 0;
 }
 
 // ------------------------------------------------------------------ row statistics
@@ -980,12 +1131,26 @@ struct LinearLauncher {
   }
 };
 
+// Walk workgroups: 1024 threads when the tokens are known; 512 for the lazy
+// walk, whose draw needs more registers per thread.
 template <int DT, bool STOCH>
 struct TreeLauncher {
   static sv_status run(const TreeParams& P, size_t smem, hipStream_t s) {
-    hipLaunchKernelGGL((tree_stream_kernel<DT, STOCH>), dim3(blocks_for(P.n_stream)), dim3(BLOCK), 0, s, P);
+    const bool eager = STOCH && P.B * P.N <= TREE_EAGER_ROWS;
+    const dim3 grid(blocks_for(P.n_stream)), trees((unsigned)P.B);
+    if (!STOCH) {
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_ARGMAX>), grid, dim3(BLOCK), 0, s, P);
+    } else if (eager) {
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_EAGER>), grid, dim3(BLOCK), 0, s, P);
+    } else {
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_LAZY>), grid, dim3(BLOCK), 0, s, P);
+    }
     if (launch_status() != SV_OK) return SV_EHIP;
-    hipLaunchKernelGGL(tree_walk_kernel, dim3((unsigned)P.B), dim3(BLOCK), smem, s, P);
+    if (STOCH && !eager) {
+      hipLaunchKernelGGL((tree_walk_kernel<DT, true, 512>), trees, dim3(512), smem, s, P);
+    } else {
+      hipLaunchKernelGGL((tree_walk_kernel<DT, false, 1024>), trees, dim3(1024), smem, s, P);
+    }
     return launch_status();
   }
 };

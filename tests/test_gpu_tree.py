@@ -107,3 +107,37 @@ def test_root_only_tree():
                              gen.uniforms(gen.key(1, 1, 1), B).reshape(B, 1), 0)
         g, o, _, _ = _check(w)
         assert np.all(g["accept_len"] == 0)
+
+
+@pytest.mark.parametrize("shape", [[2, 2, 2, 2], [3, 3, 3, 3, 3, 3]])
+def test_stochastic_tree_deep_acceptance(shape):
+    # Rows with one dominant token (all but about 1e-5 of the mass at T = 1) make the
+    # drawn tokens predictable, so candidates equal to the parent's dominant
+    # token are accepted level after level, and where siblings share a
+    # candidate, several nodes of one level are. The small batch (248 rows)
+    # draws every node while streaming; the large one (8744 rows) draws in the
+    # walk, at every accepted node.
+    parent, rank = gen.cartesian_tree(shape)
+    n = len(parent)
+    B, V = 8, 3000
+    rng = np.random.default_rng(77)
+    dom = rng.integers(0, V, size=(B, n))
+    x = rng.normal(0.0, 1.0, size=(B, n, V))
+    x[np.arange(B)[:, None], np.arange(n)[None, :], dom] += 20.0
+    logits = gen.round_to(gen.DT_BF16, x)
+    cand = np.empty((B, n), np.int32)
+    cand[:, 0] = -1
+    for b in range(B):
+        for i in range(1, n):
+            if b < 4 or rank[i] == 1:        # trees 0-3: siblings share the candidate
+                cand[b, i] = dom[b, parent[i]]
+            else:
+                cand[b, i] = (dom[b, parent[i]] + 1 + rng.integers(0, V - 1)) % V
+    u = gen.uniforms(gen.key(62, V, 4), B * n).reshape(B, n)
+    w = gen.TreeWorkload("dominant", "stochastic", 1.0, B, n, V, gen.DT_BF16, parent, cand, logits, u,
+                         len(shape))
+    g, o, _, _ = _check(w)
+    assert np.all(g["err_flags"] == 0)
+    assert g["accept_len"].mean() >= 2.0
+    # trees 0-3 accept more nodes than their path holds: several draws per level
+    assert np.sum(o["n_eval"][:4]) > np.sum(o["accept_len"][:4] + 1) + 4
