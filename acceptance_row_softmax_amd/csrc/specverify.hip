@@ -24,9 +24,12 @@
 // No wave ever waits for work that is dispatched after it except the residual
 // waves (which wait for the decision of streaming waves dispatched before them).
 //
-// Trees: a streaming launch of the same kind computes every node's token, then one
-// workgroup per tree searches the accepted path in LDS. Row statistics: the
-// streaming launch alone.
+// Trees: two launches. A streaming launch of the same kind reduces every node's
+// row (greedy: its argmax is the node's token; stochastic: for a small batch the
+// token is drawn there too, at every node), then one workgroup per tree searches
+// the accepted path in LDS; for a large stochastic batch it walks level by level
+// and draws the tokens of the accepted nodes only. Row statistics: the streaming
+// launch alone.
 //
 // Sources: "Accelerating Sonar through speculation" (sections "Spekulatives
 // Decoding", "Ziel-Entwurf", "MTP", "EAGLE"); "Speculative-Decoding, LLM推理的加速 /

@@ -14,7 +14,8 @@ the benchmark refuses to report a number if parity fails.
 
 Prints ONE JSON line (rank 0, N=1). Fields beyond the required ones:
 logit_GBps / hbm_frac (algorithmic bytes of a whole step over its time),
-kernel_us (live HIP-event duration of the step's one kernel launch), parity.
+kernel_us (live HIP-event duration of one step: the linear kernel's one launch,
+or a tree step's two launches), parity.
 """
 from __future__ import annotations
 
@@ -260,8 +261,10 @@ def main():
     ms_per_step = wall_ms / K
 
     # ---------------------------------------------------------------- kernel duration (HIP events)
-    # A step is one kernel launch, so the launch duration is the timed region's
-    # event time over its K launches (launch gaps included: an upper bound).
+    # A linear step is one kernel launch, so the launch duration is the timed
+    # region's event time over its K launches (launch gaps included: an upper
+    # bound). A tree step is two launches (streaming, then the path search); the
+    # figure covers both.
     # Second figure: one event pair per launch, with the GPU held by a spin kernel
     # while the host enqueues, so that host launch gaps stay out of the pairs.
     nprof = min(K, 400)
@@ -282,7 +285,7 @@ def main():
     torch.cuda.synchronize()
     pair_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
     dom_us = gpu_ms * 1e3 / K
-    dominant = "linear_kernel" if linear else "tree_kernel"
+    dominant = "linear_kernel" if linear else "tree_stream_kernel+tree_walk_kernel"
 
     npos = positions(w)
     value = npos / (ms_per_step * 1e-3)
