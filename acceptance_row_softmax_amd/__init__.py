@@ -25,6 +25,7 @@ from . import _build
 SV_GREEDY, SV_STOCHASTIC = 0, 1
 SV_F32, SV_BF16, SV_F16 = 0, 1, 2
 SV_ERR_TOKEN, SV_ERR_ROW, SV_ERR_TREE, SV_ERR_INTERNAL = 1, 2, 4, 8
+SV_ERR_CAPACITY, SV_ERR_UNVERIFIED = 16, 32
 SV_MAX_K, SV_MAX_TREE_NODES, SV_MAX_ROW_BYTES = 31, 16384, 2097152
 
 LIB_PATH = _build.LIB
@@ -64,13 +65,24 @@ def lib():
         L.spec_row_stats.argtypes = [i32, f32, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.spec_workspace_clear.restype = i32
         L.spec_workspace_clear.argtypes = [vp, sz, vp]
+        L.spec_commit_linear.restype = i32
+        L.spec_commit_linear.argtypes = [i64, i64, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+        L.spec_sample_workspace.restype = sz
+        L.spec_sample_workspace.argtypes = [i64, i64, i32]
+        L.spec_sample.restype = i32
+        L.spec_sample.argtypes = [i32, f32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_tree_mask.restype = i32
+        L.spec_tree_mask.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+        L.spec_tree_build_greedy.restype = i64
+        L.spec_tree_build_greedy.argtypes = [i64, i64, vp, i64, vp, vp, vp, vp]
         _lib = L
     return _lib
 
 
 EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_tree_workspace",
             "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
-            "spec_workspace_clear", "spec_verify_status_string")
+            "spec_workspace_clear", "spec_verify_status_string", "spec_commit_linear",
+            "spec_sample_workspace", "spec_sample", "spec_tree_mask", "spec_tree_build_greedy")
 
 
 def status_string(status: int) -> str:
@@ -275,3 +287,92 @@ def row_stats(x, temperature: float = 1.0, *, workspace=None, stream=None):
                           _ptr(ef), _ptr(ws), ws.numel(), s)
     _check(st, "spec_row_stats")
     return {"max": m, "lse": lse, "argmax": am, "err_flags": ef}
+
+
+def commit_linear(accept_len, out_tokens, draft_tokens, seq_len, history=None, *, shifted: bool = True,
+                  stream=None):
+    """Applies a verification's outcome in place (seq_len, history) and returns
+    {"shifted", "next_token", "err_flags"} (spec_commit_linear)."""
+    torch = _torch()
+    i32 = torch.int32
+    _need(accept_len, "accept_len", i32)
+    _need(out_tokens, "out_tokens", i32)
+    _need(seq_len, "seq_len", i32)
+    dev = accept_len.device
+    B = accept_len.shape[0]
+    k = out_tokens.shape[-1] - 1
+    if draft_tokens is not None:
+        _need(draft_tokens, "draft_tokens", i32)
+    cap = 0
+    if history is not None:
+        _need(history, "history", i32)
+        cap = history.shape[-1]
+    sh = torch.empty((B, k + 1), dtype=i32, device=dev) if shifted else None
+    nxt = torch.empty(B, dtype=i32, device=dev)
+    ef = torch.empty(B, dtype=i32, device=dev)
+    st = lib().spec_commit_linear(B, k, _ptr(accept_len), _ptr(out_tokens), _ptr(draft_tokens),
+                                  _ptr(seq_len), _ptr(history), cap, _ptr(sh), _ptr(nxt), _ptr(ef),
+                                  _stream(stream))
+    _check(st, "spec_commit_linear")
+    return {"shifted": sh, "next_token": nxt, "err_flags": ef}
+
+
+def sample(logits, uniforms=None, mode: str = "stochastic", temperature: float = 1.0, *, workspace=None,
+           stream=None):
+    """One token per row of logits [..., V] (spec_sample); returns {"tokens", "err_flags"}."""
+    torch = _torch()
+    _need(logits, "logits")
+    dev = logits.device
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    m = SV_STOCHASTIC if mode == "stochastic" else SV_GREEDY
+    if m == SV_STOCHASTIC:
+        _need(uniforms, "uniforms", torch.float32)
+    tok = torch.empty(rows, dtype=torch.int32, device=dev)
+    ef = torch.empty(rows, dtype=torch.int32, device=dev)
+    L = lib()
+    dt = sv_dtype(logits)
+    nbytes = L.spec_sample_workspace(rows, V, dt)
+    s = _stream(stream)
+    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    st = L.spec_sample(m, float(temperature), rows, V, dt, _ptr(logits),
+                       _ptr(uniforms) if m == SV_STOCHASTIC else None, _ptr(tok), _ptr(ef), _ptr(ws),
+                       ws.numel(), s)
+    _check(st, "spec_sample")
+    return {"tokens": tok, "err_flags": ef}
+
+
+def tree_mask(parent, n_trees: int = 1, *, stream=None):
+    """Ancestor-or-self bitmaps [n_trees][n][ceil(n/32)] uint32 (as int32 storage) of
+    parent arrays [n] (shared) or [n_trees][n] (spec_tree_mask)."""
+    torch = _torch()
+    _need(parent, "parent", torch.int32)
+    dev = parent.device
+    n = parent.shape[-1]
+    stride = 0 if parent.dim() == 1 else n
+    if parent.dim() > 1:
+        n_trees = parent.shape[0]
+    W = (n + 31) // 32
+    mask = torch.empty((n_trees, n, W), dtype=torch.int32, device=dev)
+    ef = torch.empty(n_trees, dtype=torch.int32, device=dev)
+    st = lib().spec_tree_mask(n_trees, n, _ptr(parent), stride, _ptr(mask), _ptr(ef), _stream(stream))
+    _check(st, "spec_tree_mask")
+    return {"mask": mask, "err_flags": ef}
+
+
+def tree_build_greedy(accuracy, budget: int):
+    """Greedy sparse tree from a [K][S] accuracy table (host; spec_tree_build_greedy).
+    Returns numpy arrays parent, depth, rank and the expected accepted length."""
+    import numpy as np
+    acc = np.ascontiguousarray(np.asarray(accuracy, np.float64))
+    K, S = acc.shape
+    par = np.empty(budget + 1, np.int32)
+    dep = np.empty(budget + 1, np.int32)
+    rk = np.empty(budget + 1, np.int32)
+    E = ctypes.c_double()
+    cp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    n = lib().spec_tree_build_greedy(K, S, cp(acc), budget, cp(par), cp(dep), cp(rk), ctypes.byref(E))
+    if n < 0:
+        raise SpecVerifyError(int(-n), "spec_tree_build_greedy")
+    return {"parent": par[:n].copy(), "depth": dep[:n].copy(), "rank": rk[:n].copy(), "expected_len": E.value}
+

@@ -5,7 +5,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "csrc", "specverify.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("specverify.hip", "steps.hip")]
 LIB = os.path.join(HERE, "libspecverify.so")
 
 HIPCC_FLAGS = [
@@ -25,7 +25,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

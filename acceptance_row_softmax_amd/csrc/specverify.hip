@@ -37,6 +37,8 @@
 // method the Sonar page cites: accept x_i iff u_i < p_t,i(x_i) / p_d,i(x_i).
 #include "../../include/specverify.h"
 #include "sv_device.hpp"
+#include "sv_host.hpp"
+#include "sv_rows.hpp"
 
 #include <hip/hip_runtime.h>
 #include <atomic>
@@ -48,14 +50,7 @@ using namespace sv;
 namespace {
 
 constexpr double LN2 = 0.69314718055994530941723212145818;
-constexpr double LOG2E = 1.4426950408889634073599246810019;
 
-constexpr int PART_WORDS = RecWords<Partial>::N;   // 6
-// Every atomic counter sits on its own 128-byte line: counters that share a line
-// serialise each other's atomics.
-constexpr int64_t CSTRIDE = 32;                     // in 32-bit words
-constexpr int64_t SSTRIDE = 16;                     // in 64-bit words
-constexpr int ROW_WORDS = RecWords<RowStat>::N;    // 8
 
 // What the residual waves of a sequence need. kind 0: no draft rejected (the bonus
 // token is final); 1: draw from the residual of rows t_L, d_L; 2: a draft was
@@ -98,140 +93,6 @@ __device__ __forceinline__ int settled_L(uint64_t s, int k) {
   return (fu == k && (s & BONUS_BIT)) ? k : -1;
 }
 
-template <class T>
-__device__ __forceinline__ T bcast(T v) { return __shfl(v, 0); }
-
-// ------------------------------------------------------------------ row combine
-// Chunk partials of one row, lane-strided (lane l holds chunks l + 64 t).
-struct RowParts {
-  float m[MAX_ROUNDS];
-  int idx[MAX_ROUNDS];
-  double s[MAX_ROUNDS];
-  bool got;    // every partial arrived (same in every lane)
-  bool xin;    // some chunk holds the draft token
-  float xv;    // its logit
-};
-
-// Reads the C partials of a row and clears them.
-__device__ __forceinline__ RowParts read_parts(uint64_t* parts, int C, uint32_t tag) {
-  const int lane = lane_id();
-  RowParts rp;
-  bool got = true;
-  int xin = 0;
-  float xv = 0.0f;
-#pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
-    Partial p;
-    p.m = -INFINITY;
-    p.idx = INT_SENTINEL;
-    p.s = 0.0;
-    p.xin = 0;
-    p.xv = 0.0f;
-    const int c = t * WAVE + lane;
-    if (c < C) got = get_rec(parts + (int64_t)c * PART_WORDS, p, tag) && got;
-    rp.m[t] = p.m;
-    rp.idx[t] = p.idx;
-    rp.s[t] = p.s;
-    if (p.xin) { xin = 1; xv = p.xv; }
-  }
-  const unsigned long long xm = __ballot(xin != 0);
-  rp.xin = xm != 0ull;
-  rp.xv = __shfl(xv, xm ? first_lane(xm) : 0);
-#pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
-    const int c = t * WAVE + lane;
-    if (c < C) clear_rec<Partial>(parts + (int64_t)c * PART_WORDS);
-  }
-  rp.got = __ballot(!got) == 0ull;
-  return rp;
-}
-
-struct RowSums {
-  float M;
-  int argmax;   // -1 if no entry exceeds -inf
-  double Z;     // relative to 2^(M*c0); 0 if not computed
-};
-
-// Combines the partials; wl receives each chunk's weight relative to 2^(M*c0).
-template <bool SUM>
-__device__ __forceinline__ RowSums row_sums(const RowParts& rp, float c0, double (&wl)[MAX_ROUNDS]) {
-  float M = -INFINITY;
-  int arg = INT_SENTINEL;
-#pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) argmax_combine(M, arg, rp.m[t], rp.idx[t]);
-  wave_argmax(M, arg);
-  RowSums r;
-  r.M = M;
-  r.argmax = (M > -INFINITY && arg != INT_SENTINEL) ? arg : -1;
-  r.Z = 0.0;
-  if constexpr (SUM) {
-    const double Mc0 = (double)M * (double)c0;
-    double local = 0.0;
-#pragma unroll
-    for (int t = 0; t < MAX_ROUNDS; ++t) {
-      wl[t] = (rp.m[t] == -INFINITY) ? 0.0 : rp.s[t] * pow2_neg((double)chunk_mc0(rp.m[t], c0) - Mc0);
-      local += wl[t];
-    }
-    r.Z = wave_sum(local);
-  }
-  return r;
-}
-
-// Inverse-CDF draw from softmax(row / T) with uniform u, given the row's chunk
-// partials: pick the chunk, then scan inside it. -1 if the row has no weight.
-template <int DT>
-__device__ __forceinline__ int softmax_draw(const char* row, int64_t V, int C, float c0, float u,
-                                            const RowParts& rp, const RowSums& rs, const double (&wl)[MAX_ROUNDS]) {
-  constexpr int W = DTraits<DT>::W;
-  const ChunkPick pk = pick_chunk(C, (double)u, wl);
-  if (pk.c < 0) return -1;
-  const int tc = pk.c / WAVE, lc = pk.c % WAVE;
-  float mm = rp.m[0];
-#pragma unroll
-  for (int t = 1; t < MAX_ROUNDS; ++t) if (t == tc) mm = rp.m[t];
-  const float mstar = __shfl(mm, lc);
-  const float mc0 = chunk_mc0(mstar, c0);
-  // threshold in the chunk's own units (weights relative to its mc0)
-  const double th = pk.fallback ? (double)INFINITY
-                                : (pk.theta - pk.before) * exp2((double)rs.M * (double)c0 - (double)mc0);
-  Raw r;
-  const Chunk k = load_chunk<DT>(row, V, pk.c, r);
-  SoftmaxW sw;
-  sw.c0 = c0;
-  sw.mc0 = mc0;
-  const int64_t y = chunk_invcdf<DT, false>(k, r, r, th, sw);
-  return (int)y;
-}
-
-// The same draw when no partials are at hand: the wave streams the row once to
-// build them (used only for the residual of two rows equal up to rounding).
-template <int DT>
-__device__ __forceinline__ int softmax_draw_streamed(const char* row, int64_t V, int C, float c0, float u) {
-  const int lane = lane_id();
-  RowParts rp;
-#pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
-    rp.m[t] = -INFINITY;
-    rp.idx[t] = INT_SENTINEL;
-    rp.s[t] = 0.0;
-  }
-#pragma unroll 1
-  for (int c = 0; c < C; ++c) {
-    const Partial p = chunk_partial<DT, true, false>(row, V, c, c0);
-    const int t = c / WAVE;
-#pragma unroll
-    for (int q = 0; q < MAX_ROUNDS; ++q)
-      if (q == t && lane == c % WAVE) {
-        rp.m[q] = p.m;
-        rp.s[q] = p.s;
-      }
-  }
-  rp.got = true;
-  double wl[MAX_ROUNDS];
-  const RowSums rs = row_sums<true>(rp, c0, wl);
-  if (!(rs.Z > 0.0) || !__builtin_isfinite(rs.Z)) return -1;
-  return softmax_draw<DT>(row, V, C, c0, u, rp, rs, wl);
-}
 
 __device__ __forceinline__ ResidW make_residw(const Decision& d, float c0) {
   ResidW rw;
@@ -1051,36 +912,7 @@ __global__ __launch_bounds__(BLOCK) void clear_kernel(unsigned char* p, size_t b
   for (size_t i = n16 * 16 + (size_t)blockIdx.x * BLOCK + threadIdx.x; i < bytes; i += stride) p[i] = 0;
 }
 
-// ------------------------------------------------------------------ host helpers
-int elem_bytes(sv_dtype dt) { return dt == SV_F32 ? 4 : 2; }
-bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_BF16 || dt == SV_F16; }
-
-int64_t chunks_per_row(int64_t V, sv_dtype dt) {
-  const int64_t W = 16 / elem_bytes(dt);
-  const int64_t units = (V + W - 1) / W;
-  return (units + CHUNK_UNITS - 1) / CHUNK_UNITS;
-}
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-struct Layout {
-  size_t off[14];
-  size_t total;
-};
-
-// Regions back to back, each 256-byte aligned.
-Layout make_layout(std::initializer_list<size_t> sizes) {
-  Layout L{};
-  size_t o = 0;
-  int i = 0;
-  for (size_t s : sizes) {
-    L.off[i++] = o;
-    o += align256(s);
-  }
-  L.total = o;
-  return L;
-}
-
+// ------------------------------------------------------------------ host side
 Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
   const int64_t R = (mode == SV_STOCHASTIC) ? 2 * k + 1 : k + 1;
   const int64_t RQ = B * R;
@@ -1099,31 +931,6 @@ Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
 Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
   const int64_t C = chunks_per_row(V, dt);
   return make_layout({(size_t)(rows * C) * PART_WORDS * 8, (size_t)(rows * CSTRIDE) * 4});
-}
-
-bool temperature_ok(float T) { return std::isfinite(T) && T > 0.0f; }
-
-float temperature_c0(float T) { return (float)(LOG2E / (double)T); }
-
-sv_status launch_status() {
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
-}
-
-// A fresh record tag per call: odd (never the cleared value 0), distinct from the
-// tags of the last 2^31 calls of this process.
-std::atomic<uint32_t> g_tag{0};
-uint32_t next_tag() { return (g_tag.fetch_add(1, std::memory_order_relaxed) << 1) | 1u; }
-
-unsigned blocks_for(int64_t waves) { return (unsigned)((waves + WPB - 1) / WPB); }
-
-template <template <int, bool> class Launcher, class... Args>
-sv_status dispatch(sv_dtype dt, bool stoch, Args&&... args) {
-  switch (dt) {
-    case SV_F32: return stoch ? Launcher<DT_F32, true>::run(args...) : Launcher<DT_F32, false>::run(args...);
-    case SV_BF16: return stoch ? Launcher<DT_BF16, true>::run(args...) : Launcher<DT_BF16, false>::run(args...);
-    case SV_F16: return stoch ? Launcher<DT_F16, true>::run(args...) : Launcher<DT_F16, false>::run(args...);
-  }
-  return SV_EDTYPE;
 }
 
 template <int DT, bool STOCH>
@@ -1165,19 +972,6 @@ struct RowStatsLauncher {
     return launch_status();
   }
 };
-
-bool ws_ok(const void* ws, size_t have, size_t need) {
-  return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0 && have >= need;
-}
-
-// Waves of one launch, and rows x chunks as 32-bit indices.
-constexpr int64_t MAX_WAVES = 0x7fffffffLL;
-
-static_assert((int64_t)MAX_CHUNKS * CHUNK_UNITS * 16 == SV_MAX_ROW_BYTES, "row limit of the header");
-
-bool shape_ok(int64_t V, sv_dtype dt) {
-  return V <= 0x7fffffffLL - 16 && chunks_per_row(V, dt) <= MAX_CHUNKS;
-}
 
 }  // namespace
 

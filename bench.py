@@ -56,13 +56,16 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources and the header, in a fixed order."""
+    """sha256 over what defines the verification kernels: their sources, the
+    header and the compiler flags, in a fixed order."""
     import hashlib
+    from acceptance_row_softmax_amd import _build
     h = hashlib.sha256()
     for rel in ("acceptance_row_softmax_amd/csrc/specverify.hip", "acceptance_row_softmax_amd/csrc/sv_device.hpp",
-                "acceptance_row_softmax_amd/_build.py", "include/specverify.h"):
+                "include/specverify.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    h.update(" ".join(_build.HIPCC_FLAGS).encode())
     return h.hexdigest()
 
 

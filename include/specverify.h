@@ -20,10 +20,21 @@
  *  [S-INF] same page, section "Inferenz mit spekulativem Decoding": the accepted
  *          count sets the next sequence length; the library never synchronises
  *          with the host, so results stay on the device.
+ *  [S-MTPZ] section "MTP-Zeitplan für ein einzelnes Token", further: after the
+ *          acceptance a kernel inserts the next target token into the target's input
+ *          tokens shifted one place left (section "MTP": the draft's token buffer is
+ *          shifted one place left against the target's hidden states), so that no
+ *          CPU-GPU synchronisation follows.
  *  [M-3]   "Speculative-Decoding, LLM推理的加速 / Medusa 方法阅读", section 三
  *          (Attention Tree): tree nodes get logits from one pass; the sampler's token
  *          at the root is looked up among level-1 candidates and followed level by
- *          level while a child matches.
+ *          level while a child matches. The tree is flattened into one sequence whose
+ *          attention mask lets a token see only itself and its ancestors, as a causal
+ *          mask does along a chain.
+ *  [M-4]   same page, section 四 (optimized tree construction): with per-head, per-rank
+ *          accuracies a_k^(i) taken as independent, a node's contribution to the
+ *          expected accepted length is the product of the accuracies on its path;
+ *          for a node budget, nodes are added greedily, largest contribution first.
  * The acceptance rule is the one of the method the Sonar page cites (Leviathan et
  * al.) but does not print: accept draft token x at position i iff
  * u_i < p_t,i(x) / p_d,i(x); after the first rejection at L, draw from
@@ -64,6 +75,8 @@
  *                          2^18 polls, a fraction of a second: only if the GPU did
  *                          not run the launch's workgroups in dispatch order, or a
  *                          concurrent call shared the workspace); outputs are not valid
+ *      bit4 SV_ERR_CAPACITY  (commit) the history buffer cannot take the new tokens
+ *      bit5 SV_ERR_UNVERIFIED (commit) the sequence's verification reported an error
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -89,7 +102,8 @@ typedef enum {
 typedef enum { SV_GREEDY = 0, SV_STOCHASTIC = 1 } sv_mode;
 typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
 
-enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4, SV_ERR_INTERNAL = 8 };
+enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4, SV_ERR_INTERNAL = 8,
+       SV_ERR_CAPACITY = 16, SV_ERR_UNVERIFIED = 32 };
 
 /* Limits: k <= SV_MAX_K drafts per sequence; n_nodes <= SV_MAX_TREE_NODES; a row
  * holds at most SV_MAX_ROW_BYTES of logits (V <= 1048576 for bf16/fp16, 524288 for
@@ -168,6 +182,76 @@ sv_status spec_row_stats(sv_dtype dtype, float temperature, int64_t rows, int64_
                          const void* x, float* row_max, float* row_lse, int32_t* row_argmax,
                          int32_t* err_flags, void* workspace, size_t workspace_bytes,
                          sv_stream_t stream);
+
+/* ---------------------------------------------------------------- commit (after verification)
+ * [S-MTPZ], [S-INF]. Applies the outcome of spec_verify_linear on the device, with no
+ * host synchronisation, for B sequences with k drafts:
+ *   accept_len [B], out_tokens [B][k+1]   the outputs of spec_verify_linear
+ *   draft_tokens [B][k]                   the drafts verified (needed for `shifted`)
+ *   seq_len    [B]            in/out: tokens in each sequence; grows by L+1
+ *   history    [B][capacity]  in/out: each sequence's tokens; out_tokens[b][0..L] are
+ *                             written at positions seq_len[b] .. seq_len[b]+L (may be NULL
+ *                             with capacity 0: lengths, shifted and next_token only)
+ *   shifted    [B][k+1]       optional out: the draft's input tokens for its pass over the
+ *                             verified positions, the target's inputs shifted one place left:
+ *                             position j holds the token that follows position j, i.e.
+ *                             out_tokens[b][j] (= x_j) for j < L, the target's token
+ *                             y = out_tokens[b][L] at j = L; positions after
+ *                             L hold x_j (their results are to be discarded) and position k
+ *                             holds y
+ *   next_token [B]            optional out: y, the first input of the next step
+ *   err_flags  [B]            optional out: SV_ERR_UNVERIFIED (accept_len outside [0, k]),
+ *                             SV_ERR_CAPACITY (seq_len + L + 1 > capacity); such a sequence
+ *                             keeps its length and history, and gets -1 in shifted and
+ *                             next_token
+ * One kernel launch, one wave per sequence.
+ */
+sv_status spec_commit_linear(int64_t B, int64_t k, const int32_t* accept_len, const int32_t* out_tokens,
+                             const int32_t* draft_tokens, int32_t* seq_len, int32_t* history,
+                             int64_t capacity, int32_t* shifted, int32_t* next_token,
+                             int32_t* err_flags, sv_stream_t stream);
+
+/* ---------------------------------------------------------------- sampler
+ * [S-MTP] (sampling shared by every scheme), [S-ZE]. One token per row of
+ * logits[rows][V]: argmax (SV_GREEDY: largest value, lowest index on ties) or the
+ * inverse-CDF draw from softmax(row / T) with uniforms[row] (SV_STOCHASTIC): the
+ * smallest v whose cumulative probability exceeds u. tokens[rows] out (-1 with
+ * SV_ERR_ROW if the row has no usable entry); err_flags[rows] optional. The same row
+ * reduction and draw as the verifier's; one kernel launch.
+ */
+size_t spec_sample_workspace(int64_t rows, int64_t V, sv_dtype dtype);
+
+sv_status spec_sample(sv_mode mode, float temperature, int64_t rows, int64_t V, sv_dtype dtype,
+                      const void* logits, const float* uniforms, int32_t* tokens, int32_t* err_flags,
+                      void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+/* ---------------------------------------------------------------- tree attention mask
+ * [M-3]. For n_trees trees of n_nodes (parent arrays as for spec_verify_tree):
+ * mask[t][i][w] (uint32 words, W = ceil(n_nodes / 32) per row) has bit (j mod 32) of
+ * word j / 32 set iff node j is node i or one of its ancestors. err_flags[t] optional
+ * (zeroed, then SV_ERR_TREE if the parent array is invalid; the mask of such a tree is
+ * unspecified). One kernel launch (two with err_flags); one wave per row.
+ */
+sv_status spec_tree_mask(int64_t n_trees, int64_t n_nodes, const int32_t* parent,
+                         int64_t parent_batch_stride, uint32_t* mask, int32_t* err_flags,
+                         sv_stream_t stream);
+
+/* ---------------------------------------------------------------- greedy sparse tree (host)
+ * [M-4]. HOST pointers; runs on the CPU (a one-off construction, no device work).
+ *   accuracy [K][S]   a_k^(i) at accuracy[(k-1)*S + (i-1)]: accuracy of the rank-i
+ *                     candidate of head k (tree depth k), each in [0, 1]
+ *   budget            candidate nodes wanted (the root is extra)
+ * Nodes are added one at a time, each time the candidate whose path product of
+ * accuracies is largest (ties: smaller depth, then the earlier-added parent, then the
+ * smaller rank), starting from the root's children; a node's children become
+ * candidates when it is added. Output (n = returned count, root included, at most
+ * budget + 1; fewer if the full tree of depth K is smaller): parent[n] in breadth-first
+ * order (by depth, then parent, then rank; parent[0] = -1, parent[i] < i), depth[n] and
+ * rank[n] optional (root: 0, 0), expected_len optional: the sum of the path products
+ * (the expected accepted length of the tree). Returns n, or -SV_EINVAL / -SV_ELIMIT.
+ */
+int64_t spec_tree_build_greedy(int64_t K, int64_t S, const double* accuracy, int64_t budget,
+                               int32_t* parent, int32_t* depth, int32_t* rank, double* expected_len);
 
 /* Zero-fill `bytes` of a 16-byte aligned workspace on `stream` with a fill kernel (no host sync). */
 sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream);

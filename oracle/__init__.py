@@ -26,6 +26,7 @@ MUT_INVCDF_GE = 4
 MUT_TREE_NO_ANCESTOR = 5
 MUT_TEMPERATURE_IGNORED = 6
 MUT_LSE_WITHOUT_MAX = 7
+MUT_COMMIT_REJECTED_DRAFT = 8
 
 
 def build(force: bool = True) -> str:
@@ -58,6 +59,14 @@ def lib():
                                       vp, vp, vp, vp, vp, vp, vp]
         L.orc_expected_accept_len.restype = dbl
         L.orc_expected_accept_len.argtypes = [i64, vp, vp, i64, vp]
+        L.orc_commit_linear.restype = i32
+        L.orc_commit_linear.argtypes = [i64, i64, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+        L.orc_sample.restype = i32
+        L.orc_sample.argtypes = [i32, dbl, i64, i64, i32, vp, vp, dbl, vp, vp, vp]
+        L.orc_tree_mask.restype = i32
+        L.orc_tree_mask.argtypes = [i64, vp, vp]
+        L.orc_tree_build_greedy.restype = i64
+        L.orc_tree_build_greedy.argtypes = [i64, i64, vp, i64, vp, vp, vp, vp]
         L.orc_set_mutation.restype = None
         L.orc_set_mutation.argtypes = [i32]
         _lib = L
@@ -161,3 +170,58 @@ def expected_accept_len(parent, rank, acc_table) -> float:
     acc_table = np.ascontiguousarray(np.asarray(acc_table, np.float64))
     S = acc_table.shape[1]
     return lib().orc_expected_accept_len(parent.size, _p(parent), _p(rank), S, _p(acc_table))
+
+
+def commit_linear(accept_len, out_tokens, drafts, seq_len, history=None):
+    """Returns (seq_len', history', {"shifted", "next_token", "err_flags"}); inputs untouched."""
+    acc = np.ascontiguousarray(np.asarray(accept_len, np.int32))
+    out = np.ascontiguousarray(np.asarray(out_tokens, np.int32))
+    B, k = out.shape[0], out.shape[1] - 1
+    dr = np.ascontiguousarray(np.asarray(drafts, np.int32).reshape(B, k)) if drafts is not None else None
+    ln = np.array(seq_len, np.int32, copy=True)
+    hist = np.array(history, np.int32, copy=True) if history is not None else None
+    cap = hist.shape[1] if hist is not None else 0
+    sh = np.empty((B, k + 1), np.int32)
+    nx = np.empty(B, np.int32)
+    ef = np.empty(B, np.int32)
+    rc = lib().orc_commit_linear(B, k, _p(acc), _p(out), _p(dr), _p(ln), _p(hist), cap, _p(sh), _p(nx), _p(ef))
+    if rc:
+        raise ValueError("orc_commit_linear: bad arguments")
+    return ln, hist, {"shifted": sh, "next_token": nx, "err_flags": ef}
+
+
+def sample(mode: str, T: float, x, uniforms, V: int, dtype: int, tie_eps: float = TIE_EPS):
+    x = np.ascontiguousarray(x)
+    rows = x.size // V
+    stoch = mode == "stochastic"
+    u = np.ascontiguousarray(np.asarray(uniforms, np.float32).reshape(rows)) if stoch else None
+    tok = np.empty(rows, np.int32)
+    ef = np.empty(rows, np.int32)
+    nt = np.empty(rows, np.int32)
+    rc = lib().orc_sample(1 if stoch else 0, T, rows, V, dtype, _p(x), _p(u), tie_eps, _p(tok), _p(ef), _p(nt))
+    if rc:
+        raise ValueError("orc_sample: bad arguments")
+    return {"tokens": tok, "err_flags": ef, "near_tie": nt}
+
+
+def tree_mask(parent):
+    """Dense [n][n] uint8 ancestor-or-self matrix, or None for an invalid parent array."""
+    parent = np.ascontiguousarray(np.asarray(parent, np.int32))
+    n = parent.size
+    dense = np.empty((n, n), np.uint8)
+    rc = lib().orc_tree_mask(n, _p(parent), _p(dense))
+    return None if rc else dense
+
+
+def tree_build_greedy(acc, budget: int):
+    acc = np.ascontiguousarray(np.asarray(acc, np.float64))
+    K, S = acc.shape
+    par = np.empty(budget + 1, np.int32)
+    dep = np.empty(budget + 1, np.int32)
+    rk = np.empty(budget + 1, np.int32)
+    E = ctypes.c_double()
+    n = lib().orc_tree_build_greedy(K, S, _p(acc), budget, _p(par), _p(dep), _p(rk), ctypes.byref(E))
+    if n < 0:
+        raise ValueError("orc_tree_build_greedy: bad arguments")
+    return {"parent": par[:n].copy(), "depth": dep[:n].copy(), "rank": rk[:n].copy(), "expected_len": E.value}
+

@@ -24,6 +24,7 @@ enum {
   MUT_TREE_NO_ANCESTOR = 5,    // tree node accepted on its own match, ancestry ignored
   MUT_TEMPERATURE_IGNORED = 6, // softmax at T = 1 whatever T is
   MUT_LSE_WITHOUT_MAX = 7,     // lse missing the m/T term
+  MUT_COMMIT_REJECTED_DRAFT = 8,  // commit keeps the rejected draft x_L in place of the target's token
 };
 
 const double kNaN = std::numeric_limits<double>::quiet_NaN();
@@ -124,6 +125,145 @@ bool near_draw(double u, const Draw& d, double eps) {
 }  // namespace
 
 extern "C" {
+
+int orc_commit_linear(int64_t B, int64_t k, const int32_t* accept_len, const int32_t* out_tokens,
+                      const int32_t* drafts, int32_t* seq_len, int32_t* history, int64_t capacity,
+                      int32_t* shifted, int32_t* next_token, int32_t* err_flags) {
+  if (B < 0 || k < 0 || !accept_len || !out_tokens || !seq_len) return -1;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t L = accept_len[b];
+    const int64_t len = seq_len[b];
+    int32_t err = 0;
+    if (L < 0 || L > k) err = 32;
+    else if (history && (len < 0 || len + L + 1 > capacity)) err = 16;
+    const int32_t* out = out_tokens + b * (k + 1);
+    const int32_t y = err ? -1 : out[L];
+    if (!err) {
+      // the sequence grows by the accepted drafts and the target's token
+      if (history)
+        for (int64_t j = 0; j <= L; ++j) history[b * capacity + len + j] = out[j];
+      if (history && g_mutation == MUT_COMMIT_REJECTED_DRAFT && L < k)
+        history[b * capacity + len + L] = drafts[b * k + L];
+      seq_len[b] = (int32_t)(len + L + 1);
+    }
+    if (shifted) {
+      // input of the draft at position j: the token that follows position j
+      for (int64_t j = 0; j <= k; ++j) {
+        int32_t v;
+        if (err) v = -1;
+        else if (j < L) v = out[j];          // accepted draft x_j
+        else if (j == L) v = y;              // the target's token
+        else if (j < k) v = drafts[b * k + j];  // not accepted: left as drafted
+        else v = y;                          // nothing follows the last position
+        shifted[b * (k + 1) + j] = v;
+      }
+    }
+    if (next_token) next_token[b] = y;
+    if (err_flags) err_flags[b] = err;
+  }
+  return 0;
+}
+
+int orc_sample(int mode, double T, int64_t rows, int64_t V, int dtype, const void* x,
+               const float* uniforms, double tie_eps, int32_t* tokens, int32_t* err_flags,
+               int32_t* near_tie) {
+  if (rows < 0 || V < 1 || !x || !tokens) return -1;
+  if (mode == 1 && (!(T > 0) || !uniforms)) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    const std::vector<double> row = load_row(dtype, x, r, V);
+    int64_t y = -1;
+    int32_t nt = 0;
+    if (mode == 0) {
+      const ArgMax a = argmax_of(row);
+      if (a.found) y = a.index;
+    } else {
+      const Softmax s = softmax_of(row, T);
+      if (s.ok) {
+        const Draw d = invcdf(s.z, (double)uniforms[r]);
+        y = d.y;
+        nt = near_draw((double)uniforms[r], d, tie_eps) ? 1 : 0;
+      }
+    }
+    tokens[r] = (int32_t)y;
+    if (err_flags) err_flags[r] = y < 0 ? 2 : 0;
+    if (near_tie) near_tie[r] = nt;
+  }
+  return 0;
+}
+
+int orc_tree_mask(int64_t n_nodes, const int32_t* parent, uint8_t* dense) {
+  if (n_nodes < 1 || !parent || !dense) return -1;
+  if (parent[0] != -1) return -1;
+  for (int64_t i = 1; i < n_nodes; ++i)
+    if (parent[i] < 0 || parent[i] >= i) return -1;
+  for (int64_t i = 0; i < n_nodes; ++i) {
+    uint8_t* row = dense + i * n_nodes;
+    if (i == 0) {
+      for (int64_t j = 0; j < n_nodes; ++j) row[j] = 0;
+    } else {
+      // what the parent sees, the node sees too
+      const uint8_t* prow = dense + (int64_t)parent[i] * n_nodes;
+      for (int64_t j = 0; j < n_nodes; ++j) row[j] = prow[j];
+    }
+    row[i] = 1;
+  }
+  return 0;
+}
+
+int64_t orc_tree_build_greedy(int64_t K, int64_t S, const double* acc, int64_t budget,
+                              int32_t* parent, int32_t* depth, int32_t* rank, double* expected_len) {
+  if (K < 1 || S < 1 || budget < 0 || !acc || !parent) return -1;
+  struct Node { double value; int64_t depth, rank, parent; };   // parent: index in `added`
+  std::vector<Node> added;
+  added.push_back({1.0, 0, 0, -1});
+  std::vector<Node> cand;
+  for (int64_t r = 1; r <= S; ++r) cand.push_back({acc[r - 1], 1, r, 0});
+  while ((int64_t)added.size() < budget + 1 && !cand.empty()) {
+    // the candidate that contributes most (ties: shallower, earlier parent, lower rank)
+    size_t best = 0;
+    for (size_t c = 1; c < cand.size(); ++c) {
+      const Node& a = cand[c];
+      const Node& b = cand[best];
+      bool better;
+      if (a.value != b.value) better = a.value > b.value;
+      else if (a.depth != b.depth) better = a.depth < b.depth;
+      else if (a.parent != b.parent) better = a.parent < b.parent;
+      else better = a.rank < b.rank;
+      if (better) best = c;
+    }
+    const Node nd = cand[best];
+    cand.erase(cand.begin() + (std::ptrdiff_t)best);
+    const int64_t id = (int64_t)added.size();
+    added.push_back(nd);
+    if (nd.depth < K)
+      for (int64_t r = 1; r <= S; ++r) cand.push_back({nd.value * acc[nd.depth * S + r - 1], nd.depth + 1, r, id});
+  }
+  // breadth-first numbering: a queue from the root, children in rank order
+  const int64_t n = (int64_t)added.size();
+  std::vector<std::vector<int64_t>> kids((size_t)n);
+  for (int64_t i = 1; i < n; ++i) kids[(size_t)added[(size_t)i].parent].push_back(i);
+  for (auto& v : kids)
+    for (size_t a = 1; a < v.size(); ++a)   // insertion sort by rank
+      for (size_t b = a; b > 0 && added[(size_t)v[b]].rank < added[(size_t)v[b - 1]].rank; --b)
+        std::swap(v[b], v[b - 1]);
+  std::vector<int64_t> queue(1, 0), num((size_t)n, -1);
+  num[0] = 0;
+  for (size_t h = 0; h < queue.size(); ++h)
+    for (int64_t c : kids[(size_t)queue[h]]) {
+      num[(size_t)c] = (int64_t)queue.size();
+      queue.push_back(c);
+    }
+  double E = 0;
+  for (size_t h = 0; h < queue.size(); ++h) {
+    const Node& nd = added[(size_t)queue[h]];
+    parent[h] = nd.parent < 0 ? -1 : (int32_t)num[(size_t)nd.parent];
+    if (depth) depth[h] = (int32_t)nd.depth;
+    if (rank) rank[h] = (int32_t)nd.rank;
+    if (h > 0) E += nd.value;
+  }
+  if (expected_len) *expected_len = E;
+  return n;
+}
 
 void orc_set_mutation(int which) { g_mutation = which; }
 

@@ -80,6 +80,45 @@ int orc_verify_tree(int mode, double T, int64_t B, int64_t n_nodes, int64_t V, i
 double orc_expected_accept_len(int64_t n_nodes, const int32_t* parent, const int32_t* rank,
                                int64_t S, const double* acc);
 
+/* Commit of a linear verification (Sonar page, section "MTP-Zeitplan für ein
+ * einzelnes Token": the target's input tokens shifted one place left, the next
+ * target token inserted at its place; section "Inferenz mit spekulativem
+ * Decoding": the accepted count sets the next length). For each sequence with
+ * L = accept_len[b] in [0, k] and len + L + 1 <= capacity (history NULL: no
+ * capacity check): history[b][len + j] = out_tokens[b][j] for j <= L, len += L + 1;
+ * shifted[b][j] = y (= out_tokens[b][L]) for j = L and j = k, else drafts[b][j];
+ * next_token[b] = y. Otherwise err 32 (L outside [0, k]) or 16 (capacity), nothing
+ * committed, shifted row and next_token -1. */
+int orc_commit_linear(int64_t B, int64_t k, const int32_t* accept_len, const int32_t* out_tokens,
+                      const int32_t* drafts, int32_t* seq_len, int32_t* history, int64_t capacity,
+                      int32_t* shifted, int32_t* next_token, int32_t* err_flags);
+
+/* One token per row of x[rows][V]: greedy = argmax (lowest index), stochastic =
+ * invcdf(softmax(x / T), u[row]) (Sonar page, sections "MTP" and "Ziel-Entwurf":
+ * sampling shared by all schemes). tokens -1 and err bit1 for a row without a usable
+ * entry; near_tie[row] (optional) 1 if u lies within tie_eps of an edge of the drawn
+ * bin. */
+int orc_sample(int mode, double T, int64_t rows, int64_t V, int dtype, const void* x,
+               const float* uniforms, double tie_eps, int32_t* tokens, int32_t* err_flags,
+               int32_t* near_tie);
+
+/* Tree attention mask (Medusa page, section 三): dense[i][j] = 1 iff node j is node i
+ * or an ancestor of it, built row by row as the parent's row plus node i itself.
+ * Returns 0, or -1 if the parent array is invalid (parent[0] != -1 or parent[i]
+ * outside [0, i)). */
+int orc_tree_mask(int64_t n_nodes, const int32_t* parent, uint8_t* dense);
+
+/* Greedy sparse tree (Medusa page, section 四): starting from the root, repeatedly
+ * add the candidate node with the largest product of accuracies along its path
+ * (acc[(depth-1)*S + rank-1]); ties by smaller depth, then the earlier-added parent,
+ * then smaller rank; the children of an added node (up to depth K) become
+ * candidates. Stops after `budget` nodes or when no candidate is left. Nodes are
+ * numbered in breadth-first order (children in rank order). Returns the node count
+ * n (root included); parent/depth/rank[n]; *expected_len = sum of the added nodes'
+ * products in node order. */
+int64_t orc_tree_build_greedy(int64_t K, int64_t S, const double* acc, int64_t budget,
+                              int32_t* parent, int32_t* depth, int32_t* rank, double* expected_len);
+
 /* Planted-mistake switch for negative-control tests only (0 = off). */
 void orc_set_mutation(int which);
 

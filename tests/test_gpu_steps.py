@@ -1,0 +1,204 @@
+"""GPU parity of the steps around verification against the oracle: commit
+(bit-exact, and end to end: speculative greedy decoding through the GPU verify and
+commit entry points equals plain greedy decoding), the sampler (bit-exact except
+draws within 1e-6 of a bin edge, counted), and the tree mask (bit-exact)."""
+import numpy as np
+import pytest
+
+import acceptance_row_softmax_amd as sv
+import gen
+import oracle
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _cpu(t):
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------ commit
+@pytest.mark.parametrize("k", [0, 1, 4, 31])
+def test_commit_matches_oracle(k):
+    import torch
+    rng = np.random.default_rng(200 + k)
+    B, cap = 300, 64
+    acc = rng.integers(0, k + 1, size=B).astype(np.int32)
+    acc[::17] = -1                                     # failed verifications
+    out = rng.integers(0, 1000, size=(B, k + 1)).astype(np.int32)
+    drafts = rng.integers(0, 1000, size=(B, k)).astype(np.int32)
+    ln = rng.integers(0, cap, size=B).astype(np.int32)
+    ln[5::11] = cap                                     # full histories: no room left
+    hist = rng.integers(0, 1000, size=(B, cap)).astype(np.int32)
+    G.say(f"commit k={k} B={B}")
+    d_ln, d_hist = G.to_dev(ln), G.to_dev(hist)
+    r = sv.commit_linear(G.to_dev(acc), G.to_dev(out), G.to_dev(drafts) if k else None, d_ln, d_hist)
+    torch.cuda.synchronize()
+    o_ln, o_hist, o = oracle.commit_linear(acc, out, drafts if k else None, ln, hist)
+    np.testing.assert_array_equal(_cpu(r["err_flags"]), o["err_flags"])
+    np.testing.assert_array_equal(_cpu(d_ln), o_ln)
+    np.testing.assert_array_equal(_cpu(d_hist), o_hist)
+    np.testing.assert_array_equal(_cpu(r["shifted"]), o["shifted"])
+    np.testing.assert_array_equal(_cpu(r["next_token"]), o["next_token"])
+    assert np.any(o["err_flags"] == 16) and np.any(o["err_flags"] == 32) and np.any(o["err_flags"] == 0)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "stochastic"])
+def test_speculative_decoding_on_device(mode):
+    """Rounds of draft (host, from a table) -> GPU verify -> GPU commit on a
+    Markov-chain model. Greedy: the history equals plain greedy decoding of the
+    target. Stochastic: it equals the oracle's verify + commit run on the same
+    uniforms, round for round."""
+    import torch
+    rng = np.random.default_rng(31)
+    V, k, B, n = 64, 4, 8, 48
+    target = rng.normal(0, 2, size=(V, V))
+    draft = target + rng.normal(0, 1.0, size=(V, V))
+    cap = n + k + 2
+    hist = np.full((B, cap), -1, np.int32)
+    hist[:, 0] = np.arange(B) % V
+    d_hist, d_ln = G.to_dev(hist), G.to_dev(np.ones(B, np.int32))
+    o_hist, o_ln = hist.copy(), np.ones(B, np.int32)
+    G.say(f"speculative decoding {mode} V={V} k={k} B={B}")
+    for rnd in range(3 * n):
+        ln = _cpu(d_ln)
+        if ln.min() >= n + 1:
+            break
+        h = _cpu(d_hist)
+        last = h[np.arange(B), ln - 1]
+        drafts = np.empty((B, k), np.int32)
+        cur = last.copy()
+        for i in range(k):
+            cur = np.argmax(draft[cur], axis=1).astype(np.int32)
+            drafts[:, i] = cur
+        inputs = np.concatenate([last[:, None], drafts], axis=1)
+        tgt = np.ascontiguousarray(target[inputs].astype(np.float32))
+        drf = np.ascontiguousarray(draft[inputs[:, :k]].astype(np.float32))
+        u = gen.uniforms(gen.key(95, rnd, 1), B * (k + 1)).reshape(B, k + 1).astype(np.float32)
+        g = sv.verify_linear(G.to_dev(tgt), G.to_dev(drf), G.to_dev(drafts), G.to_dev(u), mode=mode,
+                             temperature=1.0)
+        sv.commit_linear(g["accept_len"], g["out_tokens"], G.to_dev(drafts), d_ln, d_hist)
+        torch.cuda.synchronize()
+        if mode == "stochastic":
+            o = oracle.verify_linear(mode, 1.0, tgt, drf, drafts, u, V, gen.DT_F32)
+            assert not np.any(o["near_tie"]), "a draw at a bin edge: choose another seed"
+            o_ln, o_hist, _ = oracle.commit_linear(o["accept_len"], o["out_tokens"], drafts, o_ln, o_hist)
+            np.testing.assert_array_equal(_cpu(d_hist), o_hist)
+    ln = _cpu(d_ln)
+    assert ln.min() >= n + 1
+    h = _cpu(d_hist)
+    if mode == "greedy":
+        for b in range(B):
+            chain = [int(h[b, 0])]
+            for _ in range(n):
+                chain.append(int(np.argmax(target[chain[-1]])))
+            np.testing.assert_array_equal(h[b, :n + 1], chain)
+
+
+# ------------------------------------------------------------------ sampler
+def _sample_check(x, V, dtype, mode, T, u):
+    import torch
+    g = sv.sample(G.to_dev(x, dtype), G.to_dev(u) if mode == "stochastic" else None, mode=mode,
+                  temperature=T)
+    torch.cuda.synchronize()
+    o = oracle.sample(mode, T, x, u, V, dtype)
+    gt = _cpu(g["tokens"])
+    np.testing.assert_array_equal(_cpu(g["err_flags"]), o["err_flags"])
+    differ = gt != o["tokens"]
+    bad = differ & (o["near_tie"] == 0)
+    assert not bad.any(), (np.nonzero(bad)[0][:5], gt[bad][:5], o["tokens"][bad][:5])
+    if mode == "greedy":
+        assert not differ.any()
+    G._record(differ, o["near_tie"], np.full(len(gt), 1 if mode == "stochastic" else 0))
+    return gt, o
+
+
+def test_sampler_draft_rows_c2():
+    # the draft rows of the draft-target workload: 32 sequences x 4 positions,
+    # V = 128256 bf16, T = 0.7
+    w = gen.c2_linear(0)
+    x = np.ascontiguousarray(w.draft.reshape(-1, w.V))
+    u = gen.uniforms(gen.key(96, 0, 1), x.shape[0]).astype(np.float32)
+    G.say(f"sampler rows={x.shape[0]} V={w.V} bf16 T=0.7")
+    _sample_check(x, w.V, w.dtype, "stochastic", 0.7, u)
+    _sample_check(x, w.V, w.dtype, "greedy", 1.0, u)
+
+
+@pytest.mark.parametrize("dtype", [gen.DT_F32, gen.DT_BF16, gen.DT_F16])
+@pytest.mark.parametrize("V", [7, 1000, 20001, 65536])
+def test_sampler_ragged(dtype, V):
+    rows = 37
+    x = gen.normal_pair(gen.key(97, V, dtype), 2.5, 0, 0.0, rows * V, dtype, want_b=False)[0].reshape(rows, V)
+    u = gen.uniforms(gen.key(97, V, 9), rows).astype(np.float32)
+    G.say(f"sampler ragged V={V} dtype={dtype}")
+    for mode, T in (("stochastic", 0.8), ("greedy", 1.0)):
+        _sample_check(x, V, dtype, mode, T, u)
+
+
+def test_sampler_error_rows():
+    V = 3000
+    x = np.random.default_rng(5).normal(size=(4, V)).astype(np.float32)
+    x[1] = -np.inf
+    x[2, 17] = np.nan
+    x[3, 5] = np.inf
+    u = np.full(4, 0.5, np.float32)
+    for mode in ("greedy", "stochastic"):
+        gt, o = _sample_check(x, V, gen.DT_F32, mode, 1.0, u)
+        assert gt[1] == -1
+
+
+# ------------------------------------------------------------------ tree mask
+def _unpack(mask, n):
+    w = mask.view(np.uint32)
+    bits = (w[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
+    return bits.reshape(*w.shape[:-1], -1)[..., :n].astype(np.uint8)
+
+
+def test_tree_mask_cartesian():
+    import torch
+    parent, _ = gen.cartesian_tree([8, 8, 8, 8])
+    G.say("tree mask cartesian 4681")
+    r = sv.tree_mask(G.to_dev(parent))
+    torch.cuda.synchronize()
+    m = _unpack(_cpu(r["mask"])[0], len(parent))
+    np.testing.assert_array_equal(m, oracle.tree_mask(parent))
+    assert _cpu(r["err_flags"])[0] == 0
+
+
+def test_tree_mask_per_tree_and_errors():
+    import torch
+    rng = np.random.default_rng(9)
+    T, n = 6, 300
+    par = np.stack([np.array([-1] + [int(rng.integers(max(0, i - 5), i)) for i in range(1, n)], np.int32)
+                    for _ in range(T)])
+    par[2] = np.arange(-1, n - 1)                # a chain: the causal mask
+    par[4, 100] = 150                            # not an earlier node
+    par[5, 0] = 0                                # root without parent -1
+    G.say("tree mask per-tree")
+    r = sv.tree_mask(G.to_dev(par))
+    torch.cuda.synchronize()
+    ef = _cpu(r["err_flags"])
+    assert list(ef) == [0, 0, 0, 0, 4, 4]
+    m = _unpack(_cpu(r["mask"]), n)
+    for t in range(4):
+        np.testing.assert_array_equal(m[t], oracle.tree_mask(par[t]))
+    np.testing.assert_array_equal(m[2], np.tril(np.ones((n, n), np.uint8)))
+
+
+def test_tree_mask_deep_chain_max_nodes():
+    import torch
+    n = sv.SV_MAX_TREE_NODES
+    parent = np.arange(-1, n - 1, dtype=np.int32)
+    G.say(f"tree mask chain n={n}")
+    r = sv.tree_mask(G.to_dev(parent))
+    torch.cuda.synchronize()
+    w = _cpu(r["mask"])[0].view(np.uint32)
+    # row i: bits 0..i set; check every row's word count and sampled rows in full
+    W = (n + 31) // 32
+    full = np.uint32(0xFFFFFFFF)
+    for i in list(range(0, 70)) + list(range(n - 70, n)) + list(range(4000, 4100)):
+        nw = i // 32
+        assert np.all(w[i, :nw] == full)
+        assert w[i, nw] == np.uint32((1 << (i % 32 + 1)) - 1 if i % 32 < 31 else 0xFFFFFFFF)
+        assert np.all(w[i, nw + 1:W] == 0)
+    assert _cpu(r["err_flags"])[0] == 0
