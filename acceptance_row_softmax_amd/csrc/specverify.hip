@@ -105,14 +105,10 @@ __device__ __forceinline__ ResidW make_residw(const Decision& d, float c0) {
   return rw;
 }
 
-// Residual sum over chunk c of rows t_L, d_L (same value in every lane).
+// Residual sum over a loaded chunk of rows t_L, d_L (same value in every lane).
 template <int DT>
-__device__ __forceinline__ double residual_chunk_sum(const char* trow, const char* drow, int64_t V, int64_t c,
-                                                     const ResidW& rw) {
+__device__ __forceinline__ double residual_raw_sum(const Raw& rt, const Raw& rd, const ResidW& rw) {
   constexpr int W = DTraits<DT>::W;
-  Raw rt, rd;
-  load_chunk<DT>(trow, V, c, rt);
-  load_chunk<DT>(drow, V, c, rd);
   double s = 0.0;
 #pragma unroll
   for (int j = 0; j < CU; ++j) {
@@ -189,56 +185,83 @@ __device__ __forceinline__ const char* row_ptr(const LinearParams& P, int64_t b,
 // error bits, and the accepted drafts.
 constexpr int TOKEN_UNKNOWN = INT_SENTINEL;
 
-template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b, int known_y) {
-  const int lane = lane_id();
-  const int64_t k = P.k, V = P.V;
-  uint64_t s = 0;
-  uint32_t ew = 0;
+// What the emission of sequence b reads (per lane), and the reading: issued as
+// soon as the emitting wave knows it is last, so that it can overlap a draw.
+struct EmitIn {
+  uint64_t s;
+  uint32_t ew;
   Token t;
-  t.y = -2;
-  bool tg = true;
-  if (lane == 0) s = state_load(P.state + b * SSTRIDE);
-  if (lane == 1) ew = __hip_atomic_load(P.errw + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane == 2 && known_y == TOKEN_UNKNOWN) tg = get_rec(P.tok + b, t, P.tag);
-  const bool has = lane < k;
-  const int x = has ? P.tokens[b * k + lane] : 0;
+  bool tg, pg;
+  int x;
   Probs pr;
-  pr.pt = pr.pd = NAN;
-  bool pg = true;
+};
+
+template <int DT, bool STOCH>
+__device__ __forceinline__ EmitIn emit_load(const LinearParams& P, int64_t b, bool token_known) {
+  const int lane = lane_id();
+  const int64_t k = P.k;
+  EmitIn in;
+  in.s = 0;
+  in.ew = 0;
+  in.t.y = -2;
+  in.tg = true;
+  in.pg = true;
+  if (lane == 0) in.s = state_load(P.state + b * SSTRIDE);
+  if (lane == 1) in.ew = __hip_atomic_load(P.errw + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 2 && !token_known) in.tg = get_rec(P.tok + b, in.t, P.tag);
+  const bool has = lane < k;
+  in.x = has ? P.tokens[b * k + lane] : 0;
+  in.pr.pt = in.pr.pd = NAN;
   if (STOCH && has) {
-    pg = get_rec(P.prob + (b * k + lane) * PROB_WORDS, pr, P.tag);
+    in.pg = get_rec(P.prob + (b * k + lane) * PROB_WORDS, in.pr, P.tag);
     clear_rec<Probs>(P.prob + (b * k + lane) * PROB_WORDS);
   }
   // leave the sequence's words and records zero for the next call
   if (lane == 0) counter_reset(P.state + b * SSTRIDE);
   if (lane == 1) counter_reset(P.errw + b * CSTRIDE);
-  if (lane == 2 && known_y == TOKEN_UNKNOWN) clear_rec<Token>(P.tok + b);
+  if (lane == 2 && !token_known) clear_rec<Token>(P.tok + b);
   if (lane < P.R) {
     const int64_t i = lane <= k ? lane : lane - k - 1;
     clear_rec<RowStat>(P.rows + row_q<STOCH>(P, b, i, lane <= k ? 0 : 1) * ROW_WORDS);
   }
-  s = __shfl(s, 0);
-  int err = (int)__shfl(ew, 1);
-  const int y = known_y != TOKEN_UNKNOWN ? known_y : __shfl(tg ? t.y : -2, 2);
+  return in;
+}
+
+// Writes every output of sequence b (its last event): the first rejected
+// position from the state word, the final token (known_y, or the token record),
+// the error bits, and the accepted drafts. One writer per output.
+template <int DT, bool STOCH>
+__device__ __forceinline__ void emit_store(const LinearParams& P, int64_t b, const EmitIn& in, int known_y) {
+  const int lane = lane_id();
+  const int64_t k = P.k, V = P.V;
+  const bool has = lane < k;
+  const uint64_t s = __shfl(in.s, 0);
+  int err = (int)__shfl(in.ew, 1);
+  const int y = known_y != TOKEN_UNKNOWN ? known_y : __shfl(in.tg ? in.t.y : -2, 2);
   const uint64_t rej = (s >> 32) & ((1ull << k) - 1);
   const int L = rej ? __builtin_ctzll(rej) : (int)k;
-  if (__ballot(has && (x < 0 || x >= V))) err |= SV_ERR_TOKEN;
-  if (y == -2 || __ballot(!pg)) err |= SV_ERR_INTERNAL;
+  if (__ballot(has && (in.x < 0 || in.x >= V))) err |= SV_ERR_TOKEN;
+  if (y == -2 || __ballot(!in.pg)) err |= SV_ERR_INTERNAL;
   if (STOCH && has) {
-    if (P.p_target) P.p_target[b * k + lane] = err ? NAN : pr.pt;
-    if (P.p_draft) P.p_draft[b * k + lane] = err ? NAN : pr.pd;
+    if (P.p_target) P.p_target[b * k + lane] = err ? NAN : in.pr.pt;
+    if (P.p_draft) P.p_draft[b * k + lane] = err ? NAN : in.pr.pd;
   }
   int32_t* out = P.out_tokens + b * (k + 1);
   for (int64_t j = lane; j <= k; j += WAVE) {
     int v = -1;
-    if (!err) v = (j < L) ? x : (j == L ? y : -1);
+    if (!err) v = (j < L) ? in.x : (j == L ? y : -1);
     out[j] = v;
   }
   if (lane == 0) {
     P.accept_len[b] = err ? -1 : L;
     if (P.err_flags) P.err_flags[b] = err;
   }
+}
+
+template <int DT, bool STOCH>
+__device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b, int known_y) {
+  const EmitIn in = emit_load<DT, STOCH>(P, b, known_y != TOKEN_UNKNOWN);
+  emit_store<DT, STOCH>(P, b, in, known_y);
 }
 
 // Counts one event of sequence b (R row combines and the final token); the last
@@ -458,8 +481,11 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);
   if (d.kind == 1) {
+    Raw rt, rd;
+    load_chunk<DT>(trow, P.V, c, rt);
+    load_chunk<DT>(drow, P.V, c, rd);
     ResPart r;
-    r.s = residual_chunk_sum<DT>(trow, drow, P.V, c, rw);
+    r.s = residual_raw_sum<DT>(rt, rd, rw);
     if (lane == 0) put_rec(P.res + (b * P.C + c) * RES_WORDS, r, P.tag);
   }
   uint32_t old = 0;
@@ -474,6 +500,17 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
   if (d.kind == 0) return;   // no draft rejected: the bonus token is recorded already
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind == 1) {
+    // The token event counts before the draw: if it is the sequence's last event,
+    // this wave emits and reads the emission's inputs while the draw's loads are
+    // in flight; otherwise the last event's wave waits for the token record.
+    uint32_t fo = 0;
+    if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
+    const bool last = bcast(fo) + 1 == (uint32_t)P.R + 1u;
+    EmitIn ein;
+    if (last) {
+      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+      ein = emit_load<DT, true>(P, b, true);
+    }
     double wl[MAX_ROUNDS];
     bool ok = true;
 #pragma unroll
@@ -506,6 +543,14 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
         y = softmax_draw_streamed<DT>(trow, P.V, P.C, P.c0, u);
       }
     }
+    if (last) {
+      emit_store<DT, true>(P, b, ein, y);
+    } else if (lane == 0) {
+      Token t;
+      t.y = y;
+      put_rec(P.tok + b, t, P.tag);
+    }
+    return;
   }
   linear_event<DT, true>(P, b, true, y);
 }

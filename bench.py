@@ -20,6 +20,7 @@ or a tree step's two launches), parity.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -41,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2_linear",
-                    choices=["c1_tiny", "c2_linear", "c3_mtp", "c4_medusa_sparse", "c5_medusa_full"])
+                    choices=["c1_tiny", "c2_linear", "c3_mtp", "c4_medusa_sparse", "c5_medusa_full",
+                             *STEP_CONFIGS])
     ap.add_argument("--mode", default=None, help="greedy | stochastic (default: the config's own)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
@@ -62,6 +64,7 @@ def kernel_source_hash() -> str:
     from acceptance_row_softmax_amd import _build
     h = hashlib.sha256()
     for rel in ("acceptance_row_softmax_amd/csrc/specverify.hip", "acceptance_row_softmax_amd/csrc/sv_device.hpp",
+                "acceptance_row_softmax_amd/csrc/sv_rows.hpp", "acceptance_row_softmax_amd/csrc/sv_host.hpp",
                 "include/specverify.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read() + b"\0")
@@ -101,6 +104,158 @@ def copy_probe(mib: int):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "copies": 10}), flush=True)
+
+
+# The steps around verification, each timed on its own (one JSON line each):
+#  sample_c2_step  one draft position of the draft-target workload sampled on the
+#                  device: 32 rows of V = 128256 bf16 at T = 0.7
+#  sample_c3       the first token of the MTP workload sampled from the carried
+#                  logits: 256 rows of V = 129280 bf16 at T = 1
+#  commit_c3       commit of the MTP workload's verification: B = 256, k = 1
+#  tree_mask_c5    attention mask of the Cartesian K = 4, top-8 tree (4681 nodes)
+STEP_CONFIGS = ("sample_c2_step", "sample_c3", "commit_c3", "tree_mask_c5")
+
+
+def _graph_time(torch, calls, copies, steps, warmup):
+    """Warm up, capture `copies` calls in one graph, replay it; returns
+    (K, wall ms per call, event ms per call)."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        calls(i % copies)
+    torch.cuda.synchronize()
+    K = max(copies, (steps // copies) * copies)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(copies):
+            calls(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(K // copies):
+        graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return K, (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K
+
+
+def bench_steps(args):
+    import numpy as np
+    import torch
+
+    import acceptance_row_softmax_amd as sv
+    import gen
+    import oracle
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = args.config
+    cpu = None
+    if cfg.startswith("sample"):
+        if cfg == "sample_c2_step":
+            w = gen.c2_linear(args.seed)
+            x, T = np.ascontiguousarray(w.draft[:, 0, :]), 0.7
+        else:
+            w = gen.c3_mtp(args.seed, "stochastic")
+            x, T = np.ascontiguousarray(w.target[:, 0, :]), 1.0
+        mode = args.mode or "stochastic"
+        rows, V = x.shape
+        u = gen.uniforms(gen.key(98, args.seed, 1), rows).astype(np.float32)
+        esz = 4 if w.dtype == gen.DT_F32 else 2
+        alg = rows * V * esz
+        tdt = {gen.DT_F32: torch.float32, gen.DT_BF16: torch.bfloat16, gen.DT_F16: torch.float16}[w.dtype]
+        base = torch.from_numpy(x.view(np.int16) if esz == 2 else x).to(dev).view(tdt)
+        copies = max(1, math.ceil(3 * INFINITY_CACHE_BYTES / alg) + 1)
+        xs = [base] + [base.clone() for _ in range(copies - 1)]
+        du = torch.from_numpy(u).to(dev)
+        ws = torch.zeros(sv.lib().spec_sample_workspace(rows, V, sv.sv_dtype(base)), dtype=torch.uint8, device=dev)
+        first = sv.sample(xs[0], du, mode=mode, temperature=T, workspace=ws)
+        torch.cuda.synchronize()
+        o = oracle.sample(mode, T, x, u, V, w.dtype)
+        differ = first["tokens"].cpu().numpy() != o["tokens"]
+        parity = {"checked": int(rows), "exceptions": int(differ.sum()),
+                  "near_tie_sequences": int(o["near_tie"].sum()), "ok": bool(not (differ & (o["near_tie"] == 0)).any())}
+        K, ms, ev_ms = _graph_time(torch, lambda i: sv.sample(xs[i], du, mode=mode, temperature=T, workspace=ws),
+                                   copies, args.steps, args.warmup)
+        t0 = time.perf_counter()
+        n_rep = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.sample(mode, T, x, u, V, w.dtype)
+            n_rep += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": n_rep * rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"the full batch ({rows} rows) x {n_rep}, {el:.1f}s, single-threaded oracle"}
+        metric, unit, value = "sampled rows/sec + logit GB/s (% HBM peak)", "rows/s", rows / (ms * 1e-3)
+        kernel, dtype = "sample_kernel", gen.DTYPE_NAMES[w.dtype]
+        workload = f"{cfg}: {rows} rows of V={V} {dtype} logits, {mode}" + (f" T={T}" if mode == "stochastic" else "")
+    elif cfg == "commit_c3":
+        B, k, cap = 256, 1, 1 << 16
+        rng = np.random.default_rng(args.seed)
+        acc = rng.integers(0, k + 1, size=B).astype(np.int32)
+        out = rng.integers(0, 129280, size=(B, k + 1)).astype(np.int32)
+        drafts = out[:, :k].copy()
+        ln = rng.integers(100, 3000, size=B).astype(np.int32)
+        hist = np.zeros((B, cap), np.int32)
+        d = {n_: torch.from_numpy(a).to(dev) for n_, a in (("acc", acc), ("out", out), ("x", drafts))}
+        dl, dh = torch.from_numpy(ln).to(dev), torch.from_numpy(hist).to(dev)
+        first = sv.commit_linear(d["acc"], d["out"], d["x"], dl, dh)
+        torch.cuda.synchronize()
+        o_ln, o_hist, o = oracle.commit_linear(acc, out, drafts, ln, hist)
+        ok = (np.array_equal(dl.cpu().numpy(), o_ln) and np.array_equal(dh.cpu().numpy(), o_hist)
+              and np.array_equal(first["shifted"].cpu().numpy(), o["shifted"]))
+        parity = {"checked": B, "exceptions": 0 if ok else B, "near_tie_sequences": 0, "ok": bool(ok)}
+        sh = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+        nx = torch.empty(B, dtype=torch.int32, device=dev)
+        ef = torch.empty(B, dtype=torch.int32, device=dev)
+        L = sv.lib()
+
+        def call(i):
+            # the current stream at call time: the capture stream inside graph capture
+            st = L.spec_commit_linear(B, k, d["acc"].data_ptr(), d["out"].data_ptr(), d["x"].data_ptr(),
+                                      dl.data_ptr(), dh.data_ptr(), cap, sh.data_ptr(), nx.data_ptr(),
+                                      ef.data_ptr(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            assert st == 0
+        steps = min(args.steps, 8000)     # lengths grow by at most 2 per call: stay within capacity
+        K, ms, ev_ms = _graph_time(torch, call, 8, steps, args.warmup)
+        alg = B * (4 + (k + 1) * 4 + k * 4 + 4) + B * (4 + (k + 1) * 4 * 2 + 4 + 4)
+        metric, unit, value = "committed sequences/sec", "sequences/s", B / (ms * 1e-3)
+        kernel, dtype, workload = "commit_kernel", "int32", f"{cfg}: B={B} sequences, k={k}, history capacity {cap}"
+    else:   # tree_mask_c5
+        parent, _ = gen.cartesian_tree([8, 8, 8, 8])
+        n = len(parent)
+        W = (n + 31) // 32
+        dp = torch.from_numpy(parent).to(dev)
+        first = sv.tree_mask(dp)
+        torch.cuda.synchronize()
+        m = first["mask"].cpu().numpy()[0].view(np.uint32)
+        bits = ((m[:, :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(n, -1)[:, :n]
+        ok = np.array_equal(bits.astype(np.uint8), oracle.tree_mask(parent))
+        parity = {"checked": n, "exceptions": 0 if ok else n, "near_tie_sequences": 0, "ok": bool(ok)}
+        mask = torch.empty((1, n, W), dtype=torch.int32, device=dev)
+        L = sv.lib()
+
+        def call(i):
+            assert L.spec_tree_mask(1, n, dp.data_ptr(), 0, mask.data_ptr(), None,
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+        K, ms, ev_ms = _graph_time(torch, call, 8, args.steps, args.warmup)
+        alg = n * W * 4 + n * 4
+        metric, unit, value = "mask rows/sec + mask GB/s", "rows/s", n / (ms * 1e-3)
+        kernel, dtype, workload = "tree_mask_kernel", "u32", f"{cfg}: Cartesian K=4 top-8 tree, {n} nodes, {W} words per row"
+    if not parity["ok"]:
+        print(f"[bench] PARITY FAILED: {parity}", file=sys.stderr, flush=True)
+        sys.exit(1)
+    gbps = alg / (ev_ms * 1e-3) / 1e9
+    line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": dtype, "data": "synthetic (seeded generator; no dataset)",
+            "config": {"workload": workload, "graph": True},
+            "roofline": {"bound": "hbm", "kernel": kernel, "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "launch_us": ev_ms * 1e3, "algorithmic_bytes": alg},
+            "cpu_baseline": cpu, "parity": parity}
+    print(json.dumps(line), flush=True)
 
 
 def make_workload(cfg, mode, seed):
@@ -149,6 +304,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.config in STEP_CONFIGS:
+        bench_steps(args)
         return
     t_gen = time.time()
     w = make_workload(args.config, args.mode, args.seed)
