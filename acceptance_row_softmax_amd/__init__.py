@@ -65,6 +65,9 @@ def lib():
         L.spec_row_stats.argtypes = [i32, f32, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.spec_workspace_clear.restype = i32
         L.spec_workspace_clear.argtypes = [vp, sz, vp]
+        L.spec_verify_tree_typical.restype = i32
+        L.spec_verify_tree_typical.argtypes = [f32, ctypes.c_double, ctypes.c_double, i64, i64, i64, i32, vp,
+                                               i64, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
         L.spec_commit_linear.restype = i32
         L.spec_commit_linear.argtypes = [i64, i64, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
         L.spec_sample_workspace.restype = sz
@@ -82,7 +85,8 @@ def lib():
 EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_tree_workspace",
             "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
             "spec_workspace_clear", "spec_verify_status_string", "spec_commit_linear",
-            "spec_sample_workspace", "spec_sample", "spec_tree_mask", "spec_tree_build_greedy")
+            "spec_sample_workspace", "spec_sample", "spec_tree_mask", "spec_tree_build_greedy",
+            "spec_verify_tree_typical")
 
 
 def status_string(status: int) -> str:
@@ -216,18 +220,24 @@ def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic
 
 
 def verify_tree(parent, cand_tokens, logits, uniforms, max_depth: int, mode: str = "greedy",
-                temperature: float = 1.0, *, workspace=None, stream=None):
+                temperature: float = 1.0, *, epsilon: float = None, delta: float = None, workspace=None,
+                stream=None):
     """Verify B candidate trees of n_nodes (node 0 = root).
 
     parent [n_nodes] (shared) or [B][n_nodes] int32, cand_tokens [B][n_nodes] int32,
-    logits [B][n_nodes][V], uniforms [B][n_nodes] float32 (stochastic only).
+    logits [B][n_nodes][V], uniforms [B][n_nodes] float32 (stochastic and typical).
+    mode "greedy", "stochastic" (spec_verify_tree) or "typical" (typical acceptance,
+    spec_verify_tree_typical; epsilon and delta required).
     Returns accept_len [B], path_nodes [B][max_depth], out_tokens [B][max_depth+1],
     err_flags [B].
     """
     torch = _torch()
-    stoch = mode == "stochastic"
-    if mode not in ("stochastic", "greedy"):
-        raise ValueError("mode must be 'greedy' or 'stochastic'")
+    typical = mode == "typical"
+    stoch = mode == "stochastic" or typical
+    if mode not in ("stochastic", "greedy", "typical"):
+        raise ValueError("mode must be 'greedy', 'stochastic' or 'typical'")
+    if typical and (epsilon is None or delta is None):
+        raise ValueError("typical acceptance needs epsilon and delta")
     _need(logits, "logits")
     dev = logits.device
     B, N, V = logits.shape
@@ -259,6 +269,14 @@ def verify_tree(parent, cand_tokens, logits, uniforms, max_depth: int, mode: str
     nbytes = L.spec_verify_tree_workspace(B, N, V, dt, mcode)
     s = _stream(stream)
     ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    if typical:
+        st = L.spec_verify_tree_typical(float(temperature), float(epsilon), float(delta), B, N, V, dt,
+                                        _ptr(parent), stride, _ptr(cand_tokens), _ptr(logits),
+                                        _ptr(uniforms), int(max_depth), _ptr(acc),
+                                        _ptr(path) if max_depth > 0 else None, _ptr(out), _ptr(ef),
+                                        _ptr(ws), ws.numel(), s)
+        _check(st, "spec_verify_tree_typical")
+        return {"accept_len": acc, "path_nodes": path, "out_tokens": out, "err_flags": ef}
     st = L.spec_verify_tree(mcode, float(temperature), B, N, V, dt, _ptr(parent), stride,
                             _ptr(cand_tokens), _ptr(logits), _ptr(uniforms), int(max_depth),
                             _ptr(acc), _ptr(path) if max_depth > 0 else None, _ptr(out), _ptr(ef),

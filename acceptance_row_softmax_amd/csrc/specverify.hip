@@ -609,11 +609,21 @@ struct TreeParams {
   uint64_t* parts;      // [B*N][C] Partial records
   uint32_t* row_cnt;    // [B*N]
   int32_t* node_y;      // [B][N] token of each node (-1 unusable row, -2 a wait timed out)
+  struct NodeStat* nstat;   // [B][N] typical acceptance: each node's softmax statistics
   int64_t B, N, V, max_depth;
   int C, CP;
   float c0;
+  double eps, delta;    // typical acceptance: threshold min(eps, delta * exp(-H))
   uint32_t tag;
   int64_t n_stream;
+};
+
+// softmax(row / T) of a node: max M, Z = sum_v exp((x_v - M) / T), entropy H (nats).
+struct NodeStat {
+  double Z;
+  double H;
+  float M;
+  int ok;
 };
 
 // How the token of a node is chosen. Greedy: its argmax, while streaming.
@@ -621,8 +631,74 @@ struct TreeParams {
 // at every node (EAGER: the draws overlap the stream, best for few rows) or by
 // the walk at the accepted nodes only (LAZY: the only draws the result depends
 // on, best for many rows).
-enum TreeDraw { TD_ARGMAX = 0, TD_EAGER = 1, TD_LAZY = 2 };
+// TYPICAL: typical acceptance, the row's statistics with its entropy for the walk.
+enum TreeDraw { TD_ARGMAX = 0, TD_EAGER = 1, TD_LAZY = 2, TD_TYPICAL = 3 };
 constexpr int64_t TREE_EAGER_ROWS = 4096;   // at most this many rows (B * n_nodes) draw eagerly
+
+static_assert(RecWords<EntPartial>::N == PART_WORDS, "entropy partials use the partial records");
+
+// Typical acceptance, streaming wave of row q, chunk c: the chunk's entropy
+// partial; the row's last chunk combines them into the node's statistics.
+template <int DT>
+__device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const char* row, int64_t q, int64_t c) {
+  const int lane = lane_id();
+  Raw r;
+  load_chunk<DT>(row, P.V, c, r);
+  const EntPartial p = chunk_reduce_ent<DT>(r, P.c0);
+  uint32_t old = 0;
+  if (lane == 0) {
+    put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
+    old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
+  }
+  if (bcast(old) + 1 != (uint32_t)P.C) return;
+  if (lane == 0) counter_reset(P.row_cnt + q * CSTRIDE);
+  // lane l holds chunks l + 64 t
+  float m[MAX_ROUNDS];
+  double sv[MAX_ROUNDS], s1[MAX_ROUNDS];
+  bool got = true;
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    EntPartial e;
+    e.m = -INFINITY;
+    e.s = e.s1 = 0.0;
+    const int cc = t * WAVE + lane;
+    if (cc < P.C) {
+      uint64_t* rec = P.parts + (q * P.C + cc) * PART_WORDS;
+      got = get_rec(rec, e, P.tag) && got;
+      clear_rec<EntPartial>(rec);
+    }
+    m[t] = e.m;
+    sv[t] = e.s;
+    s1[t] = e.s1;
+    M = fmaxf(M, e.m);
+  }
+  M = wave_max(M);
+  const double Mc0 = (double)M * (double)P.c0;
+  double Z = 0.0, S1 = 0.0;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    if (m[t] == -INFINITY) continue;
+    // chunk weights are relative to fl32(m*c0): bring them to the row max
+    const double f = pow2_neg((double)chunk_mc0(m[t], P.c0) - Mc0);
+    Z += sv[t] * f;
+    S1 += (s1[t] + ((double)m[t] - (double)M) * sv[t]) * f;
+  }
+  Z = wave_sum(Z);
+  S1 = wave_sum(S1);
+  const bool all = __ballot(!got) == 0ull;
+  NodeStat st;
+  st.M = M;
+  st.Z = Z;
+  // H = ln Z - E[(x - M) / T], with 1/T = c0 ln 2
+  st.H = log(Z) - (S1 / Z) * ((double)P.c0 * LN2);
+  const bool usable = M > -INFINITY && __builtin_isfinite(Z) && Z > 0.0 && __builtin_isfinite(st.H);
+  st.ok = usable ? 1 : 0;
+  if (lane == 0) {
+    P.nstat[q] = st;
+    P.node_y[q] = !all ? -2 : (usable ? 0 : -1);
+  }
+}
 
 template <int DT, int TD>
 __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
@@ -636,6 +712,10 @@ __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
   if (c32 >= C) return;   // padding wave
   const int64_t q = q32, c = c32;
   const char* row = P.logits + (q * P.V) * E;
+  if constexpr (TD == TD_TYPICAL) {
+    tree_typical_stream<DT>(P, row, q, c);
+    return;
+  }
   const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c, P.c0);
   uint32_t old = 0;
   if (lane_id() == 0) {
@@ -725,23 +805,31 @@ __device__ __forceinline__ int walk_draw(const char* row, int64_t V, int C, floa
   return y;
 }
 
+// Walk modes: the node tokens are known (greedy, or drawn while streaming); LAZY
+// draws the tokens of the accepted nodes level by level; TYPICAL accepts a node
+// when its candidate's probability under its parent's distribution clears the
+// parent's threshold, and draws only the final token.
+enum WalkMode { WM_KNOWN = 0, WM_LAZY = 1, WM_TYPICAL = 2 };
+
 // Accepted-path search of tree b (one workgroup of NT threads). LDS: parent
-// (int16) and one state byte per node. With the node tokens known (greedy, or
-// drawn while streaming) a node is accepted when every node on its path matches
-// its parent's token. LAZY: the walk goes level by level from the root, drawing
+// (int16) and one state byte per node. WM_KNOWN / WM_TYPICAL: a node is accepted
+// when every node on its path matches (its token equals its parent's, or its
+// candidate passes the parent's threshold); the deepest such node, lowest index on
+// ties, ends the path. WM_LAZY: the walk goes level by level from the root, drawing
 // the token of each accepted node and accepting the children whose candidate
 // equals it.
-template <int DT, bool LAZY, int NT>
+template <int DT, int WM, int NT>
 __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
   constexpr int E = DTraits<DT>::E;
+  constexpr bool DRAWS = WM != WM_KNOWN;
   extern __shared__ unsigned char smem[];
   __shared__ int red_sh[NT / WAVE];
-  __shared__ float pm_sh[LAZY ? MAX_CHUNKS : 1];
-  __shared__ double ps_sh[LAZY ? MAX_CHUNKS : 1];
+  __shared__ float pm_sh[DRAWS ? MAX_CHUNKS : 1];
+  __shared__ double ps_sh[DRAWS ? MAX_CHUNKS : 1];
   const int64_t b = blockIdx.x;
   const int64_t N = P.N;
   int16_t* par_s = reinterpret_cast<int16_t*>(smem);
-  unsigned char* st_s = smem + 2 * N;   // tokens known: match flag; LAZY: 0 / 1 accepted / 2 drawn
+  unsigned char* st_s = smem + 2 * N;   // match flag; WM_LAZY: 0 / 1 accepted / 2 drawn
   const int32_t* par = P.parent + b * P.parent_stride;
   const int32_t* cand = P.cand + b * N;
   int32_t* ny = P.node_y + b * N;
@@ -750,6 +838,9 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
   // validation (and the match flags), WALK_BATCH nodes per thread at a time
   for (int64_t base = 0; base < N; base += (int64_t)NT * WALK_BATCH) {
     int yv[WALK_BATCH], pv[WALK_BATCH], cv[WALK_BATCH], yp[WALK_BATCH];
+    float xl[WALK_BATCH], nm[WALK_BATCH];
+    double nz[WALK_BATCH], nh[WALK_BATCH];
+    int nok[WALK_BATCH];
 #pragma unroll
     for (int j = 0; j < WALK_BATCH; ++j) {
       const int64_t i = base + (int64_t)j * NT + tid;
@@ -767,7 +858,19 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
       const int64_t i = base + (int64_t)j * NT + tid;
       const bool ok = i > 0 && i < N && pv[j] >= 0 && pv[j] < i;
       yp[j] = -1;
-      if (!LAZY && ok) yp[j] = ny[pv[j]];
+      xl[j] = nm[j] = 0.0f;
+      nz[j] = nh[j] = 0.0;
+      nok[j] = 0;
+      if (WM == WM_KNOWN && ok) yp[j] = ny[pv[j]];
+      if (WM == WM_TYPICAL && ok && cv[j] >= 0 && cv[j] < P.V) {
+        // the candidate's logit in its parent's row, and the parent's statistics
+        const NodeStat* ps = P.nstat + b * N + pv[j];
+        nz[j] = ps->Z;
+        nh[j] = ps->H;
+        nm[j] = ps->M;
+        nok[j] = ps->ok;
+        xl[j] = load_elem<DT>(P.logits + ((b * N + pv[j]) * P.V) * E, cv[j]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < WALK_BATCH; ++j) {
@@ -781,9 +884,15 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
       unsigned char m = 0;
       if (i > 0) {
         if (cv[j] < 0 || cv[j] >= P.V) err |= SV_ERR_TOKEN;
-        if (!LAZY && !bad) m = (cv[j] == yp[j]) ? 1 : 0;
+        if (WM == WM_KNOWN && !bad) m = (cv[j] == yp[j]) ? 1 : 0;
+        if (WM == WM_TYPICAL && !bad && nok[j]) {
+          // p_parent(cand) = exp((x - M) / T) / Z against min(eps, delta * exp(-H))
+          const double prob = exp2(((double)xl[j] - (double)nm[j]) * (double)P.c0) / nz[j];
+          const double dt = P.delta * exp(-nh[j]);
+          m = prob > (P.eps < dt ? P.eps : dt) ? 1 : 0;
+        }
       }
-      st_s[i] = LAZY ? (unsigned char)(i == 0 ? 1 : 0) : m;
+      st_s[i] = WM == WM_LAZY ? (unsigned char)(i == 0 ? 1 : 0) : m;
     }
   }
   int all_err = block_or(err);
@@ -812,14 +921,14 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
           acc[j] = 0;
           continue;
         }
-        if (!LAZY) acc[j] &= st_s[cur[j]];
+        if (WM != WM_LAZY) acc[j] &= st_s[cur[j]];
         cur[j] = par_s[cur[j]];
         ++d[j];
         moving = 1;
       }
       if (!moving) break;
     }
-    if (!LAZY) {
+    if (WM != WM_LAZY) {
 #pragma unroll
       for (int j = 0; j < WALK_BATCH; ++j) {
         const int64_t i = base + (int64_t)j * NT + tid;
@@ -842,7 +951,7 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
     }
   } else {
     int L = 0, best = 0;
-    if constexpr (LAZY) {
+    if constexpr (WM == WM_LAZY) {
       for (int level = 0;; ++level) {
         // draw the accepted nodes of this level, lowest index first
         int first = -1;
@@ -881,6 +990,13 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
       const int r = block_max_int<NT>(best_key, red_sh);
       L = r >> 15;
       best = 32767 - (r & 32767);
+      if constexpr (WM == WM_TYPICAL) {
+        // the final token: a draw from the last node's distribution
+        const char* row = P.logits + ((b * N + best) * P.V) * E;
+        const int y = walk_draw<DT, NT>(row, P.V, P.C, P.c0, P.uniforms[b * N + best], pm_sh, ps_sh);
+        if (tid == 0) ny[best] = y;
+        __syncthreads();
+      }
     }
     for (int64_t j = L + tid; j < P.max_depth; j += NT) path[j] = -1;
     for (int64_t j = L + 1 + tid; j <= P.max_depth; j += NT) out[j] = -1;
@@ -896,9 +1012,18 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
       if (P.err_flags) P.err_flags[b] = 0;
     }
   }
-  // leave the node tokens zero, as the workspace was
+  // leave the node tokens (and statistics) zero, as the workspace was
   __syncthreads();
-  for (int64_t i = tid; i < N; i += NT) ny[i] = 0;
+  for (int64_t i = tid; i < N; i += NT) {
+    ny[i] = 0;
+    if (WM == WM_TYPICAL) {
+      NodeStat z;
+      z.Z = z.H = 0.0;
+      z.M = 0.0f;
+      z.ok = 0;
+      P.nstat[b * N + i] = z;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ row statistics
@@ -970,7 +1095,8 @@ Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode)
 
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
   const int64_t C = chunks_per_row(V, dt);
-  return make_layout({(size_t)(B * N * C) * PART_WORDS * 8, (size_t)(B * N * CSTRIDE) * 4, (size_t)(B * N) * 4});
+  return make_layout({(size_t)(B * N * C) * PART_WORDS * 8, (size_t)(B * N * CSTRIDE) * 4, (size_t)(B * N) * 4,
+                      (size_t)(B * N) * sizeof(NodeStat)});
 }
 
 Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
@@ -1002,10 +1128,20 @@ struct TreeLauncher {
     }
     if (launch_status() != SV_OK) return SV_EHIP;
     if (STOCH && !eager) {
-      hipLaunchKernelGGL((tree_walk_kernel<DT, true, 512>), trees, dim3(512), smem, s, P);
+      hipLaunchKernelGGL((tree_walk_kernel<DT, WM_LAZY, 512>), trees, dim3(512), smem, s, P);
     } else {
-      hipLaunchKernelGGL((tree_walk_kernel<DT, false, 1024>), trees, dim3(1024), smem, s, P);
+      hipLaunchKernelGGL((tree_walk_kernel<DT, WM_KNOWN, 1024>), trees, dim3(1024), smem, s, P);
     }
+    return launch_status();
+  }
+};
+
+template <int DT, bool UNUSED>
+struct TypicalLauncher {
+  static sv_status run(const TreeParams& P, size_t smem, hipStream_t s) {
+    hipLaunchKernelGGL((tree_stream_kernel<DT, TD_TYPICAL>), dim3(blocks_for(P.n_stream)), dim3(BLOCK), 0, s, P);
+    if (launch_status() != SV_OK) return SV_EHIP;
+    hipLaunchKernelGGL((tree_walk_kernel<DT, WM_TYPICAL, 512>), dim3((unsigned)P.B), dim3(512), smem, s, P);
     return launch_status();
   }
 };
@@ -1017,6 +1153,50 @@ struct RowStatsLauncher {
     return launch_status();
   }
 };
+
+// Checks and fills the parameters shared by the tree entry points (B == 0: SV_OK
+// with nothing to launch).
+sv_status tree_setup(TreeParams& P, size_t& smem, bool stoch, float temperature, int64_t B, int64_t n_nodes,
+                     int64_t V, sv_dtype dtype, const int32_t* parent, int64_t parent_batch_stride,
+                     const int32_t* cand_tokens, const void* target_logits, const float* uniforms,
+                     int64_t max_depth, int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
+                     int32_t* err_flags, void* workspace, size_t workspace_bytes) {
+  if (B < 0 || n_nodes < 1 || V < 1 || max_depth < 0 || parent_batch_stride < 0) return SV_EINVAL;
+  if (n_nodes > SV_MAX_TREE_NODES || !shape_ok(V, dtype)) return SV_ELIMIT;
+  if (B == 0) return SV_OK;
+  if (!parent || !cand_tokens || !target_logits || !accept_len || !out_tokens) return SV_EINVAL;
+  if (max_depth > 0 && !path_nodes) return SV_EINVAL;
+  if (stoch && (!temperature_ok(temperature) || !uniforms)) return SV_EINVAL;
+  const Layout lay = tree_layout(B, n_nodes, V, dtype);
+  if (!ws_ok(workspace, workspace_bytes, lay.total)) return SV_EWORKSPACE;
+  P.logits = static_cast<const char*>(target_logits);
+  P.parent = parent;
+  P.parent_stride = parent_batch_stride;
+  P.cand = cand_tokens;
+  P.uniforms = uniforms;
+  P.accept_len = accept_len;
+  P.path_nodes = path_nodes;
+  P.out_tokens = out_tokens;
+  P.err_flags = err_flags;
+  char* ws = static_cast<char*>(workspace);
+  P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
+  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[1]);
+  P.node_y = reinterpret_cast<int32_t*>(ws + lay.off[2]);
+  P.nstat = reinterpret_cast<NodeStat*>(ws + lay.off[3]);
+  P.B = B;
+  P.N = n_nodes;
+  P.V = V;
+  P.max_depth = max_depth;
+  P.C = (int)chunks_per_row(V, dtype);
+  P.CP = (P.C + WPB - 1) / WPB * WPB;
+  P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
+  P.n_stream = B * n_nodes * P.CP;
+  if (P.n_stream > MAX_WAVES || B > 0x7fffffffLL) return SV_ELIMIT;
+  P.tag = next_tag();
+  // LDS of the path search: parent (2 B) + match flag (1 B) per node
+  smem = (size_t)((3 * n_nodes + 15) & ~(int64_t)15);
+  return SV_OK;
+}
 
 }  // namespace
 
@@ -1107,42 +1287,33 @@ sv_status spec_verify_tree(sv_mode mode, float temperature, int64_t B, int64_t n
   if (!dtype_ok(dtype)) return SV_EDTYPE;
   if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
   const bool stoch = (mode == SV_STOCHASTIC);
-  if (B < 0 || n_nodes < 1 || V < 1 || max_depth < 0 || parent_batch_stride < 0) return SV_EINVAL;
-  if (n_nodes > SV_MAX_TREE_NODES || !shape_ok(V, dtype)) return SV_ELIMIT;
-  if (B == 0) return SV_OK;
-  if (!parent || !cand_tokens || !target_logits || !accept_len || !out_tokens) return SV_EINVAL;
-  if (max_depth > 0 && !path_nodes) return SV_EINVAL;
-  if (stoch && (!temperature_ok(temperature) || !uniforms)) return SV_EINVAL;
-  const Layout lay = tree_layout(B, n_nodes, V, dtype);
-  if (!ws_ok(workspace, workspace_bytes, lay.total)) return SV_EWORKSPACE;
-
   TreeParams P{};
-  P.logits = static_cast<const char*>(target_logits);
-  P.parent = parent;
-  P.parent_stride = parent_batch_stride;
-  P.cand = cand_tokens;
-  P.uniforms = uniforms;
-  P.accept_len = accept_len;
-  P.path_nodes = path_nodes;
-  P.out_tokens = out_tokens;
-  P.err_flags = err_flags;
-  char* ws = static_cast<char*>(workspace);
-  P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
-  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[1]);
-  P.node_y = reinterpret_cast<int32_t*>(ws + lay.off[2]);
-  P.B = B;
-  P.N = n_nodes;
-  P.V = V;
-  P.max_depth = max_depth;
-  P.C = (int)chunks_per_row(V, dtype);
-  P.CP = (P.C + WPB - 1) / WPB * WPB;
-  P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  P.n_stream = B * n_nodes * P.CP;
-  if (P.n_stream > MAX_WAVES || B > 0x7fffffffLL) return SV_ELIMIT;
-  P.tag = next_tag();
-  // LDS of the path search: parent (2 B) + match flag (1 B) per node
-  const size_t smem = (size_t)((3 * n_nodes + 15) & ~(int64_t)15);
+  size_t smem = 0;
+  const sv_status st = tree_setup(P, smem, stoch, temperature, B, n_nodes, V, dtype, parent, parent_batch_stride,
+                                  cand_tokens, target_logits, uniforms, max_depth, accept_len, path_nodes,
+                                  out_tokens, err_flags, workspace, workspace_bytes);
+  if (st != SV_OK || B == 0) return st;
   return dispatch<TreeLauncher>(dtype, stoch, P, smem, reinterpret_cast<hipStream_t>(stream));
+}
+
+sv_status spec_verify_tree_typical(float temperature, double epsilon, double delta, int64_t B, int64_t n_nodes,
+                                   int64_t V, sv_dtype dtype, const int32_t* parent,
+                                   int64_t parent_batch_stride, const int32_t* cand_tokens,
+                                   const void* target_logits, const float* uniforms, int64_t max_depth,
+                                   int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
+                                   int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                                   sv_stream_t stream) {
+  if (!dtype_ok(dtype)) return SV_EDTYPE;
+  if (!(std::isfinite(epsilon) && epsilon >= 0.0 && std::isfinite(delta) && delta >= 0.0)) return SV_EINVAL;
+  TreeParams P{};
+  size_t smem = 0;
+  const sv_status st = tree_setup(P, smem, true, temperature, B, n_nodes, V, dtype, parent, parent_batch_stride,
+                                  cand_tokens, target_logits, uniforms, max_depth, accept_len, path_nodes,
+                                  out_tokens, err_flags, workspace, workspace_bytes);
+  if (st != SV_OK || B == 0) return st;
+  P.eps = epsilon;
+  P.delta = delta;
+  return dispatch<TypicalLauncher>(dtype, false, P, smem, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t spec_row_stats_workspace(int64_t rows, int64_t V, sv_dtype dtype) {

@@ -374,6 +374,48 @@ __device__ __forceinline__ Partial chunk_reduce(const Chunk& k, const Raw& r, fl
   return p;
 }
 
+// Partial of a chunk for the entropy of softmax(row / T): the max m, the weight
+// sum s relative to fl32(m*c0), and the first moment s1 = sum_v w_v (x_v - m).
+struct EntPartial {
+  float m;
+  int pad;
+  double s;
+  double s1;
+};
+
+template <int DT>
+__device__ __forceinline__ EntPartial chunk_reduce_ent(const Raw& r, float c0) {
+  constexpr int W = DTraits<DT>::W;
+  float best = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < CU; ++j) {
+    float x[W];
+    unit_values<DT>(r, j, x);
+    best = fmaxf(best, max_of<W>(x));
+  }
+  EntPartial p;
+  p.m = wave_max(best);
+  p.pad = 0;
+  const float mc0 = chunk_mc0(p.m, c0);
+  double s = 0.0, s1 = 0.0;
+#pragma unroll
+  for (int j = 0; j < CU; ++j) {
+    float x[W], w[W], wx[W];
+    unit_values<DT>(r, j, x);
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      w[e] = softmax_weight(x[e], c0, mc0);
+      // -inf entries have weight 0 and add nothing to the moment
+      wx[e] = w[e] > 0.0f ? w[e] * (x[e] - p.m) : 0.0f;
+    }
+    s += (double)pairwise_sum<W>(w);
+    s1 += (double)pairwise_sum<W>(wx);
+  }
+  p.s = wave_sum(s);
+  p.s1 = wave_sum(s1);
+  return p;
+}
+
 // Loads chunk c of a row and reduces it.
 template <int DT, bool SUM, bool ARG>
 __device__ __forceinline__ Partial chunk_partial(const char* row, int64_t V, int64_t c, float c0, int64_t x = -1) {

@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--config", default="c2_linear",
                     choices=["c1_tiny", "c2_linear", "c3_mtp", "c4_medusa_sparse", "c5_medusa_full",
                              *STEP_CONFIGS])
-    ap.add_argument("--mode", default=None, help="greedy | stochastic (default: the config's own)")
+    ap.add_argument("--mode", default=None,
+                    help="greedy | stochastic | typical (trees) (default: the config's own)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a HIP graph")
@@ -258,11 +259,20 @@ def bench_steps(args):
     print(json.dumps(line), flush=True)
 
 
+# Typical acceptance (trees, --mode typical): the rule's constants are the
+# caller's; these are the example setting the benchmark uses.
+TYPICAL_EPS, TYPICAL_DELTA = 0.09, 0.3
+
+
 def make_workload(cfg, mode, seed):
+    import dataclasses
     import gen
     defaults = {"c1_tiny": "stochastic", "c2_linear": "stochastic", "c3_mtp": "stochastic",
                 "c4_medusa_sparse": "greedy", "c5_medusa_full": "greedy"}
     mode = mode or defaults[cfg]
+    if mode == "typical":
+        # the stochastic workload's inputs (logits, candidates, uniforms), judged by typical acceptance
+        return dataclasses.replace(gen.CONFIGS[cfg](seed, "stochastic"), mode="typical")
     return gen.CONFIGS[cfg](seed, mode)
 
 
@@ -272,8 +282,13 @@ def describe(w):
     if hasattr(w, "k"):
         return (f"{w.name}: linear draft verification, B={w.B} k={w.k} V={w.V} {dt} logits, "
                 f"{w.mode}" + (f" T={w.temperature}" if w.mode == "stochastic" else ""))
+    extra = ""
+    if w.mode == "stochastic":
+        extra = f" T={w.temperature}"
+    elif w.mode == "typical":
+        extra = f" acceptance T={w.temperature} eps={TYPICAL_EPS} delta={TYPICAL_DELTA}"
     return (f"{w.name}: candidate-tree verification, B={w.B} trees of {w.n_nodes} nodes, V={w.V} "
-            f"{dt} logits, {w.mode}" + (f" T={w.temperature}" if w.mode == "stochastic" else ""))
+            f"{dt} logits, {w.mode}" + extra)
 
 
 def positions(w):
@@ -311,7 +326,7 @@ def main():
     t_gen = time.time()
     w = make_workload(args.config, args.mode, args.seed)
     linear = hasattr(w, "k")
-    stoch = w.mode == "stochastic"
+    stoch = w.mode in ("stochastic", "typical")
     alg_bytes = w.algorithmic_bytes()
     print(f"[bench] {describe(w)}; algorithmic bytes/step {alg_bytes} "
           f"(generated in {time.time() - t_gen:.1f}s)", file=sys.stderr, flush=True)
@@ -347,6 +362,9 @@ def main():
                 return outs[i]
             return sv.verify_linear(s["t"], s["d"], s["x"], s["u"], mode=w.mode,
                                     temperature=w.temperature, out=outs[i])
+        if w.mode == "typical":
+            return sv.verify_tree(s["par"], s["cand"], s["lg"], s["u"], w.max_depth, mode="typical",
+                                  temperature=w.temperature, epsilon=TYPICAL_EPS, delta=TYPICAL_DELTA)
         r = sv.verify_tree(s["par"], s["cand"], s["lg"], s["u"], w.max_depth, mode=w.mode,
                            temperature=w.temperature)
         return r
@@ -363,8 +381,12 @@ def main():
         differ = (g_acc != o["accept_len"]) | np.any(g_out != o["out_tokens"], axis=1)
     else:
         sample = list(range(min(w.B, 2 if w.n_nodes > 1000 else w.B)))
-        o = oracle.verify_tree(w.mode, w.temperature, w.parent, w.cand[sample], w.logits[sample],
-                               w.uniforms[sample], w.V, w.dtype, w.max_depth)
+        if w.mode == "typical":
+            o = oracle.verify_tree_typical(w.temperature, TYPICAL_EPS, TYPICAL_DELTA, w.parent, w.cand[sample],
+                                           w.logits[sample], w.uniforms[sample], w.V, w.dtype, w.max_depth)
+        else:
+            o = oracle.verify_tree(w.mode, w.temperature, w.parent, w.cand[sample], w.logits[sample],
+                                   w.uniforms[sample], w.V, w.dtype, w.max_depth)
         g_acc = first["accept_len"].cpu().numpy()[sample]
         g_out = first["out_tokens"].cpu().numpy()[sample]
         differ = (g_acc != o["accept_len"]) | np.any(g_out != o["out_tokens"], axis=1)
@@ -464,6 +486,11 @@ def main():
                                      w.draft_tokens, w.uniforms, w.V, w.dtype)
                 per = w.B * w.k
                 what = f"the full batch ({w.B} sequences)"
+            elif w.mode == "typical":
+                oracle.verify_tree_typical(w.temperature, TYPICAL_EPS, TYPICAL_DELTA, w.parent, w.cand[:1],
+                                           w.logits[:1], w.uniforms[:1], w.V, w.dtype, w.max_depth)
+                per = w.n_nodes - 1
+                what = "one tree of the batch"
             else:
                 oracle.verify_tree(w.mode, w.temperature, w.parent, w.cand[:1], w.logits[:1],
                                    w.uniforms[:1], w.V, w.dtype, w.max_depth)

@@ -169,6 +169,24 @@ sv_status spec_verify_tree(sv_mode mode, float temperature, int64_t B, int64_t n
                            int32_t* path_nodes, int32_t* out_tokens, int32_t* err_flags,
                            void* workspace, size_t workspace_bytes, sv_stream_t stream);
 
+/* ---------------------------------------------------------------- typical acceptance (trees)
+ * Named by the workload description of the full Medusa tree, NOT defined on the source
+ * pages: the rule below is this library's reading, and its constants are the caller's.
+ * Same arguments and outputs as spec_verify_tree (stochastic, at temperature T, same
+ * workspace size), plus epsilon, delta >= 0. With p_n = softmax(row n / T) and H_n its
+ * entropy in nats, node i passes iff p_parent(i)(cand_i) > min(epsilon, delta * exp(-H_parent(i)));
+ * node i is accepted iff it passes and its parent is accepted (the root always is).
+ * The deepest accepted node (lowest index on ties) ends the path; the final token is the
+ * inverse-CDF draw from p_last with u[b][last]. Two kernel launches.
+ */
+sv_status spec_verify_tree_typical(float temperature, double epsilon, double delta, int64_t B,
+                                   int64_t n_nodes, int64_t V, sv_dtype dtype, const int32_t* parent,
+                                   int64_t parent_batch_stride, const int32_t* cand_tokens,
+                                   const void* target_logits, const float* uniforms, int64_t max_depth,
+                                   int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
+                                   int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                                   sv_stream_t stream);
+
 /* ---------------------------------------------------------------- row statistics
  * The streaming row softmax the verifier is built on, exposed for diagnostics:
  * for rows x[rows][V], row_max = max_v x_v, row_lse = log sum_v exp(x_v / T),

@@ -67,6 +67,9 @@ def lib():
         L.orc_tree_mask.argtypes = [i64, vp, vp]
         L.orc_tree_build_greedy.restype = i64
         L.orc_tree_build_greedy.argtypes = [i64, i64, vp, i64, vp, vp, vp, vp]
+        L.orc_verify_tree_typical.restype = i32
+        L.orc_verify_tree_typical.argtypes = [dbl, dbl, dbl, i64, i64, i64, i32, vp, i64, vp, vp, vp, i64,
+                                              dbl, vp, vp, vp, vp, vp, vp]
         L.orc_set_mutation.restype = None
         L.orc_set_mutation.argtypes = [i32]
         _lib = L
@@ -224,4 +227,27 @@ def tree_build_greedy(acc, budget: int):
     if n < 0:
         raise ValueError("orc_tree_build_greedy: bad arguments")
     return {"parent": par[:n].copy(), "depth": dep[:n].copy(), "rank": rk[:n].copy(), "expected_len": E.value}
+
+
+def verify_tree_typical(T: float, epsilon: float, delta: float, parent, cand, logits, uniforms, V: int,
+                        dtype: int, max_depth: int, tie_eps: float = TIE_EPS):
+    logits = np.ascontiguousarray(logits)
+    B, n = logits.shape[0], logits.shape[1]
+    parent = np.ascontiguousarray(np.asarray(parent, np.int32))
+    stride = 0 if parent.ndim == 1 else n
+    cand = np.ascontiguousarray(np.asarray(cand, np.int32).reshape(B, n))
+    u = np.ascontiguousarray(np.asarray(uniforms, np.float32).reshape(B, n))
+    acc = np.empty(B, np.int32)
+    path = np.empty((B, max_depth), np.int32)
+    out = np.empty((B, max_depth + 1), np.int32)
+    err = np.empty(B, np.int32)
+    nt = np.empty(B, np.int32)
+    ne = np.empty(B, np.int32)
+    rc = lib().orc_verify_tree_typical(T, epsilon, delta, B, n, V, dtype, _p(parent), stride, _p(cand),
+                                       _p(logits), _p(u), max_depth, tie_eps, _p(acc), _p(path), _p(out),
+                                       _p(err), _p(nt), _p(ne))
+    if rc:
+        raise ValueError("orc_verify_tree_typical: bad arguments")
+    return {"accept_len": acc, "path_nodes": path, "out_tokens": out, "err_flags": err,
+            "near_tie": nt, "n_eval": ne}
 

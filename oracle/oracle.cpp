@@ -6,6 +6,7 @@
 // fp32 as stored). Citations and the rule set are in oracle.h.
 #include "oracle.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -263,6 +264,87 @@ int64_t orc_tree_build_greedy(int64_t K, int64_t S, const double* acc, int64_t b
   }
   if (expected_len) *expected_len = E;
   return n;
+}
+
+int orc_verify_tree_typical(double T, double epsilon, double delta, int64_t B, int64_t n_nodes,
+                            int64_t V, int dtype, const int32_t* parent, int64_t parent_stride,
+                            const int32_t* cand, const void* logits, const float* uniforms,
+                            int64_t max_depth, double tie_eps, int32_t* accept_len,
+                            int32_t* path_nodes, int32_t* out_tokens, int32_t* err_flags,
+                            int32_t* near_tie, int32_t* n_eval) {
+  if (B < 0 || n_nodes < 1 || V < 1 || !parent || !cand || !logits || !uniforms || max_depth < 0 ||
+      !accept_len || !path_nodes || !out_tokens || !(T > 0))
+    return -1;
+  for (int64_t b = 0; b < B; ++b) {
+    const int32_t* par = parent + b * parent_stride;
+    const int32_t* cd = cand + b * n_nodes;
+    int32_t* pn = path_nodes + b * max_depth;
+    int32_t* out = out_tokens + b * (max_depth + 1);
+    for (int64_t j = 0; j < max_depth; ++j) pn[j] = -1;
+    for (int64_t j = 0; j <= max_depth; ++j) out[j] = -1;
+    int32_t err = 0, nt = 0, ne = 0;
+    std::vector<int64_t> depth((size_t)n_nodes, 0);
+    if (par[0] != -1) err |= 4;
+    for (int64_t i = 1; i < n_nodes && !(err & 4); ++i) {
+      if (par[i] < 0 || par[i] >= i) { err |= 4; break; }
+      depth[(size_t)i] = depth[(size_t)par[i]] + 1;
+      if (depth[(size_t)i] > max_depth) err |= 4;
+    }
+    for (int64_t i = 1; i < n_nodes; ++i)
+      if (cd[i] < 0 || cd[i] >= V) err |= 1;
+    // every node's distribution and its entropy
+    std::vector<Softmax> sm((size_t)n_nodes);
+    std::vector<double> H((size_t)n_nodes, 0.0);
+    for (int64_t n = 0; n < n_nodes; ++n) {
+      sm[(size_t)n] = softmax_of(load_row(dtype, logits, b * n_nodes + n, V), T);
+      if (!sm[(size_t)n].ok) { err |= 2; continue; }
+      double h = 0;
+      for (int64_t v = 0; v < V; ++v) {
+        const double pv = sm[(size_t)n].prob(v);
+        if (pv > 0) h -= pv * std::log(pv);
+      }
+      H[(size_t)n] = h;
+    }
+    if (!err) {
+      std::vector<char> acc((size_t)n_nodes, 0), close((size_t)n_nodes, 0);
+      acc[0] = 1;
+      for (int64_t i = 1; i < n_nodes; ++i) {
+        const int64_t p = par[i];
+        const double prob = sm[(size_t)p].prob(cd[i]);
+        const double tau = std::min(epsilon, delta * std::exp(-H[(size_t)p]));
+        close[(size_t)i] = std::fabs(prob - tau) <= tie_eps * tau;
+        acc[(size_t)i] = (prob > tau) && acc[(size_t)p];
+      }
+      int64_t best = 0;
+      for (int64_t i = 1; i < n_nodes; ++i)
+        if (acc[(size_t)i] && depth[(size_t)i] > depth[(size_t)best]) best = i;
+      const int64_t L = depth[(size_t)best];
+      accept_len[b] = (int32_t)L;
+      int64_t node = best;
+      for (int64_t j = L - 1; j >= 0; --j) {
+        pn[j] = (int32_t)node;
+        out[j] = cd[node];
+        node = par[node];
+      }
+      // the result depends on the test of every child of an accepted node
+      for (int64_t i = 1; i < n_nodes; ++i)
+        if (acc[(size_t)par[i]]) {
+          ++ne;
+          if (close[(size_t)i]) nt = 1;
+        }
+      const double u = (double)uniforms[b * n_nodes + best];
+      const Draw d = invcdf(sm[(size_t)best].z, u);
+      out[L] = (int32_t)d.y;
+      ++ne;
+      if (near_draw(u, d, tie_eps)) nt = 1;
+    } else {
+      accept_len[b] = -1;
+    }
+    if (err_flags) err_flags[b] = err;
+    if (near_tie) near_tie[b] = nt;
+    if (n_eval) n_eval[b] = ne;
+  }
+  return 0;
 }
 
 void orc_set_mutation(int which) { g_mutation = which; }

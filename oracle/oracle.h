@@ -119,6 +119,23 @@ int orc_tree_mask(int64_t n_nodes, const int32_t* parent, uint8_t* dense);
 int64_t orc_tree_build_greedy(int64_t K, int64_t S, const double* acc, int64_t budget,
                               int32_t* parent, int32_t* depth, int32_t* rank, double* expected_len);
 
+/* Typical acceptance on candidate trees (named by the workload description, NOT
+ * defined on the pages: a reading, parity unpinned by the pages). With p_n =
+ * softmax(row n / T) and H_n = -sum_v p_n(v) ln p_n(v) (its entropy, nats), node
+ * i >= 1 passes iff p_parent(cand_i) > min(epsilon, delta * exp(-H_parent)); it is
+ * accepted iff it passes and its parent is accepted (the root always is); the
+ * deepest accepted node (lowest index on ties) ends the path, and the final token is
+ * invcdf(p_best, u[b][best]). near_tie[b]: a decisive pass test (one of a child of an
+ * accepted node) within tie_eps (relative) of its threshold, or the final draw within
+ * tie_eps of a bin edge. n_eval[b]: decisive tests plus the final draw. Errors as for
+ * orc_verify_tree. */
+int orc_verify_tree_typical(double T, double epsilon, double delta, int64_t B, int64_t n_nodes,
+                            int64_t V, int dtype, const int32_t* parent, int64_t parent_stride,
+                            const int32_t* cand, const void* logits, const float* uniforms,
+                            int64_t max_depth, double tie_eps, int32_t* accept_len,
+                            int32_t* path_nodes, int32_t* out_tokens, int32_t* err_flags,
+                            int32_t* near_tie, int32_t* n_eval);
+
 /* Planted-mistake switch for negative-control tests only (0 = off). */
 void orc_set_mutation(int which);
 
