@@ -681,17 +681,18 @@ __device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const c
     if (m[t] == -INFINITY) continue;
     // chunk weights are relative to fl32(m*c0): bring them to the row max
     const double f = pow2_neg((double)chunk_mc0(m[t], P.c0) - Mc0);
+    // exponents relative to the row: t_v + (fl32(m*c0) - M*c0)
     Z += sv[t] * f;
-    S1 += (s1[t] + ((double)m[t] - (double)M) * sv[t]) * f;
+    S1 += (s1[t] + ((double)chunk_mc0(m[t], P.c0) - Mc0) * sv[t]) * f;
   }
   Z = wave_sum(Z);
-  S1 = wave_sum(S1);
+  S1 = wave_sum(S1);   // sum_v w_v (x_v - M) c0
   const bool all = __ballot(!got) == 0ull;
   NodeStat st;
   st.M = M;
   st.Z = Z;
-  // H = ln Z - E[(x - M) / T], with 1/T = c0 ln 2
-  st.H = log(Z) - (S1 / Z) * ((double)P.c0 * LN2);
+  // H = ln Z - E[(x - M) / T], with (x - M) / T = (x - M) c0 ln 2
+  st.H = log(Z) - (S1 / Z) * LN2;
   const bool usable = M > -INFINITY && __builtin_isfinite(Z) && Z > 0.0 && __builtin_isfinite(st.H);
   st.ok = usable ? 1 : 0;
   if (lane == 0) {

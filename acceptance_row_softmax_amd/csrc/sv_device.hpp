@@ -375,7 +375,8 @@ __device__ __forceinline__ Partial chunk_reduce(const Chunk& k, const Raw& r, fl
 }
 
 // Partial of a chunk for the entropy of softmax(row / T): the max m, the weight
-// sum s relative to fl32(m*c0), and the first moment s1 = sum_v w_v (x_v - m).
+// sum s relative to fl32(m*c0), and the first moment s1 = sum_v w_v t_v of the
+// exponents t_v = x_v*c0 - fl32(m*c0) (base-2 units; divide by c0 for x - m).
 struct EntPartial {
   float m;
   int pad;
@@ -404,9 +405,12 @@ __device__ __forceinline__ EntPartial chunk_reduce_ent(const Raw& r, float c0) {
     unit_values<DT>(r, j, x);
 #pragma unroll
     for (int e = 0; e < W; ++e) {
-      w[e] = softmax_weight(x[e], c0, mc0);
-      // -inf entries have weight 0 and add nothing to the moment
-      wx[e] = w[e] > 0.0f ? w[e] * (x[e] - p.m) : 0.0f;
+      // the weight from the exponent as it is (a NaN entry poisons the sum, as it
+      // must); in the moment the exponent is floored at -1000, where the weight is
+      // 0 in fp32 anyway, so that -inf entries add 0 * -1000 = 0
+      const float t = __builtin_fmaf(x[e], c0, -mc0);
+      w[e] = __builtin_amdgcn_exp2f(t);
+      wx[e] = w[e] * fmaxf(t, -1000.0f);
     }
     s += (double)pairwise_sum<W>(w);
     s1 += (double)pairwise_sum<W>(wx);
