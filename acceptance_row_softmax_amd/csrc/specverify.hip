@@ -290,20 +290,34 @@ __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, b
 // mode with L < k, hand rows t_L, d_L to the residual waves; otherwise the final
 // token is known (the bonus draw, or argmax of t_L in greedy mode): record it.
 template <int DT, bool STOCH>
+// `other` (lane 0, when have_other): the statistics of the other row of position
+// mi, which the pair combine has just read.
 __device__ __forceinline__ void linear_settle(const LinearParams& P, int64_t b, uint64_t old, uint64_t now,
-                                              const RowStat& mine, int64_t mi, int mwhich) {
+                                              const RowStat& mine, int64_t mi, int mwhich,
+                                              const RowStat& other, bool have_other, bool other_got) {
   const int k = (int)P.k;
   const int Ln = settled_L(now, k);
   if (Ln < 0 || settled_L(old, k) >= 0) return;
+  const bool here = mi == Ln;
   RowStat tl = mine;
   bool got = true;
-  if (!(mi == Ln && mwhich == 0)) {
-    if (lane_id() == 0) got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 0) * ROW_WORDS, tl, P.tag);
+  if (!(here && mwhich == 0)) {
+    if (here && have_other) {
+      tl = other;
+      got = other_got;
+    } else if (lane_id() == 0) {
+      got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 0) * ROW_WORDS, tl, P.tag);
+    }
   }
   if (STOCH && Ln < k) {
     RowStat dl = mine;
-    if (!(mi == Ln && mwhich == 1)) {
-      if (lane_id() == 0) got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 1) * ROW_WORDS, dl, P.tag) && got;
+    if (!(here && mwhich == 1)) {
+      if (here && have_other) {
+        dl = other;
+        got = other_got && got;
+      } else if (lane_id() == 0) {
+        got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 1) * ROW_WORDS, dl, P.tag) && got;
+      }
     }
     if (lane_id() == 0) {
       Decision d;
@@ -371,6 +385,8 @@ __device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q,
 
   uint64_t bits = 0;
   bool update = true;
+  RowStat other;            // stochastic pair: the other row of position i (lane 0)
+  bool have_other = false, other_got = true;
   if (i == k) {
     bits = BONUS_BIT;   // the row after the last draft is combined (and drawn)
   } else if constexpr (!STOCH) {
@@ -383,11 +399,12 @@ __device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q,
     update = (old == 1);
     if (update) {
       // second row of the pair: the acceptance test of position i
-      RowStat other;
+      have_other = true;
       bool got = true;
       if (lane == 0) {
         counter_reset(P.pair_cnt + (b * k + i) * CSTRIDE);
         got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);
+        other_got = got;
         const double pt = which == 0 ? st.px : other.px;
         const double pd = which == 0 ? other.px : st.px;
         double qr;
@@ -411,7 +428,7 @@ __device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q,
     uint64_t olds = 0;
     if (lane == 0) olds = state_or(P.state + b * SSTRIDE, bits);
     olds = bcast(olds);
-    linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which);
+    linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which, other, have_other, other_got);
   }
   linear_event<DT, STOCH>(P, b);
 }
