@@ -68,6 +68,9 @@ def lib():
         L.spec_verify_tree_typical.restype = i32
         L.spec_verify_tree_typical.argtypes = [f32, ctypes.c_double, ctypes.c_double, i64, i64, i64, i32, vp,
                                                i64, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_verify_linear_commit.restype = i32
+        L.spec_verify_linear_commit.argtypes = [i32, f32, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, vp, vp, i64, vp, vp, vp, sz, vp]
         L.spec_commit_linear.restype = i32
         L.spec_commit_linear.argtypes = [i64, i64, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
         L.spec_sample_workspace.restype = sz
@@ -86,7 +89,7 @@ EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_t
             "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
             "spec_workspace_clear", "spec_verify_status_string", "spec_commit_linear",
             "spec_sample_workspace", "spec_sample", "spec_tree_mask", "spec_tree_build_greedy",
-            "spec_verify_tree_typical")
+            "spec_verify_tree_typical", "spec_verify_linear_commit")
 
 
 def status_string(status: int) -> str:
@@ -162,7 +165,7 @@ _WS = Workspace()
 
 def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic",
                   temperature: float = 1.0, *, with_probs: bool = True, err_flags: bool = True,
-                  workspace=None, stream=None, out=None):
+                  seq_len=None, history=None, shifted: bool = True, workspace=None, stream=None, out=None):
     """Verify B linear drafts of k tokens.
 
     target [B][k+1][V], draft [B][k][V] (same dtype; draft unused in greedy mode),
@@ -170,6 +173,9 @@ def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic
     Returns a dict of device tensors: accept_len [B], out_tokens [B][k+1],
     p_target / p_draft [B][k] (stochastic, if with_probs), err_flags [B].
     ``out`` may hold preallocated tensors of those names and shapes.
+    With ``seq_len`` [B] int32 (and optionally ``history`` [B][capacity] int32) the
+    same launch also commits the result in place (spec_verify_linear_commit) and
+    the dict gains "shifted" [B][k+1] (if ``shifted``) and "next_token" [B].
     """
     torch = _torch()
     stoch = mode == "stochastic"
@@ -212,6 +218,23 @@ def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic
     nbytes = L.spec_verify_linear_workspace(B, k, V, dt, mcode)
     s = _stream(stream)
     ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    if seq_len is not None:
+        _need(seq_len, "seq_len", torch.int32, dev)
+        cap = 0
+        if history is not None:
+            _need(history, "history", torch.int32, dev)
+            cap = history.shape[-1]
+        if shifted and "shifted" not in out:
+            out["shifted"] = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+        if "next_token" not in out:
+            out["next_token"] = torch.empty(B, dtype=torch.int32, device=dev)
+        st = L.spec_verify_linear_commit(
+            mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+            _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("p_target")), _ptr(out.get("p_draft")),
+            _ptr(out.get("err_flags")), _ptr(seq_len), _ptr(history), cap, _ptr(out.get("shifted")),
+            _ptr(out["next_token"]), _ptr(ws), ws.numel(), s)
+        _check(st, "spec_verify_linear_commit")
+        return out
     st = L.spec_verify_linear(mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft), _ptr(draft_tokens),
             _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("p_target")),
             _ptr(out.get("p_draft")), _ptr(out.get("err_flags")), _ptr(ws), ws.numel(), s)

@@ -162,6 +162,13 @@ struct LinearParams {
   float c0;
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
+  // optional commit by the emitting wave (spec_verify_linear_commit)
+  int32_t* seq_len;     // [B] in/out
+  int32_t* history;     // [B][capacity]
+  int64_t capacity;
+  int32_t* shifted;     // [B][k+1]
+  int32_t* next_token;  // [B]
+  bool commit;
 };
 
 // Row order. Stochastic: q = i*2B + 2b + which for i < k (which 0 target, 1
@@ -252,8 +259,24 @@ __device__ __forceinline__ void emit_store(const LinearParams& P, int64_t b, con
     if (!err) v = (j < L) ? in.x : (j == L ? y : -1);
     out[j] = v;
   }
+  if (P.commit) {
+    // the commit of spec_commit_linear, applied by the same wave
+    const int len = P.seq_len[b];   // every lane reads it before lane 0 updates it
+    const bool full = !err && P.history && (len < 0 || (int64_t)len + L + 1 > P.capacity);
+    const bool ok = !err && !full;
+    if (full) err |= SV_ERR_CAPACITY;
+    if (lane <= k) {
+      const int64_t j = lane;
+      if (ok && j <= L && P.history) P.history[b * P.capacity + len + j] = (j < L) ? in.x : y;
+      if (P.shifted) P.shifted[b * (k + 1) + j] = !ok ? -1 : ((j == L || j == k) ? y : in.x);
+    }
+    if (lane == 0) {
+      if (ok) P.seq_len[b] = len + L + 1;
+      if (P.next_token) P.next_token[b] = ok ? y : -1;
+    }
+  }
   if (lane == 0) {
-    P.accept_len[b] = err ? -1 : L;
+    P.accept_len[b] = (err & ~SV_ERR_CAPACITY) ? -1 : L;
     if (P.err_flags) P.err_flags[b] = err;
   }
 }
@@ -1172,6 +1195,59 @@ struct RowStatsLauncher {
   }
 };
 
+// Checks and fills the parameters of the linear entry points (B == 0: SV_OK with
+// nothing to launch).
+sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                       sv_dtype dtype, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const float* uniforms, int32_t* accept_len,
+                       int32_t* out_tokens, float* p_target, float* p_draft, int32_t* err_flags,
+                       void* workspace, size_t workspace_bytes) {
+  if (!dtype_ok(dtype)) return SV_EDTYPE;
+  if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
+  const bool stoch = (mode == SV_STOCHASTIC);
+  if (B < 0 || k < 0 || V < 1) return SV_EINVAL;
+  if (k > SV_MAX_K || !shape_ok(V, dtype)) return SV_ELIMIT;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !accept_len || !out_tokens || (k > 0 && !draft_tokens)) return SV_EINVAL;
+  if (stoch && (!temperature_ok(temperature) || !uniforms || (k > 0 && !draft_logits))) return SV_EINVAL;
+  const Layout lay = linear_layout(B, k, V, dtype, mode);
+  if (!ws_ok(workspace, workspace_bytes, lay.total)) return SV_EWORKSPACE;
+  P.target = static_cast<const char*>(target_logits);
+  P.draft = static_cast<const char*>(draft_logits);
+  P.tokens = draft_tokens;
+  P.uniforms = uniforms;
+  P.accept_len = accept_len;
+  P.out_tokens = out_tokens;
+  P.p_target = stoch ? p_target : nullptr;
+  P.p_draft = stoch ? p_draft : nullptr;
+  P.err_flags = err_flags;
+  char* ws = static_cast<char*>(workspace);
+  P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
+  P.rows = reinterpret_cast<uint64_t*>(ws + lay.off[1]);
+  P.dec = reinterpret_cast<uint64_t*>(ws + lay.off[2]);
+  P.res = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
+  P.tok = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
+  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[5]);
+  P.pair_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[6]);
+  P.state = reinterpret_cast<uint64_t*>(ws + lay.off[7]);
+  P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
+  P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
+  P.errw = reinterpret_cast<uint32_t*>(ws + lay.off[10]);
+  P.prob = reinterpret_cast<uint64_t*>(ws + lay.off[11]);
+  P.B = B;
+  P.k = k;
+  P.V = V;
+  P.R = (int)(stoch ? 2 * k + 1 : k + 1);
+  P.C = (int)chunks_per_row(V, dtype);
+  P.CP = (P.C + WPB - 1) / WPB * WPB;
+  P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
+  P.n_waves = B * P.R * P.CP + ((stoch && k > 0) ? B * P.C : 0);
+  if (P.n_waves > MAX_WAVES) return SV_ELIMIT;
+  P.commit = false;
+  P.tag = next_tag();
+  return SV_OK;
+}
+
 // Checks and fills the parameters shared by the tree entry points (B == 0: SV_OK
 // with nothing to launch).
 sv_status tree_setup(TreeParams& P, size_t& smem, bool stoch, float temperature, int64_t B, int64_t n_nodes,
@@ -1243,51 +1319,35 @@ sv_status spec_verify_linear(sv_mode mode, float temperature, int64_t B, int64_t
                              int32_t* out_tokens, float* p_target, float* p_draft,
                              int32_t* err_flags, void* workspace, size_t workspace_bytes,
                              sv_stream_t stream) {
-  if (!dtype_ok(dtype)) return SV_EDTYPE;
-  if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
-  const bool stoch = (mode == SV_STOCHASTIC);
-  if (B < 0 || k < 0 || V < 1) return SV_EINVAL;
-  if (k > SV_MAX_K || !shape_ok(V, dtype)) return SV_ELIMIT;
-  if (B == 0) return SV_OK;
-  if (!target_logits || !accept_len || !out_tokens || (k > 0 && !draft_tokens)) return SV_EINVAL;
-  if (stoch && (!temperature_ok(temperature) || !uniforms || (k > 0 && !draft_logits))) return SV_EINVAL;
-  const Layout lay = linear_layout(B, k, V, dtype, mode);
-  if (!ws_ok(workspace, workspace_bytes, lay.total)) return SV_EWORKSPACE;
-
   LinearParams P{};
-  P.target = static_cast<const char*>(target_logits);
-  P.draft = static_cast<const char*>(draft_logits);
-  P.tokens = draft_tokens;
-  P.uniforms = uniforms;
-  P.accept_len = accept_len;
-  P.out_tokens = out_tokens;
-  P.p_target = stoch ? p_target : nullptr;
-  P.p_draft = stoch ? p_draft : nullptr;
-  P.err_flags = err_flags;
-  char* ws = static_cast<char*>(workspace);
-  P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
-  P.rows = reinterpret_cast<uint64_t*>(ws + lay.off[1]);
-  P.dec = reinterpret_cast<uint64_t*>(ws + lay.off[2]);
-  P.res = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
-  P.tok = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
-  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[5]);
-  P.pair_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[6]);
-  P.state = reinterpret_cast<uint64_t*>(ws + lay.off[7]);
-  P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
-  P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
-  P.errw = reinterpret_cast<uint32_t*>(ws + lay.off[10]);
-  P.prob = reinterpret_cast<uint64_t*>(ws + lay.off[11]);
-  P.B = B;
-  P.k = k;
-  P.V = V;
-  P.R = (int)(stoch ? 2 * k + 1 : k + 1);
-  P.C = (int)chunks_per_row(V, dtype);
-  P.CP = (P.C + WPB - 1) / WPB * WPB;
-  P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  P.n_waves = B * P.R * P.CP + ((stoch && k > 0) ? B * P.C : 0);
-  if (P.n_waves > MAX_WAVES) return SV_ELIMIT;
-  P.tag = next_tag();
-  return dispatch<LinearLauncher>(dtype, stoch, P, reinterpret_cast<hipStream_t>(stream));
+  const sv_status st = linear_setup(P, mode, temperature, B, k, V, dtype, target_logits, draft_logits, draft_tokens,
+                                    uniforms, accept_len, out_tokens, p_target, p_draft, err_flags, workspace,
+                                    workspace_bytes);
+  if (st != SV_OK || B == 0) return st;
+  return dispatch<LinearLauncher>(dtype, mode == SV_STOCHASTIC, P, reinterpret_cast<hipStream_t>(stream));
+}
+
+sv_status spec_verify_linear_commit(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                    sv_dtype dtype, const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* uniforms, int32_t* accept_len,
+                                    int32_t* out_tokens, float* p_target, float* p_draft, int32_t* err_flags,
+                                    int32_t* seq_len, int32_t* history, int64_t capacity, int32_t* shifted,
+                                    int32_t* next_token, void* workspace, size_t workspace_bytes,
+                                    sv_stream_t stream) {
+  if (capacity < 0) return SV_EINVAL;
+  LinearParams P{};
+  const sv_status st = linear_setup(P, mode, temperature, B, k, V, dtype, target_logits, draft_logits, draft_tokens,
+                                    uniforms, accept_len, out_tokens, p_target, p_draft, err_flags, workspace,
+                                    workspace_bytes);
+  if (st != SV_OK || B == 0) return st;
+  if (!seq_len || (capacity > 0 && !history)) return SV_EINVAL;
+  P.commit = true;
+  P.seq_len = seq_len;
+  P.history = capacity > 0 ? history : nullptr;
+  P.capacity = capacity;
+  P.shifted = shifted;
+  P.next_token = next_token;
+  return dispatch<LinearLauncher>(dtype, mode == SV_STOCHASTIC, P, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t spec_verify_tree_workspace(int64_t B, int64_t n_nodes, int64_t V, sv_dtype dtype, sv_mode mode) {

@@ -229,6 +229,22 @@ sv_status spec_commit_linear(int64_t B, int64_t k, const int32_t* accept_len, co
                              int64_t capacity, int32_t* shifted, int32_t* next_token,
                              int32_t* err_flags, sv_stream_t stream);
 
+/* Verification and commit in one launch: spec_verify_linear's arguments and outputs,
+ * then the commit of spec_commit_linear (seq_len, history, capacity, shifted,
+ * next_token as there) applied by the wave that writes the sequence's outputs, with
+ * no second launch. err_flags carries the verification's bits and SV_ERR_CAPACITY;
+ * with SV_ERR_CAPACITY alone the verification outputs are valid and nothing is
+ * committed. Same workspace as spec_verify_linear.
+ */
+sv_status spec_verify_linear_commit(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                    sv_dtype dtype, const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* uniforms,
+                                    int32_t* accept_len, int32_t* out_tokens, float* p_target,
+                                    float* p_draft, int32_t* err_flags, int32_t* seq_len,
+                                    int32_t* history, int64_t capacity, int32_t* shifted,
+                                    int32_t* next_token, void* workspace, size_t workspace_bytes,
+                                    sv_stream_t stream);
+
 /* ---------------------------------------------------------------- sampler
  * [S-MTP] (sampling shared by every scheme), [S-ZE]. One token per row of
  * logits[rows][V]: argmax (SV_GREEDY: largest value, lowest index on ties) or the

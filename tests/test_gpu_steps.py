@@ -202,3 +202,46 @@ def test_tree_mask_deep_chain_max_nodes():
         assert w[i, nw] == np.uint32((1 << (i % 32 + 1)) - 1 if i % 32 < 31 else 0xFFFFFFFF)
         assert np.all(w[i, nw + 1:W] == 0)
     assert _cpu(r["err_flags"])[0] == 0
+
+
+# ------------------------------------------------------------------ verify + commit in one launch
+@pytest.mark.parametrize("case", ["c2", "small_k0", "small_greedy", "full_histories"])
+def test_fused_commit_equals_verify_then_commit(case):
+    import torch
+    if case == "c2":
+        w = gen.c2_linear(1)
+    elif case == "small_k0":
+        w = gen.linear_draft_target(65, 0, 40, 0, 5000, gen.DT_F16, 2.0, 0.5, "stochastic", 0.9, "k0")
+    else:
+        w = gen.linear_draft_target(66, 0, 64, 3, 7001, gen.DT_BF16, 2.0, 0.5,
+                                    "greedy" if case == "small_greedy" else "stochastic", 1.0, case)
+    B, k = w.B, w.k
+    rng = np.random.default_rng(7)
+    cap = 40
+    ln = rng.integers(0, cap - k - 1, size=B).astype(np.int32)
+    if case == "full_histories":
+        ln[::3] = cap                           # no room left: capacity errors
+    hist = rng.integers(0, 1000, size=(B, cap)).astype(np.int32)
+    G.say(f"fused commit {case} B={B} k={k}")
+    t, d = G.to_dev(w.target, w.dtype), (G.to_dev(w.draft, w.dtype) if k else None)
+    x = G.to_dev(w.draft_tokens.astype(np.int32)) if k else None
+    u = G.to_dev(w.uniforms.astype(np.float32))
+    # two launches
+    l1, h1 = G.to_dev(ln), G.to_dev(hist)
+    g = sv.verify_linear(t, d, x, u, mode=w.mode, temperature=w.temperature)
+    c = sv.commit_linear(g["accept_len"], g["out_tokens"], x, l1, h1)
+    # one launch
+    l2, h2 = G.to_dev(ln), G.to_dev(hist)
+    f = sv.verify_linear(t, d, x, u, mode=w.mode, temperature=w.temperature, seq_len=l2, history=h2)
+    torch.cuda.synchronize()
+    for key in ("accept_len", "out_tokens"):
+        np.testing.assert_array_equal(_cpu(f[key]), _cpu(g[key]))
+    np.testing.assert_array_equal(_cpu(l2), _cpu(l1))
+    np.testing.assert_array_equal(_cpu(h2), _cpu(h1))
+    np.testing.assert_array_equal(_cpu(f["shifted"]), _cpu(c["shifted"]))
+    np.testing.assert_array_equal(_cpu(f["next_token"]), _cpu(c["next_token"]))
+    # err_flags: the verification's bits, plus SV_ERR_CAPACITY where the commit found no room
+    exp = _cpu(g["err_flags"]) | np.where(_cpu(c["err_flags"]) == sv.SV_ERR_CAPACITY, sv.SV_ERR_CAPACITY, 0)
+    np.testing.assert_array_equal(_cpu(f["err_flags"]), exp)
+    if case == "full_histories":
+        assert np.any(_cpu(f["err_flags"]) == sv.SV_ERR_CAPACITY)
