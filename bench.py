@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="rotating input copies (0 = auto)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of a HIP graph")
+    ap.add_argument("--commit", action="store_true",
+                    help="linear configs: verify and commit in one launch (spec_verify_linear_commit)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -353,15 +355,25 @@ def main():
                      for _ in range(copies - 1)]
     outs = []
 
+    commit = None
+    if linear and args.commit:
+        # the sequences' lengths and histories, committed in place by every call
+        # (capacity for every call of the run: warmup, parity, graph, timed steps and
+        # the per-launch event pairs; lengths grow by at most k + 1 per call)
+        cap = (args.steps + args.warmup + 2 * copies + 410) * (w.k + 1)
+        commit = {"seq_len": torch.zeros(w.B, dtype=torch.int32, device=dev),
+                  "history": torch.zeros((w.B, cap), dtype=torch.int32, device=dev)}
+
     def call(i):
         s = sets[i]
         if linear:
+            kw = commit or {}
             if len(outs) <= i:
                 outs.append(sv.verify_linear(s["t"], s["d"], s["x"], s["u"], mode=w.mode,
-                                             temperature=w.temperature))
+                                             temperature=w.temperature, **kw))
                 return outs[i]
             return sv.verify_linear(s["t"], s["d"], s["x"], s["u"], mode=w.mode,
-                                    temperature=w.temperature, out=outs[i])
+                                    temperature=w.temperature, out=outs[i], **kw)
         if w.mode == "typical":
             return sv.verify_tree(s["par"], s["cand"], s["lg"], s["u"], w.max_depth, mode="typical",
                                   temperature=w.temperature, epsilon=TYPICAL_EPS, delta=TYPICAL_DELTA)
@@ -518,7 +530,8 @@ def main():
         "vs_baseline": None,
         "dtype": {gen.DT_F32: "f32", gen.DT_BF16: "bf16", gen.DT_F16: "f16"}[w.dtype],
         "data": "synthetic (seeded generator; no dataset)",
-        "config": {"workload": describe(w), "global_batch": w.B,
+        "config": {"workload": describe(w) + (" + commit in the same launch" if commit else ""),
+                   "global_batch": w.B,
                    "positions_per_step": npos, "algorithmic_bytes_per_step": alg_bytes,
                    "input_copies": copies, "graph": not args.no_graph},
         "logit_GBps": step_gbps,
