@@ -2,6 +2,8 @@
 (bit-exact, and end to end: speculative greedy decoding through the GPU verify and
 commit entry points equals plain greedy decoding), the sampler (bit-exact except
 draws within 1e-6 of a bin edge, counted), and the tree mask (bit-exact)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -245,3 +247,50 @@ def test_fused_commit_equals_verify_then_commit(case):
     np.testing.assert_array_equal(_cpu(f["err_flags"]), exp)
     if case == "full_histories":
         assert np.any(_cpu(f["err_flags"]) == sv.SV_ERR_CAPACITY)
+
+
+def test_one_workspace_serves_every_entry_point():
+    """Every entry point leaves its workspace all zeros, so one workspace serves them
+    all in any order (linear, linear + commit, trees greedy / eager / lazy / typical,
+    sampler, row statistics)."""
+    import torch
+    L = sv.lib()
+    wl = gen.c2_linear(11, B=6)
+    ws_shape = [3, 3, 3, 3, 3, 3]                      # 1093 nodes x 4 trees: lazy draws
+    parent, _ = gen.cartesian_tree(ws_shape)
+    n, Bt, Vt = len(parent), 4, 3000
+    x = gen.normal_pair(gen.key(67, 1, 1), 2.0, 0, 0.0, Bt * n * Vt, gen.DT_F16, want_b=False)[0].reshape(Bt, n, Vt)
+    cand = np.random.default_rng(3).integers(0, Vt, size=(Bt, n)).astype(np.int32)
+    ut = gen.uniforms(gen.key(67, 1, 2), Bt * n).reshape(Bt, n)
+    tl = gen.TreeWorkload("ws-lazy", "stochastic", 1.0, Bt, n, Vt, gen.DT_F16, parent, cand, x, ut, 6)
+    te = gen.c4_medusa_sparse(3, mode="stochastic", B=4)      # eager draws
+    need = max(L.spec_verify_linear_workspace(wl.B, wl.k, wl.V, wl.dtype, sv.SV_STOCHASTIC),
+               L.spec_verify_tree_workspace(Bt, n, Vt, gen.DT_F16, sv.SV_STOCHASTIC),
+               L.spec_verify_tree_workspace(te.B, te.n_nodes, te.V, te.dtype, sv.SV_STOCHASTIC),
+               L.spec_sample_workspace(wl.B * wl.k, wl.V, wl.dtype),
+               L.spec_row_stats_workspace(wl.B * wl.k, wl.V, wl.dtype))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    t, d = G.to_dev(wl.target, wl.dtype), G.to_dev(wl.draft, wl.dtype)
+    xd, u = G.to_dev(wl.draft_tokens.astype(np.int32)), G.to_dev(wl.uniforms.astype(np.float32))
+    rows = G.to_dev(np.ascontiguousarray(wl.draft.reshape(-1, wl.V)), wl.dtype)
+    ur = G.to_dev(gen.uniforms(gen.key(67, 2, 1), wl.B * wl.k).astype(np.float32))
+    ln = G.to_dev(np.zeros(wl.B, np.int32))
+    hist = G.to_dev(np.zeros((wl.B, 64), np.int32))
+    calls = [
+        ("linear", lambda: sv.verify_linear(t, d, xd, u, mode="stochastic", temperature=0.7, workspace=ws)),
+        ("tree lazy", lambda: G.run_tree(tl, None, workspace=ws)),
+        ("linear+commit", lambda: sv.verify_linear(t, d, xd, u, mode="stochastic", temperature=0.7,
+                                                   seq_len=ln, history=hist, workspace=ws)),
+        ("tree eager", lambda: G.run_tree(te, None, workspace=ws)),
+        ("tree typical", lambda: G.run_tree(dataclasses.replace(tl, mode="typical"), None, epsilon=0.1,
+                                            delta=0.3, workspace=ws)),
+        ("sampler", lambda: sv.sample(rows, ur, mode="stochastic", temperature=0.7, workspace=ws)),
+        ("tree greedy", lambda: G.run_tree(dataclasses.replace(te, mode="greedy"), None, workspace=ws)),
+        ("row stats", lambda: sv.row_stats(rows, 0.7, workspace=ws)),
+        ("linear again", lambda: sv.verify_linear(t, d, xd, u, mode="stochastic", temperature=0.7, workspace=ws)),
+    ]
+    for name, f in calls:
+        G.say(f"shared workspace: {name}")
+        f()
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, name
