@@ -400,9 +400,7 @@ __device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q,
       st.y = softmax_draw<DT>(row, V, P.C, P.c0, P.uniforms[b * (k + 1) + k], rp, rs, wl);
   }
   if (lane == 0) {
-    if (st.ok != 1)
-      __hip_atomic_fetch_or(P.errw + b * CSTRIDE, (uint32_t)(st.ok < 0 ? SV_ERR_INTERNAL : SV_ERR_ROW),
-                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (st.ok != 1) error_or(P.errw + b * CSTRIDE, (uint32_t)(st.ok < 0 ? SV_ERR_INTERNAL : SV_ERR_ROW));
     put_rec(P.rows + q * ROW_WORDS, st, P.tag);
   }
 
@@ -440,9 +438,7 @@ __device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q,
         pr.pt = (float)pt;
         pr.pd = (float)pd;
         put_rec(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
-        if (!got)
-          __hip_atomic_fetch_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+        if (!got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
       }
       bits = bcast(bits);
     }

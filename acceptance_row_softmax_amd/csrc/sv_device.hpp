@@ -698,6 +698,13 @@ __device__ __forceinline__ void clear_rec(uint64_t* dst) {
 __device__ __forceinline__ uint32_t counter_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// OR of error bits, complete before the wave goes on: the returned value is
+// consumed, so the wave waits for it, and the bits are in place before any later
+// event count of this wave (the emission, which reads them, follows that count).
+__device__ __forceinline__ void error_or(uint32_t* p, uint32_t v) {
+  uint32_t prev = __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" : "+v"(prev));
+}
 __device__ __forceinline__ uint64_t state_or(uint64_t* p, uint64_t v) {
   return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

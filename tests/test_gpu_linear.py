@@ -48,6 +48,16 @@ def test_tiles_and_ragged_tails(dtype, V, mode):
     _check(w)
 
 
+@pytest.mark.parametrize("V", [262144, 262145, 524288])
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_long_rows(V, mode):
+    # fp32 rows of exactly 1 MiB (a target/draft pair's 256 chunk partials fill a
+    # wave's four rounds), one element over (each row of a pair combined on its
+    # own), and the longest row the library takes (2 MiB)
+    w = gen.linear_draft_target(96, V % 7, 3, 2, V, gen.DT_F32, 3.0, 1.0, mode, 0.8, f"long{V}")
+    _check(w)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_c2_draft_target_full_size(seed):
     w = gen.c2_linear(seed)            # B=32, k=4, V=128256, bf16, T=0.7
