@@ -24,11 +24,13 @@
 // No wave ever waits for work that is dispatched after it except the residual
 // waves (which wait for the decision of streaming waves dispatched before them).
 //
-// Trees: two launches. A streaming launch of the same kind reduces every node's
-// row (greedy: its argmax is the node's token; stochastic: for a small batch the
-// token is drawn there too, at every node), then one workgroup per tree searches
-// the accepted path in LDS; for a large stochastic batch it walks level by level
-// and draws the tokens of the accepted nodes only. Row statistics: the streaming
+// Trees: a streaming launch of the same kind reduces every node's row (greedy:
+// its argmax is the node's token; stochastic: for a small batch the token is
+// drawn there too, at every node). Trees of at most 256 nodes whose tokens are
+// then known are walked in that launch, by the wave that combines the tree's last
+// node; otherwise a second launch runs one workgroup per tree that searches the
+// accepted path in LDS, and for a large stochastic batch walks level by level and
+// draws the tokens of the accepted nodes only. Row statistics: the streaming
 // launch alone.
 //
 // Sources: "Accelerating Sonar through speculation" (sections "Spekulatives
@@ -645,6 +647,9 @@ struct TreeParams {
   uint64_t* parts;      // [B*N][C] Partial records
   uint32_t* row_cnt;    // [B*N]
   int32_t* node_y;      // [B][N] token of each node (-1 unusable row, -2 a wait timed out)
+  uint64_t* yrec;       // [B][N] the same as Token records, when the stream launch walks the trees
+  uint32_t* tree_cnt;   // [B]    nodes combined per tree (wave walk)
+  bool wave_walk;       // trees of at most WAVE_WALK_NODES nodes, tokens known while streaming
   struct NodeStat* nstat;   // [B][N] typical acceptance: each node's softmax statistics
   int64_t B, N, V, max_depth;
   int C, CP;
@@ -737,6 +742,156 @@ __device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const c
   }
 }
 
+// Trees of at most WAVE_WALK_NODES nodes whose tokens are known once every row is
+// combined (greedy, or stochastic with every node drawn while streaming) are
+// walked by the wave that combines the tree's last node, in registers: lane l
+// holds nodes l + 64 s, and a node's parent, token or match flag is fetched
+// across lanes. The result is the one the walk launch computes.
+constexpr int WW_SLOTS = 4;
+constexpr int64_t WAVE_WALK_NODES = WW_SLOTS * WAVE;
+
+// a[m / 64] of lane m % 64, for every lane's own m in [0, WAVE_WALK_NODES)
+__device__ __forceinline__ int ww_gather(const int (&a)[WW_SLOTS], int m) {
+  int r = 0;
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int v = __shfl(a[s], m & (WAVE - 1));
+    if ((m >> 6) == s) r = v;
+  }
+  return r;
+}
+
+__device__ __forceinline__ int wave_or_int(int v) {
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) v |= __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ void tree_wave_walk(const TreeParams& P, int64_t b) {
+  const int lane = lane_id();
+  const int N = (int)P.N;
+  const int32_t* par = P.parent + b * P.parent_stride;
+  const int32_t* cand = P.cand + b * N;
+  uint64_t* yr = P.yrec + b * N;
+  int pv[WW_SLOTS], cv[WW_SLOTS], yv[WW_SLOTS], st[WW_SLOTS];
+  int err = 0;
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int i = s * WAVE + lane;
+    pv[s] = -1;
+    cv[s] = 0;
+    yv[s] = 0;
+    if (i < N) {
+      pv[s] = par[i];
+      cv[s] = cand[i];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int i = s * WAVE + lane;
+    if (i < N) {
+      Token t;
+      yv[s] = get_rec(yr + i, t, P.tag) ? t.y : -2;
+      clear_rec<Token>(yr + i);
+    }
+  }
+  // validation; a bad parent is replaced by the root, so every chain ends
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int i = s * WAVE + lane;
+    st[s] = 0;
+    if (i >= N) continue;
+    if (yv[s] == -1) err |= SV_ERR_ROW;
+    if (yv[s] == -2) err |= SV_ERR_INTERNAL;
+    const bool bad = (i == 0) ? (pv[s] != -1) : (pv[s] < 0 || pv[s] >= i);
+    if (bad) err |= SV_ERR_TREE;
+    if (i > 0 && (cv[s] < 0 || cv[s] >= P.V)) err |= SV_ERR_TOKEN;
+    pv[s] = bad ? 0 : pv[s];
+    st[s] = bad ? 0 : 1;   // whether the match test applies
+  }
+  // match: the candidate is its parent's token
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int yp = ww_gather(yv, pv[s]);
+    const int i = s * WAVE + lane;
+    st[s] = (i > 0 && i < N && st[s] && cv[s] == yp) ? 1 : 0;
+  }
+  // every node's chain to the root: depth, and whether every node on it matched
+  int cur[WW_SLOTS], d[WW_SLOTS], acc[WW_SLOTS];
+  int too_deep = 0;
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int i = s * WAVE + lane;
+    cur[s] = i < N ? i : 0;
+    d[s] = 0;
+    acc[s] = i < N ? 1 : 0;
+  }
+  for (;;) {
+    int moving = 0;
+#pragma unroll
+    for (int s = 0; s < WW_SLOTS; ++s) {
+      const int m = ww_gather(st, cur[s]);
+      const int up = ww_gather(pv, cur[s]);
+      if (cur[s] == 0) continue;
+      if (d[s] >= P.max_depth) {
+        too_deep = 1;
+        cur[s] = 0;
+        acc[s] = 0;
+        continue;
+      }
+      acc[s] &= m;
+      cur[s] = up;
+      ++d[s];
+      moving = 1;
+    }
+    if (__ballot(moving) == 0ull) break;
+  }
+  int best_key = -1;   // depth * 2^15 + (2^15 - 1 - index): deepest, then lowest index
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int i = s * WAVE + lane;
+    if (acc[s]) {
+      const int key = (d[s] << 15) | (32767 - i);
+      best_key = key > best_key ? key : best_key;
+    }
+  }
+  best_key = wave_max_int(best_key);
+  if (__ballot(too_deep) != 0ull) err |= SV_ERR_TREE;
+  err = wave_or_int(err);
+  int32_t* path = P.path_nodes + b * P.max_depth;
+  int32_t* out = P.out_tokens + b * (P.max_depth + 1);
+  if (err) {
+    for (int64_t j = lane; j < P.max_depth; j += WAVE) path[j] = -1;
+    for (int64_t j = lane; j <= P.max_depth; j += WAVE) out[j] = -1;
+    if (lane == 0) {
+      P.accept_len[b] = -1;
+      if (P.err_flags) P.err_flags[b] = err;
+    }
+    return;
+  }
+  const int L = best_key >> 15;
+  const int best = 32767 - (best_key & 32767);
+  for (int64_t j = L + lane; j < P.max_depth; j += WAVE) path[j] = -1;
+  for (int64_t j = L + 1 + lane; j <= P.max_depth; j += WAVE) out[j] = -1;
+  // the accepted path, from the deepest node up
+  int node = best;
+  const int yb = ww_gather(yv, best);
+  for (int j = L - 1; j >= 0; --j) {
+    const int cn = ww_gather(cv, node);
+    const int up = ww_gather(pv, node);
+    if (lane == 0) {
+      path[j] = node;
+      out[j] = cn;
+    }
+    node = up;
+  }
+  if (lane == 0) {
+    out[L] = yb;
+    P.accept_len[b] = L;
+    if (P.err_flags) P.err_flags[b] = 0;
+  }
+}
+
 template <int DT, int TD>
 __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
   constexpr int E = DTraits<DT>::E;
@@ -778,6 +933,22 @@ __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
       y = usable ? 0 : -1;
   } else {
     y = rs.argmax;
+  }
+  if constexpr (TD == TD_ARGMAX || TD == TD_EAGER) {
+    if (P.wave_walk) {
+      const int64_t b = q / P.N;
+      uint32_t told = 0;
+      if (lane_id() == 0) {
+        Token t;
+        t.y = y;
+        put_rec(P.yrec + q, t, P.tag);
+        told = counter_add(P.tree_cnt + b * CSTRIDE, 1u);
+      }
+      if (bcast(told) + 1 != (uint32_t)P.N) return;
+      if (lane_id() == 0) counter_reset(P.tree_cnt + b * CSTRIDE);
+      tree_wave_walk(P, b);
+      return;
+    }
   }
   if (lane_id() == 0) P.node_y[q] = y;
 }
@@ -1133,7 +1304,7 @@ Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode)
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
   const int64_t C = chunks_per_row(V, dt);
   return make_layout({(size_t)(B * N * C) * PART_WORDS * 8, (size_t)(B * N * CSTRIDE) * 4, (size_t)(B * N) * 4,
-                      (size_t)(B * N) * sizeof(NodeStat)});
+                      (size_t)(B * N) * sizeof(NodeStat), (size_t)(B * N) * 8, (size_t)(B * CSTRIDE) * 4});
 }
 
 Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
@@ -1156,14 +1327,17 @@ struct TreeLauncher {
   static sv_status run(const TreeParams& P, size_t smem, hipStream_t s) {
     const bool eager = STOCH && P.B * P.N <= TREE_EAGER_ROWS;
     const dim3 grid(blocks_for(P.n_stream)), trees((unsigned)P.B);
+    TreeParams Q = P;
+    Q.wave_walk = (!STOCH || eager) && P.N <= WAVE_WALK_NODES;
     if (!STOCH) {
-      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_ARGMAX>), grid, dim3(BLOCK), 0, s, P);
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_ARGMAX>), grid, dim3(BLOCK), 0, s, Q);
     } else if (eager) {
-      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_EAGER>), grid, dim3(BLOCK), 0, s, P);
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_EAGER>), grid, dim3(BLOCK), 0, s, Q);
     } else {
-      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_LAZY>), grid, dim3(BLOCK), 0, s, P);
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_LAZY>), grid, dim3(BLOCK), 0, s, Q);
     }
     if (launch_status() != SV_OK) return SV_EHIP;
+    if (Q.wave_walk) return SV_OK;   // the streaming launch has walked every tree
     if (STOCH && !eager) {
       hipLaunchKernelGGL((tree_walk_kernel<DT, WM_LAZY, 512>), trees, dim3(512), smem, s, P);
     } else {
@@ -1273,6 +1447,9 @@ sv_status tree_setup(TreeParams& P, size_t& smem, bool stoch, float temperature,
   P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[1]);
   P.node_y = reinterpret_cast<int32_t*>(ws + lay.off[2]);
   P.nstat = reinterpret_cast<NodeStat*>(ws + lay.off[3]);
+  P.yrec = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
+  P.tree_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[5]);
+  P.wave_walk = false;
   P.B = B;
   P.N = n_nodes;
   P.V = V;

@@ -141,3 +141,34 @@ def test_stochastic_tree_deep_acceptance(shape):
     assert g["accept_len"].mean() >= 2.0
     # trees 0-3 accept more nodes than their path holds: several draws per level
     assert np.sum(o["n_eval"][:4]) > np.sum(o["accept_len"][:4] + 1) + 4
+
+
+@pytest.mark.parametrize("n", [256, 257])
+@pytest.mark.parametrize("mode", ["greedy", "stochastic"])
+def test_random_trees_at_the_wave_walk_bound(n, mode):
+    # Trees of at most 256 nodes whose tokens are known while streaming are walked
+    # by one wave of the streaming launch (four nodes per lane); a 257-node tree
+    # goes to the walk launch. Random recursive trees (each parent uniform among
+    # the earlier nodes) with one dominant token per row, so that long paths are
+    # accepted; then a depth bound one below the deepest node is an error for
+    # every tree on both paths.
+    rng = np.random.default_rng(n * 3 + (mode == "stochastic"))
+    parent = np.array([-1] + [rng.integers(0, i) for i in range(1, n)], np.int32)
+    depth = np.zeros(n, np.int64)
+    for i in range(1, n):
+        depth[i] = depth[parent[i]] + 1
+    B, V = 6, 2000
+    dom = rng.integers(0, V, size=(B, n))
+    x = rng.normal(0.0, 1.0, size=(B, n, V))
+    x[np.arange(B)[:, None], np.arange(n)[None, :], dom] += 20.0
+    logits = gen.round_to(gen.DT_BF16, x)
+    cand = np.where(rng.random((B, n)) < 0.7, dom[:, parent], rng.integers(0, V, (B, n))).astype(np.int32)
+    cand[:, 0] = -1
+    u = gen.uniforms(gen.key(64, n, 5), B * n).reshape(B, n)
+    w = gen.TreeWorkload("wavewalk", mode, 1.0, B, n, V, gen.DT_BF16, parent, cand, logits, u,
+                         int(depth.max()))
+    g, o, _, _ = _check(w)
+    assert np.all(g["err_flags"] == 0)
+    assert g["accept_len"].max() >= 3
+    g2, _, _, _ = _check(w, max_depth=int(depth.max()) - 1)
+    assert np.all(g2["err_flags"] & 4)
