@@ -650,19 +650,25 @@ struct TreeParams {
   uint64_t* yrec;       // [B][N] the same as Token records, when the stream launch walks the trees
   uint32_t* tree_cnt;   // [B]    nodes combined per tree (wave walk)
   bool wave_walk;       // trees of at most WAVE_WALK_NODES nodes, tokens known while streaming
+  float* xl;            // [B][N] typical acceptance: each candidate's logit in its parent's row
+  int64_t n_gather;     // typical acceptance: waves that gather xl, ahead of the streaming waves
   struct NodeStat* nstat;   // [B][N] typical acceptance: each node's softmax statistics
   int64_t B, N, V, max_depth;
   int C, CP;
   float c0;
-  double eps, delta;    // typical acceptance: threshold min(eps, delta * exp(-H))
+  double l2eps, l2delta;   // typical acceptance: log2 of eps and delta (-inf for 0)
   uint32_t tag;
   int64_t n_stream;
 };
 
-// softmax(row / T) of a node: max M, Z = sum_v exp((x_v - M) / T), entropy H (nats).
+// Typical acceptance, the gate of a node: a child's candidate v passes iff
+// p(v) = exp2((x_v - M) c0) / Z > min(eps, delta * exp(-H)), with max M, normaliser
+// Z = sum_v exp2((x_v - M) c0) and entropy H (nats) of softmax(row / T); in base-2
+// logarithms, iff (x_v - M) c0 > G = log2(Z) + log2(min(eps, delta * exp(-H))).
+// With S1 = sum_v w_v (x_v - M) c0 over the weights w_v = exp2((x_v - M) c0),
+// H / ln 2 = log2(Z) - S1 / Z, so G = min(log2(Z) + log2(eps), log2(delta) + S1 / Z).
 struct NodeStat {
-  double Z;
-  double H;
+  double G;
   float M;
   int ok;
 };
@@ -731,10 +737,14 @@ __device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const c
   const bool all = __ballot(!got) == 0ull;
   NodeStat st;
   st.M = M;
-  st.Z = Z;
-  // H = ln Z - E[(x - M) / T], with (x - M) / T = (x - M) c0 ln 2
-  st.H = log(Z) - (S1 / Z) * LN2;
-  const bool usable = M > -INFINITY && __builtin_isfinite(Z) && Z > 0.0 && __builtin_isfinite(st.H);
+  // log2(Z) from Z = m 2^e, m in [0.5, 1): e + log2(m), the fraction's log2 in fp32
+  // (absolute error about 1e-7)
+  int ez = 0;
+  const double mz = frexp(Z, &ez);
+  const double l2z = (double)ez + (double)__builtin_amdgcn_logf((float)mz);
+  const double g1 = l2z + P.l2eps, g2 = P.l2delta + S1 / Z;
+  st.G = g1 < g2 ? g1 : g2;
+  const bool usable = M > -INFINITY && __builtin_isfinite(Z) && Z > 0.0 && __builtin_isfinite(S1);
   st.ok = usable ? 1 : 0;
   if (lane == 0) {
     P.nstat[q] = st;
@@ -892,11 +902,37 @@ __device__ __forceinline__ void tree_wave_walk(const TreeParams& P, int64_t b) {
   }
 }
 
+// Typical acceptance, gather wave g: lane l takes node t = 64 g + l of the batch
+// and reads its candidate's logit in its parent's row (0 where the parent or the
+// candidate is out of range: the walk flags those). Many waves across the chip
+// keep these scattered reads in flight together; they run ahead of the stream.
+template <int DT>
+__device__ __forceinline__ void tree_gather_candidates(const TreeParams& P, int64_t g) {
+  constexpr int E = DTraits<DT>::E;
+  const int64_t t = g * WAVE + lane_id();
+  if (t >= P.B * P.N) return;
+  const int64_t b = t / P.N, i = t - b * P.N;
+  float x = 0.0f;
+  if (i > 0) {
+    const int32_t pi = P.parent[b * P.parent_stride + i];
+    const int32_t ci = P.cand[t];
+    if (pi >= 0 && pi < i && ci >= 0 && ci < P.V) x = load_elem<DT>(P.logits + ((b * P.N + pi) * P.V) * E, ci);
+  }
+  P.xl[t] = x;
+}
+
 template <int DT, int TD>
 __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
   constexpr int E = DTraits<DT>::E;
   constexpr bool STOCH = TD != TD_ARGMAX;
-  const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
+  int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
+  if constexpr (TD == TD_TYPICAL) {
+    if (w < P.n_gather) {
+      tree_gather_candidates<DT>(P, w);
+      return;
+    }
+    w -= P.n_gather;
+  }
   if (w >= P.n_stream) return;
   const uint32_t C = (uint32_t)P.C;
   uint32_t q32, c32;
@@ -957,11 +993,16 @@ __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
 static_assert(SV_MAX_TREE_NODES <= 16384, "tree walk keys");
 constexpr int WALK_BATCH = 8;   // nodes per thread whose loads are in flight together
 
-__device__ __forceinline__ int block_or(int v) {
-  // OR over the workgroup (each bit through __syncthreads_or)
+// OR over the workgroup (sh: one int per wave).
+template <int NT>
+__device__ __forceinline__ int block_or(int v, int* sh) {
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) v |= __shfl_xor(v, o);
+  if (lane_id() == 0) sh[wave_in_block()] = v;
+  __syncthreads();
   int r = 0;
-  for (int bit = 1; bit <= SV_ERR_INTERNAL; bit <<= 1)
-    if (__syncthreads_or(v & bit)) r |= bit;
+  for (int wv = 0; wv < NT / WAVE; ++wv) r |= sh[wv];
+  __syncthreads();
   return r;
 }
 
@@ -1047,7 +1088,7 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
   for (int64_t base = 0; base < N; base += (int64_t)NT * WALK_BATCH) {
     int yv[WALK_BATCH], pv[WALK_BATCH], cv[WALK_BATCH], yp[WALK_BATCH];
     float xl[WALK_BATCH], nm[WALK_BATCH];
-    double nz[WALK_BATCH], nh[WALK_BATCH];
+    double ng[WALK_BATCH];
     int nok[WALK_BATCH];
 #pragma unroll
     for (int j = 0; j < WALK_BATCH; ++j) {
@@ -1067,17 +1108,16 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
       const bool ok = i > 0 && i < N && pv[j] >= 0 && pv[j] < i;
       yp[j] = -1;
       xl[j] = nm[j] = 0.0f;
-      nz[j] = nh[j] = 0.0;
+      ng[j] = 0.0;
       nok[j] = 0;
       if (WM == WM_KNOWN && ok) yp[j] = ny[pv[j]];
       if (WM == WM_TYPICAL && ok && cv[j] >= 0 && cv[j] < P.V) {
         // the candidate's logit in its parent's row, and the parent's statistics
-        const NodeStat* ps = P.nstat + b * N + pv[j];
-        nz[j] = ps->Z;
-        nh[j] = ps->H;
-        nm[j] = ps->M;
-        nok[j] = ps->ok;
-        xl[j] = load_elem<DT>(P.logits + ((b * N + pv[j]) * P.V) * E, cv[j]);
+        const NodeStat ps = P.nstat[b * N + pv[j]];
+        ng[j] = ps.G;
+        nm[j] = ps.M;
+        nok[j] = ps.ok;
+        xl[j] = P.xl[b * N + i];
       }
     }
 #pragma unroll
@@ -1094,16 +1134,14 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
         if (cv[j] < 0 || cv[j] >= P.V) err |= SV_ERR_TOKEN;
         if (WM == WM_KNOWN && !bad) m = (cv[j] == yp[j]) ? 1 : 0;
         if (WM == WM_TYPICAL && !bad && nok[j]) {
-          // p_parent(cand) = exp((x - M) / T) / Z against min(eps, delta * exp(-H))
-          const double prob = exp2(((double)xl[j] - (double)nm[j]) * (double)P.c0) / nz[j];
-          const double dt = P.delta * exp(-nh[j]);
-          m = prob > (P.eps < dt ? P.eps : dt) ? 1 : 0;
+          // p_parent(cand) against the parent's threshold, through its gate
+          m = ((double)xl[j] - (double)nm[j]) * (double)P.c0 > ng[j] ? 1 : 0;
         }
       }
       st_s[i] = WM == WM_LAZY ? (unsigned char)(i == 0 ? 1 : 0) : m;
     }
   }
-  int all_err = block_or(err);
+  int all_err = block_or<NT>(err, red_sh);
   // depth check (bad parents were replaced by the root, so every chain ends; the
   // bound is checked whatever other error was found) and, tokens known, the path
   // search; WALK_BATCH chains per thread advance together
@@ -1225,8 +1263,9 @@ __global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
   for (int64_t i = tid; i < N; i += NT) {
     ny[i] = 0;
     if (WM == WM_TYPICAL) {
+      P.xl[b * N + i] = 0.0f;
       NodeStat z;
-      z.Z = z.H = 0.0;
+      z.G = 0.0;
       z.M = 0.0f;
       z.ok = 0;
       P.nstat[b * N + i] = z;
@@ -1304,7 +1343,8 @@ Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode)
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
   const int64_t C = chunks_per_row(V, dt);
   return make_layout({(size_t)(B * N * C) * PART_WORDS * 8, (size_t)(B * N * CSTRIDE) * 4, (size_t)(B * N) * 4,
-                      (size_t)(B * N) * sizeof(NodeStat), (size_t)(B * N) * 8, (size_t)(B * CSTRIDE) * 4});
+                      (size_t)(B * N) * sizeof(NodeStat), (size_t)(B * N) * 8, (size_t)(B * CSTRIDE) * 4,
+                      (size_t)(B * N) * 4});
 }
 
 Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
@@ -1350,9 +1390,14 @@ struct TreeLauncher {
 template <int DT, bool UNUSED>
 struct TypicalLauncher {
   static sv_status run(const TreeParams& P, size_t smem, hipStream_t s) {
-    hipLaunchKernelGGL((tree_stream_kernel<DT, TD_TYPICAL>), dim3(blocks_for(P.n_stream)), dim3(BLOCK), 0, s, P);
+    // gather waves ahead of the streaming waves, whole groups of 8 workgroups so
+    // that the streaming waves keep their XCD placement
+    TreeParams Q = P;
+    Q.n_gather = ((P.B * P.N + WAVE - 1) / WAVE + 8 * WPB - 1) / (8 * WPB) * (8 * WPB);
+    hipLaunchKernelGGL((tree_stream_kernel<DT, TD_TYPICAL>), dim3(blocks_for(Q.n_gather + P.n_stream)), dim3(BLOCK),
+                       0, s, Q);
     if (launch_status() != SV_OK) return SV_EHIP;
-    hipLaunchKernelGGL((tree_walk_kernel<DT, WM_TYPICAL, 512>), dim3((unsigned)P.B), dim3(512), smem, s, P);
+    hipLaunchKernelGGL((tree_walk_kernel<DT, WM_TYPICAL, 512>), dim3((unsigned)P.B), dim3(512), smem, s, Q);
     return launch_status();
   }
 };
@@ -1449,7 +1494,9 @@ sv_status tree_setup(TreeParams& P, size_t& smem, bool stoch, float temperature,
   P.nstat = reinterpret_cast<NodeStat*>(ws + lay.off[3]);
   P.yrec = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
   P.tree_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[5]);
+  P.xl = reinterpret_cast<float*>(ws + lay.off[6]);
   P.wave_walk = false;
+  P.n_gather = 0;
   P.B = B;
   P.N = n_nodes;
   P.V = V;
@@ -1562,8 +1609,8 @@ sv_status spec_verify_tree_typical(float temperature, double epsilon, double del
                                   cand_tokens, target_logits, uniforms, max_depth, accept_len, path_nodes,
                                   out_tokens, err_flags, workspace, workspace_bytes);
   if (st != SV_OK || B == 0) return st;
-  P.eps = epsilon;
-  P.delta = delta;
+  P.l2eps = epsilon > 0.0 ? std::log2(epsilon) : -INFINITY;
+  P.l2delta = delta > 0.0 ? std::log2(delta) : -INFINITY;
   return dispatch<TypicalLauncher>(dtype, false, P, smem, reinterpret_cast<hipStream_t>(stream));
 }
 
