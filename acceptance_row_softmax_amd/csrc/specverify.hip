@@ -161,6 +161,7 @@ struct LinearParams {
   uint32_t* errw;       // [B]      error bits per sequence
   int64_t B, k, V;
   int C, CP, R;         // chunks per row, streaming waves per row (C rounded up to 4), rows per sequence
+  int G;                // chunks per residual wave (1 or 2; the kernel's template argument)
   float c0;
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
@@ -492,14 +493,14 @@ __device__ __forceinline__ void linear_stream_wave(const LinearParams& P, uint32
   linear_combine<DT, STOCH>(P, q, b, i, which);
 }
 
-// Residual wave (b, c), dispatched after every streaming wave: waits for the
-// decision of sequence b; if a draft was rejected, sums the residual over chunk c
-// of rows t_L, d_L. The sequence's last residual wave picks the chunk holding u*S,
-// scans it and records the token.
-template <int DT>
-__device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int64_t b, int64_t c) {
+// Residual wave (b, g), dispatched after every streaming wave: waits for the
+// decision of sequence b; if a draft was rejected, sums the residual over chunks
+// G g ... G g + G - 1 of rows t_L, d_L. The sequence's last residual wave picks
+// the chunk holding u*S, scans it and records the token.
+template <int DT, int G>
+__device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
   const int lane = lane_id();
-  const uint32_t C = (uint32_t)P.C;
+  const uint32_t CG = (uint32_t)((P.C + G - 1) / G);   // residual waves per sequence
   const int64_t k = P.k;
   Decision d;
   d.L = 0;
@@ -519,17 +520,29 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);
   if (d.kind == 1) {
-    Raw rt, rd;
-    load_chunk<DT>(trow, P.V, c, rt);
-    load_chunk<DT>(drow, P.V, c, rd);
-    ResPart r;
-    r.s = residual_raw_sum<DT>(rt, rd, rw);
-    if (lane == 0) put_rec(P.res + (b * P.C + c) * RES_WORDS, r, P.tag);
+    if constexpr (G == 1) {
+      Raw rt, rd;
+      load_chunk<DT>(trow, P.V, g, rt);
+      load_chunk<DT>(drow, P.V, g, rd);
+      ResPart r;
+      r.s = residual_raw_sum<DT>(rt, rd, rw);
+      if (lane == 0) put_rec(P.res + (b * P.C + g) * RES_WORDS, r, P.tag);
+    } else {
+#pragma unroll 1
+      for (int64_t c = g * G; c < min(g * G + G, (int64_t)P.C); ++c) {
+        Raw rt, rd;
+        load_chunk<DT>(trow, P.V, c, rt);
+        load_chunk<DT>(drow, P.V, c, rd);
+        ResPart r;
+        r.s = residual_raw_sum<DT>(rt, rd, rw);
+        if (lane == 0) put_rec(P.res + (b * P.C + c) * RES_WORDS, r, P.tag);
+      }
+    }
   }
   uint32_t old = 0;
   if (lane == 0) old = counter_add(P.res_cnt + b * CSTRIDE, 1u);
   old = bcast(old);
-  if (old + 1 != C) return;
+  if (old + 1 != CG) return;
   // last residual wave of the sequence: draw the correction token
   if (lane == 0) {
     counter_reset(P.res_cnt + b * CSTRIDE);
@@ -593,6 +606,8 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
   linear_event<DT, true>(P, b, true, y);
 }
 
+constexpr int64_t RESID_GROUP_WAVES = 4096;
+
 // Wave roles of a linear launch: the streaming waves (rows in order, see
 // stream_coords), then in stochastic mode with k > 0 one residual wave per
 // (sequence, chunk). Residual waves follow every row their decision depends on.
@@ -601,7 +616,7 @@ struct Role {
   uint32_t q, b, c;
 };
 
-template <bool STOCH>
+template <bool STOCH, int G>
 __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
   Role r;
   r.kind = 0;
@@ -614,22 +629,23 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
     r.kind = r.c < C ? 1 : 0;
   } else {
     const uint32_t v = w - RQ * CP;
-    r.b = v / C;
-    r.c = v - r.b * C;
+    const uint32_t CG = (C + G - 1) / G;
+    r.b = v / CG;
+    r.c = v - r.b * CG;
     r.kind = 2;
   }
   return r;
 }
 
-template <int DT, bool STOCH>
+template <int DT, bool STOCH, int G>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void linear_kernel(LinearParams P) {
   const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
   if (w >= P.n_waves) return;
-  const Role r = linear_role<STOCH>(P, (uint32_t)w);
+  const Role r = linear_role<STOCH, G>(P, (uint32_t)w);
   if (r.kind == 1) {
     linear_stream_wave<DT, STOCH>(P, r.q, r.c);
   } else if (r.kind == 2) {
-    if constexpr (STOCH) linear_residual_wave<DT>(P, r.b, r.c);
+    if constexpr (STOCH) linear_residual_wave<DT, G>(P, r.b, r.c);
   }
 }
 
@@ -1355,7 +1371,13 @@ Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
 template <int DT, bool STOCH>
 struct LinearLauncher {
   static sv_status run(const LinearParams& P, hipStream_t s) {
-    hipLaunchKernelGGL((linear_kernel<DT, STOCH>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
+    if constexpr (STOCH) {
+      if (P.G == 2) {
+        hipLaunchKernelGGL((linear_kernel<DT, true, 2>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
+        return launch_status();
+      }
+    }
+    hipLaunchKernelGGL((linear_kernel<DT, STOCH, 1>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
     return launch_status();
   }
 };
@@ -1456,7 +1478,10 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.C = (int)chunks_per_row(V, dtype);
   P.CP = (P.C + WPB - 1) / WPB * WPB;
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  P.n_waves = B * P.R * P.CP + ((stoch && k > 0) ? B * P.C : 0);
+  // residual waves: one per chunk, or one per two chunks when a launch would have
+  // more than RESID_GROUP_WAVES of them (then their dispatch sets the time)
+  P.G = (stoch && B * P.C > RESID_GROUP_WAVES) ? 2 : 1;
+  P.n_waves = B * P.R * P.CP + ((stoch && k > 0) ? B * ((P.C + P.G - 1) / P.G) : 0);
   if (P.n_waves > MAX_WAVES) return SV_ELIMIT;
   P.commit = false;
   P.tag = next_tag();

@@ -58,6 +58,14 @@ def test_long_rows(V, mode):
     _check(w)
 
 
+def test_grouped_residual_waves_odd_chunks():
+    # more than 4096 (sequence, chunk) pairs: each residual wave sums two chunks;
+    # V = 20000 bf16 rows have 5 chunks, so every sequence's last wave has one
+    w = gen.linear_draft_target(97, 0, 1000, 1, 20000, gen.DT_BF16, 3.0, 1.0, "stochastic", 1.0, "grouped")
+    g, o, near, n_eval = _check(w)
+    assert 0.1 < np.mean(g["accept_len"] == 0) < 0.9
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_c2_draft_target_full_size(seed):
     w = gen.c2_linear(seed)            # B=32, k=4, V=128256, bf16, T=0.7
