@@ -581,17 +581,37 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
     if (__ballot(!ok)) {
       y = -2;
     } else {
+      // The draw from the residual. With no residual mass (the rows agree up to
+      // rounding) it is taken from p_t,L instead: the same pick and scan with the
+      // draft's weights zeroed (and taken from row t_L, so that they stay finite),
+      // over chunk sums formed here.
+      ResidW rx = rw;
+      const char* dx = drow;
       double tot = 0.0;
 #pragma unroll
       for (int t = 0; t < MAX_ROUNDS; ++t) tot += wl[t];
       tot = wave_sum(tot);
-      const ChunkPick pk = pick_chunk(P.C, (double)u, wl);
+      ChunkPick pk = pick_chunk(P.C, (double)u, wl);
+      if (pk.c < 0 && tot == 0.0) {
+        rx.mc0d = rx.mc0t;
+        rx.izd = 0.0f;
+        dx = trow;
+#pragma unroll
+        for (int t = 0; t < MAX_ROUNDS; ++t) wl[t] = 0.0;
+#pragma unroll 1
+        for (int c = 0; c < P.C; ++c) {
+          Raw rt;
+          load_chunk<DT>(trow, P.V, c, rt);
+          const double sc = residual_raw_sum<DT>(rt, rt, rx);
+#pragma unroll
+          for (int t = 0; t < MAX_ROUNDS; ++t)
+            if (t * WAVE + lane == c) wl[t] = sc;
+        }
+        pk = pick_chunk(P.C, (double)u, wl);
+      }
       if (pk.c >= 0) {
         const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
-        y = residual_chunk_draw<DT>(trow, drow, P.V, pk.c, rw, th);
-      } else if (tot == 0.0) {
-        // no residual mass (rows equal up to rounding): draw from p_t,L instead
-        y = softmax_draw_streamed<DT>(trow, P.V, P.C, P.c0, u);
+        y = residual_chunk_draw<DT>(trow, dx, P.V, pk.c, rx, th);
       }
     }
     if (last) {

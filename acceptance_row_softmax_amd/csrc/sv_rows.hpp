@@ -119,34 +119,4 @@ __device__ __forceinline__ int softmax_draw(const char* row, int64_t V, int C, f
   return (int)y;
 }
 
-// The same draw when no partials are at hand: the wave streams the row once to
-// build them (used only for the residual of two rows equal up to rounding).
-template <int DT>
-__device__ __forceinline__ int softmax_draw_streamed(const char* row, int64_t V, int C, float c0, float u) {
-  const int lane = lane_id();
-  RowParts rp;
-#pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
-    rp.m[t] = -INFINITY;
-    rp.idx[t] = INT_SENTINEL;
-    rp.s[t] = 0.0;
-  }
-#pragma unroll 1
-  for (int c = 0; c < C; ++c) {
-    const Partial p = chunk_partial<DT, true, false>(row, V, c, c0);
-    const int t = c / WAVE;
-#pragma unroll
-    for (int q = 0; q < MAX_ROUNDS; ++q)
-      if (q == t && lane == c % WAVE) {
-        rp.m[q] = p.m;
-        rp.s[q] = p.s;
-      }
-  }
-  rp.got = true;
-  double wl[MAX_ROUNDS];
-  const RowSums rs = row_sums<true>(rp, c0, wl);
-  if (!(rs.Z > 0.0) || !__builtin_isfinite(rs.Z)) return -1;
-  return softmax_draw<DT>(row, V, C, c0, u, rp, rs, wl);
-}
-
 }  // namespace sv

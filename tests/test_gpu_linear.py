@@ -58,6 +58,30 @@ def test_long_rows(V, mode):
     _check(w)
 
 
+def test_zero_residual_falls_back_to_the_target_row():
+    # One dominant logit, equal in target and draft; every other draft logit is
+    # 0.5 above the target's, so the draft token is rejected when u >= about 0.61.
+    # In fp32 every residual term rounds to zero (the dominant probabilities agree
+    # to about 1e-10), so the draw falls back to softmax of the target row. The
+    # exact residual (the oracle) has all its mass on the dominant token, which the
+    # fallback draws too unless u lands in a tail of about 1e-10.
+    B, k, V = 16, 2, 3000
+    rng = np.random.default_rng(5)
+    dom = rng.integers(0, V, size=(B, k + 1))
+    t = np.zeros((B, k + 1, V))
+    d = np.full((B, k, V), 0.5)
+    t[np.arange(B)[:, None], np.arange(k + 1)[None, :], dom] = 30.0
+    d[np.arange(B)[:, None], np.arange(k)[None, :], dom[:, :k]] = 30.0
+    tok = (dom[:, :k] + 1 + rng.integers(0, V - 1, size=(B, k))) % V
+    u = np.full((B, k + 1), 0.9, np.float32)
+    u[:, k] = rng.random(B).astype(np.float32)
+    w = gen.LinearWorkload("zero-residual", "stochastic", 1.0, B, k, V, gen.DT_F32, t.astype(np.float32),
+                           d.astype(np.float32), tok.astype(np.int32), u)
+    g, o, near, n_eval = _check(w)
+    assert np.all(g["accept_len"] == 0)
+    np.testing.assert_array_equal(g["out_tokens"][:, 0], dom[:, 0])
+
+
 def test_grouped_residual_waves_odd_chunks():
     # more than 4096 (sequence, chunk) pairs: each residual wave sums two chunks;
     # V = 20000 bf16 rows have 5 chunks, so every sequence's last wave has one
