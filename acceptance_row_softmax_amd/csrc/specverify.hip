@@ -290,16 +290,26 @@ __device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b, in
   emit_store<DT, STOCH>(P, b, in, known_y);
 }
 
-// Counts one event of sequence b (R row combines and the final token); the last
+// Events a wave counts when it is done: n of sequence b (n = 0: none), the final
+// token among them if `token`. Every role returns its events to the kernel body,
+// which counts them at one place.
+struct Ev {
+  int64_t b;
+  uint32_t n;
+  bool token;
+  int y;
+};
+
+// Counts n events of sequence b (R row combines and the final token); the last
 // one writes the outputs. The token event carries the token: if it is not the
 // last event, the token goes to the token record for the wave that will be.
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, bool token = false, int y = 0) {
+__device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, bool token, int y, uint32_t n) {
   const uint32_t total = (uint32_t)P.R + 1u;
   uint32_t old = 0;
-  if (lane_id() == 0) old = counter_add(P.fin + b * CSTRIDE, 1u);
+  if (lane_id() == 0) old = counter_add(P.fin + b * CSTRIDE, n);
   old = bcast(old);
-  if (old + 1 != total) {
+  if (old + n != total) {
     if (token && lane_id() == 0) {
       Token t;
       t.y = y;
@@ -314,16 +324,17 @@ __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, b
 // Called after the state update old -> now by the wave that combined row
 // (mi, mwhich) with statistics `mine`. If this update settles L: in stochastic
 // mode with L < k, hand rows t_L, d_L to the residual waves; otherwise the final
-// token is known (the bonus draw, or argmax of t_L in greedy mode): record it.
-template <int DT, bool STOCH>
+// token is known (the bonus draw, or argmax of t_L in greedy mode): return true
+// with it in y_out, for the caller to count with its own event.
 // `other` (lane 0, when have_other): the statistics of the other row of position
 // mi, which the pair combine has just read.
-__device__ __forceinline__ void linear_settle(const LinearParams& P, int64_t b, uint64_t old, uint64_t now,
+template <int DT, bool STOCH>
+__device__ __forceinline__ bool linear_settle(const LinearParams& P, int64_t b, uint64_t old, uint64_t now,
                                               const RowStat& mine, int64_t mi, int mwhich,
-                                              const RowStat& other, bool have_other, bool other_got) {
+                                              const RowStat& other, bool have_other, bool other_got, int& y_out) {
   const int k = (int)P.k;
   const int Ln = settled_L(now, k);
-  if (Ln < 0 || settled_L(old, k) >= 0) return;
+  if (Ln < 0 || settled_L(old, k) >= 0) return false;
   const bool here = mi == Ln;
   RowStat tl = mine;
   bool got = true;
@@ -355,7 +366,7 @@ __device__ __forceinline__ void linear_settle(const LinearParams& P, int64_t b, 
       d.Zd = dl.Z;
       put_rec(P.dec + b * DEC_WORDS, d, P.tag);
     }
-    return;   // the residual waves draw the token
+    return false;   // the residual waves draw the token
   }
   int y = 0;
   if (lane_id() == 0) {
@@ -369,12 +380,13 @@ __device__ __forceinline__ void linear_settle(const LinearParams& P, int64_t b, 
       put_rec(P.dec + b * DEC_WORDS, d, P.tag);
     }
   }
-  linear_event<DT, STOCH>(P, b, true, bcast(y));   // the final token
+  y_out = bcast(y);
+  return true;   // the final token is known
 }
 
 // Combines row q (b, position i, target/draft) once its last chunk is done.
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q, int64_t b, int64_t i, int which) {
+__device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, int64_t b, int64_t i, int which) {
   const int lane = lane_id();
   const int64_t k = P.k, V = P.V;
   const char* row = row_ptr<DT, STOCH>(P, b, i, which);
@@ -446,17 +458,25 @@ __device__ __forceinline__ void linear_combine(const LinearParams& P, int64_t q,
       bits = bcast(bits);
     }
   }
+  Ev ev;
+  ev.b = b;
+  ev.n = 1;   // the row's combine
+  ev.token = false;
+  ev.y = 0;
   if (update) {
     uint64_t olds = 0;
     if (lane == 0) olds = state_or(P.state + b * SSTRIDE, bits);
     olds = bcast(olds);
-    linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which, other, have_other, other_got);
+    if (linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which, other, have_other, other_got, ev.y)) {
+      ev.token = true;   // and the final token
+      ev.n = 2;
+    }
   }
-  linear_event<DT, STOCH>(P, b);
+  return ev;
 }
 
 template <int DT, bool STOCH>
-__device__ __forceinline__ void linear_stream_wave(const LinearParams& P, uint32_t q32, uint32_t c32) {
+__device__ __forceinline__ Ev linear_stream_wave(const LinearParams& P, uint32_t q32, uint32_t c32) {
   const int64_t q = q32, c = c32;
   int64_t b, i;
   int which;
@@ -488,9 +508,9 @@ __device__ __forceinline__ void linear_stream_wave(const LinearParams& P, uint32
     old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
   }
   old = bcast(old);
-  if (old + 1 != (uint32_t)P.C) return;
+  if (old + 1 != (uint32_t)P.C) return Ev{0, 0u, false, 0};
   if (lane_id() == 0) counter_reset(P.row_cnt + q * CSTRIDE);
-  linear_combine<DT, STOCH>(P, q, b, i, which);
+  return linear_combine<DT, STOCH>(P, q, b, i, which);
 }
 
 // Residual wave (b, g), dispatched after every streaming wave: waits for the
@@ -498,7 +518,7 @@ __device__ __forceinline__ void linear_stream_wave(const LinearParams& P, uint32
 // G g ... G g + G - 1 of rows t_L, d_L. The sequence's last residual wave picks
 // the chunk holding u*S, scans it and records the token.
 template <int DT, int G>
-__device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
+__device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
   const int lane = lane_id();
   const uint32_t CG = (uint32_t)((P.C + G - 1) / G);   // residual waves per sequence
   const int64_t k = P.k;
@@ -542,13 +562,13 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
   uint32_t old = 0;
   if (lane == 0) old = counter_add(P.res_cnt + b * CSTRIDE, 1u);
   old = bcast(old);
-  if (old + 1 != CG) return;
+  if (old + 1 != CG) return Ev{0, 0u, false, 0};
   // last residual wave of the sequence: draw the correction token
   if (lane == 0) {
     counter_reset(P.res_cnt + b * CSTRIDE);
     clear_rec<Decision>(P.dec + b * DEC_WORDS);
   }
-  if (d.kind == 0) return;   // no draft rejected: the bonus token is recorded already
+  if (d.kind == 0) return Ev{0, 0u, false, 0};   // no draft rejected: the bonus token is recorded already
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind == 1) {
     // The token event counts before the draw: if it is the sequence's last event,
@@ -621,9 +641,9 @@ __device__ __forceinline__ void linear_residual_wave(const LinearParams& P, int6
       t.y = y;
       put_rec(P.tok + b, t, P.tag);
     }
-    return;
+    return Ev{0, 0u, false, 0};
   }
-  linear_event<DT, true>(P, b, true, y);
+  return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
 }
 
 constexpr int64_t RESID_GROUP_WAVES = 4096;
@@ -662,11 +682,13 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
   const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
   if (w >= P.n_waves) return;
   const Role r = linear_role<STOCH, G>(P, (uint32_t)w);
+  Ev ev{0, 0u, false, 0};
   if (r.kind == 1) {
-    linear_stream_wave<DT, STOCH>(P, r.q, r.c);
+    ev = linear_stream_wave<DT, STOCH>(P, r.q, r.c);
   } else if (r.kind == 2) {
-    if constexpr (STOCH) linear_residual_wave<DT, G>(P, r.b, r.c);
+    if constexpr (STOCH) ev = linear_residual_wave<DT, G>(P, r.b, r.c);
   }
+  if (ev.n) linear_event<DT, STOCH>(P, ev.b, ev.token, ev.y, ev.n);
 }
 
 // ------------------------------------------------------------------ trees
