@@ -710,6 +710,7 @@ struct TreeParams {
   bool wave_walk;       // trees of at most WAVE_WALK_NODES nodes, tokens known while streaming
   float* xl;            // [B][N] typical acceptance: each candidate's logit in its parent's row
   int64_t n_gather;     // typical acceptance: waves that gather xl, ahead of the streaming waves
+  bool row_waves;       // one streaming wave per row (large batches), else one per (row, chunk)
   struct NodeStat* nstat;   // [B][N] typical acceptance: each node's softmax statistics
   int64_t B, N, V, max_depth;
   int C, CP;
@@ -744,9 +745,55 @@ static_assert(RecWords<EntPartial>::N == PART_WORDS, "entropy partials use the p
 
 // Typical acceptance, streaming wave of row q, chunk c: the chunk's entropy
 // partial; the row's last chunk combines them into the node's statistics.
-template <int DT>
-__device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const char* row, int64_t q, int64_t c) {
+// One wave streams all C chunks of a row, two in flight at a time, and hands each
+// chunk's partial (the same in every lane) to put(c, partial): the row waves of
+// large tree batches, which need neither partial records nor arrival counters.
+template <int DT, class Reduce, class Put>
+__device__ __forceinline__ void row_chunks(const char* row, int64_t V, int C, Reduce reduce, Put put) {
+  Raw ra, rb;
+  Chunk ka = load_chunk<DT>(row, V, 0, ra);
+#pragma unroll 1
+  for (int c = 0; c < C; c += 2) {
+    Chunk kb;
+    if (c + 1 < C) kb = load_chunk<DT>(row, V, c + 1, rb);
+    put(c, reduce(ka, ra));
+    if (c + 2 < C) ka = load_chunk<DT>(row, V, c + 2, ra);
+    if (c + 1 < C) put(c + 1, reduce(kb, rb));
+  }
+}
+
+// Typical acceptance: the entropy partials of row q, lane l holding chunks
+// l + 64 t: from the records of its chunk waves (by the last of them; false for
+// the others), or streamed by a row wave.
+struct EntParts {
+  float m[MAX_ROUNDS];
+  double sv[MAX_ROUNDS], s1[MAX_ROUNDS];
+  bool got;
+};
+
+template <int DT, bool ROWS>
+__device__ __forceinline__ bool tree_typical_parts(const TreeParams& P, const char* row, int64_t q, int64_t c,
+                                                   EntParts& ep) {
   const int lane = lane_id();
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    ep.m[t] = -INFINITY;
+    ep.sv[t] = ep.s1[t] = 0.0;
+  }
+  ep.got = true;
+  if constexpr (ROWS) {
+    row_chunks<DT>(row, P.V, P.C, [&](const Chunk&, const Raw& r) { return chunk_reduce_ent<DT>(r, P.c0); },
+                   [&](int cc, const EntPartial& e) {
+#pragma unroll
+                     for (int t = 0; t < MAX_ROUNDS; ++t)
+                       if (t * WAVE + lane == cc) {
+                         ep.m[t] = e.m;
+                         ep.sv[t] = e.s;
+                         ep.s1[t] = e.s1;
+                       }
+                   });
+    return true;
+  } else {
   Raw r;
   load_chunk<DT>(row, P.V, c, r);
   const EntPartial p = chunk_reduce_ent<DT>(r, P.c0);
@@ -755,13 +802,9 @@ __device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const c
     put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
     old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
   }
-  if (bcast(old) + 1 != (uint32_t)P.C) return;
+  if (bcast(old) + 1 != (uint32_t)P.C) return false;
   if (lane == 0) counter_reset(P.row_cnt + q * CSTRIDE);
-  // lane l holds chunks l + 64 t
-  float m[MAX_ROUNDS];
-  double sv[MAX_ROUNDS], s1[MAX_ROUNDS];
   bool got = true;
-  float M = -INFINITY;
 #pragma unroll
   for (int t = 0; t < MAX_ROUNDS; ++t) {
     EntPartial e;
@@ -773,26 +816,35 @@ __device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const c
       got = get_rec(rec, e, P.tag) && got;
       clear_rec<EntPartial>(rec);
     }
-    m[t] = e.m;
-    sv[t] = e.s;
-    s1[t] = e.s1;
-    M = fmaxf(M, e.m);
+    ep.m[t] = e.m;
+    ep.sv[t] = e.s;
+    ep.s1[t] = e.s1;
   }
+  ep.got = __ballot(!got) == 0ull;
+  return true;
+  }
+}
+
+// Typical acceptance: the node's statistics from its entropy partials.
+__device__ __forceinline__ void tree_typical_combine(const TreeParams& P, int64_t q, const EntParts& ep) {
+  const int lane = lane_id();
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) M = fmaxf(M, ep.m[t]);
   M = wave_max(M);
   const double Mc0 = (double)M * (double)P.c0;
   double Z = 0.0, S1 = 0.0;
 #pragma unroll
   for (int t = 0; t < MAX_ROUNDS; ++t) {
-    if (m[t] == -INFINITY) continue;
+    if (ep.m[t] == -INFINITY) continue;
     // chunk weights are relative to fl32(m*c0): bring them to the row max
-    const double f = pow2_neg((double)chunk_mc0(m[t], P.c0) - Mc0);
+    const double f = pow2_neg((double)chunk_mc0(ep.m[t], P.c0) - Mc0);
     // exponents relative to the row: t_v + (fl32(m*c0) - M*c0)
-    Z += sv[t] * f;
-    S1 += (s1[t] + ((double)chunk_mc0(m[t], P.c0) - Mc0) * sv[t]) * f;
+    Z += ep.sv[t] * f;
+    S1 += (ep.s1[t] + ((double)chunk_mc0(ep.m[t], P.c0) - Mc0) * ep.sv[t]) * f;
   }
   Z = wave_sum(Z);
   S1 = wave_sum(S1);   // sum_v w_v (x_v - M) c0
-  const bool all = __ballot(!got) == 0ull;
   NodeStat st;
   st.M = M;
   // log2(Z) from Z = m 2^e, m in [0.5, 1): e + log2(m), the fraction's log2 in fp32
@@ -806,7 +858,7 @@ __device__ __forceinline__ void tree_typical_stream(const TreeParams& P, const c
   st.ok = usable ? 1 : 0;
   if (lane == 0) {
     P.nstat[q] = st;
-    P.node_y[q] = !all ? -2 : (usable ? 0 : -1);
+    P.node_y[q] = !ep.got ? -2 : (usable ? 0 : -1);
   }
 }
 
@@ -979,7 +1031,9 @@ __device__ __forceinline__ void tree_gather_candidates(const TreeParams& P, int6
   P.xl[t] = x;
 }
 
-template <int DT, int TD>
+// ROWS: one wave per row (P.row_waves), a separate instantiation so that the
+// chunk waves keep their own register budget.
+template <int DT, int TD, bool ROWS>
 __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
   constexpr int E = DTraits<DT>::E;
   constexpr bool STOCH = TD != TD_ARGMAX;
@@ -992,26 +1046,56 @@ __global__ __launch_bounds__(BLOCK) void tree_stream_kernel(TreeParams P) {
     w -= P.n_gather;
   }
   if (w >= P.n_stream) return;
-  const uint32_t C = (uint32_t)P.C;
-  uint32_t q32, c32;
-  stream_coords((uint32_t)w, (uint32_t)P.CP, (uint32_t)(P.B * P.N), q32, c32);
-  if (c32 >= C) return;   // padding wave
-  const int64_t q = q32, c = c32;
+  // row waves: wave w streams row w; chunk waves: see stream_coords
+  int64_t q = w, c = 0;
+  if constexpr (!ROWS) {
+    uint32_t q32, c32;
+    stream_coords((uint32_t)w, (uint32_t)P.CP, (uint32_t)(P.B * P.N), q32, c32);
+    if (c32 >= (uint32_t)P.C) return;   // padding wave
+    q = q32;
+    c = c32;
+  }
   const char* row = P.logits + (q * P.V) * E;
   if constexpr (TD == TD_TYPICAL) {
-    tree_typical_stream<DT>(P, row, q, c);
+    EntParts ep;
+    if (tree_typical_parts<DT, ROWS>(P, row, q, c, ep)) tree_typical_combine(P, q, ep);
     return;
   }
-  const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c, P.c0);
-  uint32_t old = 0;
-  if (lane_id() == 0) {
-    put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
-    old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
+  RowParts rp;
+  if constexpr (ROWS) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int t = 0; t < MAX_ROUNDS; ++t) {
+      rp.m[t] = -INFINITY;
+      rp.idx[t] = INT_SENTINEL;
+      rp.s[t] = 0.0;
+    }
+    rp.got = true;
+    rp.xin = false;
+    rp.xv = 0.0f;
+    row_chunks<DT>(row, P.V, P.C,
+                   [&](const Chunk& k, const Raw& r) { return chunk_reduce<DT, STOCH, !STOCH>(k, r, P.c0, -1); },
+                   [&](int cc, const Partial& p) {
+#pragma unroll
+                     for (int t = 0; t < MAX_ROUNDS; ++t)
+                       if (t * WAVE + lane == cc) {
+                         rp.m[t] = p.m;
+                         rp.idx[t] = p.idx;
+                         rp.s[t] = p.s;
+                       }
+                   });
+  } else {
+    const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c, P.c0);
+    uint32_t old = 0;
+    if (lane_id() == 0) {
+      put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
+      old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
+    }
+    old = bcast(old);
+    if (old + 1 != (uint32_t)P.C) return;
+    if (lane_id() == 0) counter_reset(P.row_cnt + q * CSTRIDE);
+    rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
   }
-  old = bcast(old);
-  if (old + 1 != C) return;
-  if (lane_id() == 0) counter_reset(P.row_cnt + q * CSTRIDE);
-  const RowParts rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
   double wl[MAX_ROUNDS];
   const RowSums rs = row_sums<STOCH>(rp, P.c0, wl);
   // the node's token (TD_LAZY: 0 for a usable row); -1 an unusable row, -2 a
@@ -1434,11 +1518,17 @@ struct TreeLauncher {
     TreeParams Q = P;
     Q.wave_walk = (!STOCH || eager) && P.N <= WAVE_WALK_NODES;
     if (!STOCH) {
-      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_ARGMAX>), grid, dim3(BLOCK), 0, s, Q);
+      if (P.row_waves)
+        hipLaunchKernelGGL((tree_stream_kernel<DT, TD_ARGMAX, true>), grid, dim3(BLOCK), 0, s, Q);
+      else
+        hipLaunchKernelGGL((tree_stream_kernel<DT, TD_ARGMAX, false>), grid, dim3(BLOCK), 0, s, Q);
     } else if (eager) {
-      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_EAGER>), grid, dim3(BLOCK), 0, s, Q);
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_EAGER, false>), grid, dim3(BLOCK), 0, s, Q);
     } else {
-      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_LAZY>), grid, dim3(BLOCK), 0, s, Q);
+      if (P.row_waves)
+        hipLaunchKernelGGL((tree_stream_kernel<DT, TD_LAZY, true>), grid, dim3(BLOCK), 0, s, Q);
+      else
+        hipLaunchKernelGGL((tree_stream_kernel<DT, TD_LAZY, false>), grid, dim3(BLOCK), 0, s, Q);
     }
     if (launch_status() != SV_OK) return SV_EHIP;
     if (Q.wave_walk) return SV_OK;   // the streaming launch has walked every tree
@@ -1458,8 +1548,12 @@ struct TypicalLauncher {
     // that the streaming waves keep their XCD placement
     TreeParams Q = P;
     Q.n_gather = ((P.B * P.N + WAVE - 1) / WAVE + 8 * WPB - 1) / (8 * WPB) * (8 * WPB);
-    hipLaunchKernelGGL((tree_stream_kernel<DT, TD_TYPICAL>), dim3(blocks_for(Q.n_gather + P.n_stream)), dim3(BLOCK),
-                       0, s, Q);
+    if (P.row_waves)
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_TYPICAL, true>), dim3(blocks_for(Q.n_gather + P.n_stream)),
+                         dim3(BLOCK), 0, s, Q);
+    else
+      hipLaunchKernelGGL((tree_stream_kernel<DT, TD_TYPICAL, false>), dim3(blocks_for(Q.n_gather + P.n_stream)),
+                         dim3(BLOCK), 0, s, Q);
     if (launch_status() != SV_OK) return SV_EHIP;
     hipLaunchKernelGGL((tree_walk_kernel<DT, WM_TYPICAL, 512>), dim3((unsigned)P.B), dim3(512), smem, s, Q);
     return launch_status();
@@ -1571,8 +1665,10 @@ sv_status tree_setup(TreeParams& P, size_t& smem, bool stoch, float temperature,
   P.C = (int)chunks_per_row(V, dtype);
   P.CP = (P.C + WPB - 1) / WPB * WPB;
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  P.n_stream = B * n_nodes * P.CP;
-  if (P.n_stream > MAX_WAVES || B > 0x7fffffffLL) return SV_ELIMIT;
+  // more rows than one launch of chunk waves fills the chip with: one wave per row
+  P.row_waves = B * n_nodes > TREE_EAGER_ROWS;
+  P.n_stream = P.row_waves ? B * n_nodes : B * n_nodes * P.CP;
+  if (B * n_nodes * P.CP > MAX_WAVES || B > 0x7fffffffLL) return SV_ELIMIT;
   P.tag = next_tag();
   // LDS of the path search: parent (2 B) + match flag (1 B) per node
   smem = (size_t)((3 * n_nodes + 15) & ~(int64_t)15);

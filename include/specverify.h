@@ -74,7 +74,9 @@
  *      bit3 SV_ERR_INTERNAL a wait between workgroups of the launch gave up (after
  *                          2^18 polls, a fraction of a second: only if the GPU did
  *                          not run the launch's workgroups in dispatch order, or a
- *                          concurrent call shared the workspace); outputs are not valid
+ *                          concurrent call shared the workspace); outputs are not
+ *                          valid, and a wait that gave up can also leave other
+ *                          sequences of that launch unwritten
  *      bit4 SV_ERR_CAPACITY  (commit) the history buffer cannot take the new tokens
  *      bit5 SV_ERR_UNVERIFIED (commit) the sequence's verification reported an error
  */

@@ -207,11 +207,13 @@ def test_tree_mask_deep_chain_max_nodes():
 
 
 # ------------------------------------------------------------------ verify + commit in one launch
-@pytest.mark.parametrize("case", ["c2", "small_k0", "small_greedy", "full_histories"])
+@pytest.mark.parametrize("case", ["c2", "c3_stochastic", "small_k0", "small_greedy", "full_histories"])
 def test_fused_commit_equals_verify_then_commit(case):
     import torch
     if case == "c2":
         w = gen.c2_linear(1)
+    elif case == "c3_stochastic":
+        w = gen.c3_mtp(1, "stochastic")     # 8192 (sequence, chunk) pairs: two chunks per residual wave
     elif case == "small_k0":
         w = gen.linear_draft_target(65, 0, 40, 0, 5000, gen.DT_F16, 2.0, 0.5, "stochastic", 0.9, "k0")
     else:

@@ -172,3 +172,38 @@ def test_random_trees_at_the_wave_walk_bound(n, mode):
     assert g["accept_len"].max() >= 3
     g2, _, _, _ = _check(w, max_depth=int(depth.max()) - 1)
     assert np.all(g2["err_flags"] & 4)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "stochastic", "typical"])
+def test_row_waves_large_batch_ragged_rows(mode):
+    # More than 4096 rows in a batch: one wave streams each row, two chunks in
+    # flight. bf16 rows of V = 20001 have five chunks (an odd count, the last one
+    # ragged). Two random recursive trees of 2100 nodes, dominant tokens so that
+    # paths several levels deep are accepted.
+    import dataclasses
+    import oracle
+    rng = np.random.default_rng(21)
+    n, B, V = 2100, 2, 20001
+    parent = np.array([-1] + [rng.integers(0, i) for i in range(1, n)], np.int32)
+    depth = np.zeros(n, np.int64)
+    for i in range(1, n):
+        depth[i] = depth[parent[i]] + 1
+    dom = rng.integers(0, V, size=(B, n))
+    x = rng.normal(0.0, 1.0, size=(B, n, V)).astype(np.float32)
+    x[np.arange(B)[:, None], np.arange(n)[None, :], dom] += 20.0
+    logits = gen.round_to(gen.DT_BF16, x)
+    cand = np.where(rng.random((B, n)) < 0.8, dom[:, parent], rng.integers(0, V, (B, n))).astype(np.int32)
+    cand[:, 0] = -1
+    u = gen.uniforms(gen.key(65, n, 1), B * n).reshape(B, n)
+    w = gen.TreeWorkload("rowwaves", "greedy" if mode == "greedy" else "stochastic", 1.0, B, n, V, gen.DT_BF16,
+                         parent, cand, logits, u, int(depth.max()))
+    if mode != "typical":
+        g, o, _, _ = _check(w)
+    else:
+        G.say(f"typical rowwaves B={B} N={n} V={V}")
+        g = G.run_tree(dataclasses.replace(w, mode="typical"), None, epsilon=0.09, delta=0.3)
+        o = oracle.verify_tree_typical(1.0, 0.09, 0.3, parent, cand, logits, u, V, gen.DT_BF16, w.max_depth,
+                                       G.TIE_EPS)
+        G.compare_tree(g, o)
+    assert np.all(g["err_flags"] == 0)
+    assert g["accept_len"].max() >= 2
