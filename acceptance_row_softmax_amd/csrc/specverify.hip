@@ -128,7 +128,6 @@ __device__ __forceinline__ double residual_raw_sum(const Raw& rt, const Raw& rd,
 template <int DT>
 __device__ __forceinline__ int residual_chunk_draw(const char* trow, const char* drow, int64_t V, int64_t c,
                                                    const ResidW& rw, double th) {
-  constexpr int W = DTraits<DT>::W;
   Raw rt, rd;
   const Chunk kt = load_chunk<DT>(trow, V, c, rt);
   load_chunk<DT>(drow, V, c, rd);

@@ -98,7 +98,6 @@ __device__ __forceinline__ RowSums row_sums(const RowParts& rp, float c0, double
 template <int DT>
 __device__ __forceinline__ int softmax_draw(const char* row, int64_t V, int C, float c0, float u,
                                             const RowParts& rp, const RowSums& rs, const double (&wl)[MAX_ROUNDS]) {
-  constexpr int W = DTraits<DT>::W;
   const ChunkPick pk = pick_chunk(C, (double)u, wl);
   if (pk.c < 0) return -1;
   const int tc = pk.c / WAVE, lc = pk.c % WAVE;
