@@ -124,17 +124,6 @@ __device__ __forceinline__ double residual_raw_sum(const Raw& rt, const Raw& rd,
   return wave_sum(s);
 }
 
-// Inverse CDF of the residual inside chunk c.
-template <int DT>
-__device__ __forceinline__ int residual_chunk_draw(const char* trow, const char* drow, int64_t V, int64_t c,
-                                                   const ResidW& rw, double th) {
-  Raw rt, rd;
-  const Chunk kt = load_chunk<DT>(trow, V, c, rt);
-  load_chunk<DT>(drow, V, c, rd);
-  const int64_t y = chunk_invcdf<DT, true>(kt, rt, rd, th, rw);
-  return (int)y;
-}
-
 // ------------------------------------------------------------------ linear drafts
 struct LinearParams {
   const char* target;
@@ -570,17 +559,13 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   if (d.kind == 0) return Ev{0, 0u, false, 0};   // no draft rejected: the bonus token is recorded already
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind == 1) {
-    // The token event counts before the draw: if it is the sequence's last event,
-    // this wave emits and reads the emission's inputs while the draw's loads are
-    // in flight; otherwise the last event's wave waits for the token record.
+    // Round trips overlap: the token event's count goes out with the reads of the
+    // residual sums; after the pick, the chosen chunk's reloads go out with the
+    // emission's reads (if this is the sequence's last event, which the count
+    // tells); then the scan. Otherwise the last event's wave waits for the token
+    // record.
     uint32_t fo = 0;
     if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
-    const bool last = bcast(fo) + 1 == (uint32_t)P.R + 1u;
-    EmitIn ein;
-    if (last) {
-      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-      ein = emit_load<DT, true>(P, b, true);
-    }
     double wl[MAX_ROUNDS];
     bool ok = true;
 #pragma unroll
@@ -596,21 +581,25 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
         clear_rec<ResPart>(rec);
       }
     }
+    const bool last = bcast(fo) + 1 == (uint32_t)P.R + 1u;
     const float u = P.uniforms[b * (k + 1) + k];
-    if (__ballot(!ok)) {
+    ChunkPick pk;
+    pk.c = -1;
+    ResidW rx = rw;
+    const char* dx = drow;
+    const bool rec_ok = __ballot(!ok) == 0ull;
+    if (!rec_ok) {
       y = -2;
     } else {
       // The draw from the residual. With no residual mass (the rows agree up to
       // rounding) it is taken from p_t,L instead: the same pick and scan with the
       // draft's weights zeroed (and taken from row t_L, so that they stay finite),
       // over chunk sums formed here.
-      ResidW rx = rw;
-      const char* dx = drow;
       double tot = 0.0;
 #pragma unroll
       for (int t = 0; t < MAX_ROUNDS; ++t) tot += wl[t];
       tot = wave_sum(tot);
-      ChunkPick pk = pick_chunk(P.C, (double)u, wl);
+      pk = pick_chunk(P.C, (double)u, wl);
       if (pk.c < 0 && tot == 0.0) {
         rx.mc0d = rx.mc0t;
         rx.izd = 0.0f;
@@ -628,10 +617,21 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
         }
         pk = pick_chunk(P.C, (double)u, wl);
       }
-      if (pk.c >= 0) {
-        const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
-        y = residual_chunk_draw<DT>(trow, dx, P.V, pk.c, rx, th);
-      }
+    }
+    Raw rt, rd;
+    Chunk kt;
+    if (pk.c >= 0) {
+      kt = load_chunk<DT>(trow, P.V, pk.c, rt);
+      load_chunk<DT>(dx, P.V, pk.c, rd);
+    }
+    EmitIn ein;
+    if (last) {
+      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+      ein = emit_load<DT, true>(P, b, true);
+    }
+    if (pk.c >= 0) {
+      const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
+      y = (int)chunk_invcdf<DT, true>(kt, rt, rd, th, rx);
     }
     if (last) {
       emit_store<DT, true>(P, b, ein, y);
