@@ -527,6 +527,11 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);
+  // Counted before the sums: the count's round trip overlaps this wave's loads. The
+  // last to count draws; it reads the others' records with polling reads, which
+  // wait for any that are not written yet.
+  uint32_t old = 0;
+  if (lane == 0) old = counter_add(P.res_cnt + b * CSTRIDE, 1u);
   if (d.kind == 1) {
     if constexpr (G == 1) {
       Raw rt, rd;
@@ -547,8 +552,6 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
       }
     }
   }
-  uint32_t old = 0;
-  if (lane == 0) old = counter_add(P.res_cnt + b * CSTRIDE, 1u);
   old = bcast(old);
   if (old + 1 != CG) return Ev{0, 0u, false, 0};
   // last residual wave of the sequence: draw the correction token
