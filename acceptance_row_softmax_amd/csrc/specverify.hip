@@ -515,15 +515,7 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   d.kind = 2;
   d.Mt = d.Md = 0.0f;
   d.Zt = d.Zd = 0.0;
-  bool got = true;
-  if (lane == 0) got = poll_rec(P.dec + b * DEC_WORDS, d, P.tag);
-  got = bcast(got ? 1 : 0) != 0;
-  d.L = bcast(d.L);
-  d.kind = got ? bcast(d.kind) : 3;   // 3: the decision never arrived
-  d.Mt = bcast(d.Mt);
-  d.Md = bcast(d.Md);
-  d.Zt = bcast(d.Zt);
-  d.Zd = bcast(d.Zd);
+  if (!poll_rec(P.dec + b * DEC_WORDS, d, P.tag)) d.kind = 3;   // 3: the decision never arrived
   const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);

@@ -676,13 +676,25 @@ __device__ __forceinline__ bool get_rec(const uint64_t* src, T& v, uint32_t tag)
   return false;
 }
 
-// Polls only the record's first word, with a longer pause between polls, then
-// reads the whole record: for waits that may last a while.
+// Polls a whole record with one load per word, lane i reading word i (one request
+// for the record's line), with a longer pause between polls: for waits that may
+// last a while. Called by every lane of the wave; the record is returned in every
+// lane; false on timeout (v undefined).
 template <class T>
 __device__ __forceinline__ bool poll_rec(const uint64_t* src, T& v, uint32_t tag) {
+  constexpr int N = RecWords<T>::N;
+  static_assert(N <= WAVE, "one word per lane");
+  const int lane = lane_id();
   for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
-    const uint64_t x = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(x >> 32) == tag) return get_rec(src, v, tag);
+    uint64_t x = 0;
+    if (lane < N) x = __hip_atomic_load(src + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__ballot(lane < N && (uint32_t)(x >> 32) != tag) == 0ull) {
+      uint32_t w[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) w[i] = __shfl((uint32_t)x, i);
+      __builtin_memcpy(&v, w, sizeof(T));
+      return true;
+    }
     __builtin_amdgcn_s_sleep(8);
   }
   return false;
