@@ -142,7 +142,7 @@ struct LinearParams {
   uint64_t* tok;        // [B]      Token records
   uint64_t* prob;       // [B][k]   Probs records (stochastic)
   uint32_t* row_cnt;    // [RQ]     chunks done per row
-  uint32_t* pair_cnt;   // [B][k]   rows combined per (target, draft) pair
+  uint64_t* pair;       // [B][k]   per (target, draft) pair: each row's draft-token probability
   uint64_t* state;      // [B]      sequence state words
   uint32_t* fin;        // [B]      events per sequence
   uint32_t* res_cnt;    // [B]      residual waves done per sequence
@@ -417,33 +417,38 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
     const bool acc = st.ok == 1 && x == st.argmax;
     bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
   } else {
-    uint32_t old = 0;
-    if (lane == 0) old = counter_add(P.pair_cnt + (b * k + i) * CSTRIDE, 1u);
-    old = bcast(old);
-    update = (old == 1);
+    // Each row of the pair ORs its probability of the draft token (fp32, sign bit
+    // set as the mark that it is there; NaN for an unusable row) into its half of
+    // the pair's word; the atomic's old value gives the second row the first's.
+    const float pxf = st.ok == 1 ? (float)st.px : NAN;
+    const uint64_t half = (uint64_t)(0x80000000u | (__float_as_uint(pxf) & 0x7fffffffu)) << (32 * which);
+    uint64_t* pw = P.pair + (b * k + i) * SSTRIDE;
+    uint64_t oldw = 0;
+    if (lane == 0) oldw = state_or(pw, half);
+    oldw = bcast(oldw);
+    const uint32_t oh = (uint32_t)(oldw >> (32 * (1 - which)));
+    update = (oh & 0x80000000u) != 0;
     if (update) {
       // second row of the pair: the acceptance test of position i
       have_other = true;
-      bool got = true;
+      // both probabilities as fp32, whichever row arrives second
+      const double opx = (double)__uint_as_float(oh & 0x7fffffffu);
+      const double mpx = (double)pxf;
+      const double pt = which == 0 ? mpx : opx;
+      const double pd = which == 0 ? opx : mpx;
+      double qr;
+      if (pd > 0.0) qr = pt / pd;
+      else qr = (pt > 0.0) ? INFINITY : NAN;
+      const bool ok = !isnan(pt) && !isnan(pd);   // an unusable row rejects
+      const bool acc = ok && (double)P.uniforms[b * (k + 1) + i] < qr;   // NaN ratio rejects
+      bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
       if (lane == 0) {
-        counter_reset(P.pair_cnt + (b * k + i) * CSTRIDE);
-        got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);
-        other_got = got;
-        const double pt = which == 0 ? st.px : other.px;
-        const double pd = which == 0 ? other.px : st.px;
-        double qr;
-        if (pd > 0.0) qr = pt / pd;
-        else qr = (pt > 0.0) ? INFINITY : NAN;
-        const bool ok = got && st.ok == 1 && other.ok == 1;
-        const bool acc = ok && (double)P.uniforms[b * (k + 1) + i] < qr;   // NaN ratio rejects
-        bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
+        counter_reset(pw);
         Probs pr;
         pr.pt = (float)pt;
         pr.pd = (float)pd;
         put_rec(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
-        if (!got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
       }
-      bits = bcast(bits);
     }
   }
   Ev ev;
@@ -454,6 +459,12 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
   if (update) {
     uint64_t olds = 0;
     if (lane == 0) olds = state_or(P.state + b * SSTRIDE, bits);
+    if (STOCH && have_other && lane == 0) {
+      // the other row's statistics, for a decision settled here; read while the
+      // state update is in flight
+      other_got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);
+      if (!other_got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
+    }
     olds = bcast(olds);
     if (linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which, other, have_other, other_got, ev.y)) {
       ev.token = true;   // and the final token
@@ -1472,7 +1483,7 @@ Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode)
   const int64_t C = chunks_per_row(V, dt);
   return make_layout({(size_t)(RQ * C) * PART_WORDS * 8, (size_t)RQ * ROW_WORDS * 8, (size_t)B * DEC_WORDS * 8,
                       (size_t)(B * C) * RES_WORDS * 8, (size_t)B * 8, (size_t)(RQ * CSTRIDE) * 4,
-                      (size_t)(B * k * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
+                      (size_t)(B * k * SSTRIDE) * 8, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
                       (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8});
 }
 
@@ -1595,7 +1606,7 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.res = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
   P.tok = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
   P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[5]);
-  P.pair_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[6]);
+  P.pair = reinterpret_cast<uint64_t*>(ws + lay.off[6]);
   P.state = reinterpret_cast<uint64_t*>(ws + lay.off[7]);
   P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
   P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
