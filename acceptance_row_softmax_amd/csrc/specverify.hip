@@ -16,13 +16,15 @@
 //    rows t_L, d_L to the residual waves (or, if no draft is rejected, releases
 //    the bonus token);
 //  * residual waves (stochastic mode), one per (sequence, chunk), dispatched after
-//    all streaming waves: each sums max(0, p_t,L - p_d,L) over its chunk; the last
-//    of a sequence picks the chunk holding u*S and draws the correction token by
-//    an inverse-CDF scan inside it;
+//    the streaming waves of positions 0..k-1 and before those of the target rows
+//    k (the decision never depends on row k): each sums max(0, p_t,L - p_d,L)
+//    over its chunk; the last of a sequence picks the chunk holding u*S and draws
+//    the correction token by an inverse-CDF scan inside it;
 //  * the last event of a sequence (an atomic counter per sequence) writes all of
 //    its outputs.
-// No wave ever waits for work that is dispatched after it except the residual
-// waves (which wait for the decision of streaming waves dispatched before them).
+// No wave ever waits for work that is dispatched after it: residual waves wait
+// for decisions of streaming waves dispatched before them, and a last event waits
+// only for a token whose wave has already counted itself.
 //
 // Trees: a streaming launch of the same kind reduces every node's row (greedy:
 // its argmax is the node's token; stochastic: for a small batch the token is
@@ -153,6 +155,7 @@ struct LinearParams {
   float c0;
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
+  uint32_t res0, res1, tk0;   // stochastic, k > 0: first residual wave, end of the residual waves, first wave of target rows k
   // optional commit by the emitting wave (spec_verify_linear_commit)
   int32_t* seq_len;     // [B] in/out
   int32_t* history;     // [B][capacity]
@@ -357,17 +360,7 @@ __device__ __forceinline__ bool linear_settle(const LinearParams& P, int64_t b, 
     return false;   // the residual waves draw the token
   }
   int y = 0;
-  if (lane_id() == 0) {
-    y = !got ? -2 : (tl.ok != 1 ? -1 : (STOCH ? tl.y : tl.argmax));
-    if (STOCH && k > 0) {
-      Decision d;
-      d.L = Ln;
-      d.kind = 0;
-      d.Mt = d.Md = 0.0f;
-      d.Zt = d.Zd = 0.0;
-      put_rec(P.dec + b * DEC_WORDS, d, P.tag);
-    }
-  }
+  if (lane_id() == 0) y = !got ? -2 : (tl.ok != 1 ? -1 : (STOCH ? tl.y : tl.argmax));
   y_out = bcast(y);
   return true;   // the final token is known
 }
@@ -466,6 +459,20 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
       if (!other_got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
     }
     olds = bcast(olds);
+    if (STOCH && i < k && lane == 0) {
+      // The update that decides the last position with none rejected tells the
+      // residual waves that L = k (they have nothing to draw), without waiting for
+      // target row k: those waves are dispatched before it.
+      const uint64_t mk = (1ull << k) - 1, now = olds | bits;
+      if ((now & mk) == mk && ((now >> 32) & mk) == 0 && (olds & mk) != mk) {
+        Decision d;
+        d.L = (int)k;
+        d.kind = 0;
+        d.Mt = d.Md = 0.0f;
+        d.Zt = d.Zd = 0.0;
+        put_rec(P.dec + b * DEC_WORDS, d, P.tag);
+      }
+    }
     if (linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which, other, have_other, other_got, ev.y)) {
       ev.token = true;   // and the final token
       ev.n = 2;
@@ -654,8 +661,10 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
 constexpr int64_t RESID_GROUP_WAVES = 4096;
 
 // Wave roles of a linear launch: the streaming waves (rows in order, see
-// stream_coords), then in stochastic mode with k > 0 one residual wave per
-// (sequence, chunk). Residual waves follow every row their decision depends on.
+// stream_coords); in stochastic mode with k > 0 the streaming waves of the rows of
+// positions 0..k-1, one residual wave per (sequence, G chunks), idle waves up to a
+// multiple of 8 workgroups, and the streaming waves of the target rows k. Residual
+// waves follow every row their decision depends on.
 struct Role {
   int kind;       // 0 idle, 1 streaming (q, c), 2 residual (b, c)
   uint32_t q, b, c;
@@ -668,16 +677,24 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
   r.q = r.b = r.c = 0;
   const uint32_t CP = (uint32_t)P.CP;
   const uint32_t C = (uint32_t)P.C;
-  const uint32_t RQ = (uint32_t)(P.B * P.R);
-  if (w < RQ * CP) {
-    stream_coords(w, CP, RQ, r.q, r.c);
+  if (!STOCH || P.k == 0) {
+    stream_coords(w, CP, (uint32_t)(P.B * P.R), r.q, r.c);
     r.kind = r.c < C ? 1 : 0;
-  } else {
-    const uint32_t v = w - RQ * CP;
+  } else if (w < P.res0) {
+    // the rows of positions 0..k-1
+    stream_coords(w, CP, (uint32_t)(2 * P.k * P.B), r.q, r.c);
+    r.kind = r.c < C ? 1 : 0;
+  } else if (w < P.res1) {
+    const uint32_t v = w - P.res0;
     const uint32_t CG = (C + G - 1) / G;
     r.b = v / CG;
     r.c = v - r.b * CG;
     r.kind = 2;
+  } else if (w >= P.tk0) {
+    // target rows k, from a multiple of 8 workgroups so that rows keep to one XCD
+    stream_coords(w - P.tk0, CP, (uint32_t)P.B, r.q, r.c);
+    r.q += (uint32_t)(2 * P.k * P.B);
+    r.kind = r.c < C ? 1 : 0;
   }
   return r;
 }
@@ -1622,7 +1639,18 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   // residual waves: one per chunk, or one per two chunks when a launch would have
   // more than RESID_GROUP_WAVES of them (then their dispatch sets the time)
   P.G = (stoch && B * P.C > RESID_GROUP_WAVES) ? 2 : 1;
-  P.n_waves = B * P.R * P.CP + ((stoch && k > 0) ? B * ((P.C + P.G - 1) / P.G) : 0);
+  P.n_waves = B * P.R * P.CP;
+  P.res0 = P.res1 = P.tk0 = 0;
+  if (stoch && k > 0) {
+    // rows of positions 0..k-1, residual waves, padding to a multiple of 8
+    // workgroups, target rows k
+    const int64_t r0 = 2 * k * B * P.CP, r1 = r0 + B * ((P.C + P.G - 1) / P.G);
+    const int64_t t0 = (r1 + 8 * WPB - 1) / (8 * WPB) * (8 * WPB);
+    P.n_waves = t0 + B * P.CP;
+    P.res0 = (uint32_t)r0;
+    P.res1 = (uint32_t)r1;
+    P.tk0 = (uint32_t)t0;
+  }
   if (P.n_waves > MAX_WAVES) return SV_ELIMIT;
   P.commit = false;
   P.tag = next_tag();
