@@ -373,6 +373,10 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
   const char* row = row_ptr<DT, STOCH>(P, b, i, which);
   // the draft token of this position; its logit in this row comes with the partials
   const int x = (i < k) ? P.tokens[b * k + i] : -1;
+  // target row k: the sequence's state, read with the partials (an earlier
+  // position already rejected makes the bonus draw useless)
+  uint64_t sn = 0;
+  if (STOCH && i == k && lane == 0) sn = state_load(P.state + b * SSTRIDE);
   const RowParts rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
   const float xv = rp.xv;
   double wl[MAX_ROUNDS];
@@ -389,8 +393,6 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
     st.px = exp2(((double)xv - (double)rs.M) * (double)P.c0) / rs.Z;
   if (STOCH && i == k && st.ok == 1) {
     // the bonus draw, unless an earlier position has already been rejected
-    uint64_t sn = 0;
-    if (lane == 0) sn = state_load(P.state + b * SSTRIDE);
     sn = bcast(sn);
     if (settled_L(sn, (int)k) < 0)
       st.y = softmax_draw<DT>(row, V, P.C, P.c0, P.uniforms[b * (k + 1) + k], rp, rs, wl);
