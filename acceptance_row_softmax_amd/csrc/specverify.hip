@@ -521,10 +521,11 @@ __device__ __forceinline__ Ev linear_stream_wave(const LinearParams& P, uint32_t
   return linear_combine<DT, STOCH>(P, q, b, i, which);
 }
 
-// Residual wave (b, g), dispatched after every streaming wave: waits for the
-// decision of sequence b; if a draft was rejected, sums the residual over chunks
-// G g ... G g + G - 1 of rows t_L, d_L. The sequence's last residual wave picks
-// the chunk holding u*S, scans it and records the token.
+// Residual wave (b, g), dispatched after the streaming waves of every row a
+// decision depends on (positions 0..k-1): waits for the decision of sequence b;
+// if a draft was rejected, sums the residual over chunks G g ... G g + G - 1 of
+// rows t_L, d_L. The sequence's last residual wave picks the chunk holding u*S,
+// scans it and records the token.
 template <int DT, int G>
 __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
   const int lane = lane_id();

@@ -61,16 +61,22 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """sha256 over what defines the verification kernels: their sources, the
-    header and the compiler flags, in a fixed order."""
+    """sha256 over what defines the verification kernels: their sources and the
+    header with comments and runs of whitespace taken out (edits to those do not
+    change the kernels), and the compiler flags, in a fixed order."""
     import hashlib
+    import re
     from acceptance_row_softmax_amd import _build
     h = hashlib.sha256()
     for rel in ("acceptance_row_softmax_amd/csrc/specverify.hip", "acceptance_row_softmax_amd/csrc/sv_device.hpp",
                 "acceptance_row_softmax_amd/csrc/sv_rows.hpp", "acceptance_row_softmax_amd/csrc/sv_host.hpp",
                 "include/specverify.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+        with open(os.path.join(ROOT, rel), "r", encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(rel.encode() + b"\0" + text.encode() + b"\0")
     h.update(" ".join(_build.HIPCC_FLAGS).encode())
     return h.hexdigest()
 
