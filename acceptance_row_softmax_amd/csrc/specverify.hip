@@ -46,6 +46,7 @@
 
 #include <hip/hip_runtime.h>
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -406,6 +407,7 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
   bool update = true;
   RowStat other;            // stochastic pair: the other row of position i (lane 0)
   bool have_other = false, other_got = true;
+  bool read_early = false;  // its record was read for the acceptance test
   if (i == k) {
     bits = BONUS_BIT;   // the row after the last draft is combined (and drawn)
   } else if constexpr (!STOCH) {
@@ -426,9 +428,23 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
     if (update) {
       // second row of the pair: the acceptance test of position i
       have_other = true;
-      // both probabilities as fp32, whichever row arrives second
-      const double opx = (double)__uint_as_float(oh & 0x7fffffffu);
-      const double mpx = (double)pxf;
+      // Both probabilities as fp32, whichever row arrives second: the ratio keeps
+      // about 1e-7 relative. Below the smallest normal fp32 (or at zero) that no
+      // longer holds, and the test takes both in fp64, the other's from its record.
+      const float of = __uint_as_float(oh & 0x7fffffffu);
+      double opx = (double)of;
+      double mpx = (double)pxf;
+      if (pxf < FLT_MIN || of < FLT_MIN) {   // NaN (an unusable row) compares false
+        read_early = true;
+        double o = NAN;
+        if (lane == 0) {
+          other_got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);
+          if (other_got && other.ok == 1) o = other.px;
+          if (!other_got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
+        }
+        opx = __shfl(o, 0);
+        mpx = st.ok == 1 ? st.px : (double)NAN;
+      }
       const double pt = which == 0 ? mpx : opx;
       const double pd = which == 0 ? opx : mpx;
       double qr;
@@ -454,7 +470,7 @@ __device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, i
   if (update) {
     uint64_t olds = 0;
     if (lane == 0) olds = state_or(P.state + b * SSTRIDE, bits);
-    if (STOCH && have_other && lane == 0) {
+    if (STOCH && have_other && !read_early && lane == 0) {
       // the other row's statistics, for a decision settled here; read while the
       // state update is in flight
       other_got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);

@@ -82,6 +82,28 @@ def test_zero_residual_falls_back_to_the_target_row():
     np.testing.assert_array_equal(g["out_tokens"][:, 0], dom[:, 0])
 
 
+def test_tiny_draft_token_probabilities():
+    # Every draft token sits about 110 natural units below the maxima of both its
+    # rows (T = 1), so p_t and p_d are near 1e-52: zero in fp32, ordinary in fp64.
+    # Their ratio is e^(-delta) times the ratio of the normalisers, delta uniform in
+    # [-1.5, 1.5], so the acceptance test decides on u. Rounded to fp32 both
+    # probabilities would vanish and every test would reject.
+    B, k, V = 64, 2, 3000
+    rng = np.random.default_rng(11)
+    t = rng.normal(0.0, 1.0, size=(B, k + 1, V))
+    d = rng.normal(0.0, 1.0, size=(B, k, V))
+    tok = rng.integers(0, V, size=(B, k))
+    bi, ii = np.arange(B)[:, None], np.arange(k)[None, :]
+    t[bi, ii, tok] = -110.0
+    d[bi, ii, tok] = -110.0 + rng.uniform(-1.5, 1.5, size=(B, k))
+    u = gen.uniforms(gen.key(66, V, 2), B * (k + 1)).reshape(B, k + 1)
+    w = gen.LinearWorkload("tiny-p", "stochastic", 1.0, B, k, V, gen.DT_F32, t.astype(np.float32),
+                           d.astype(np.float32), tok.astype(np.int32), u)
+    g, o, near, n_eval = _check(w)
+    assert np.all(o["p_target"] < 1e-45) and np.all(o["p_target"] > 0.0)
+    assert 0.2 < np.mean(o["accept_len"] >= 1) < 0.95
+
+
 def test_grouped_residual_waves_odd_chunks():
     # more than 4096 (sequence, chunk) pairs: each residual wave sums two chunks;
     # V = 20000 bf16 rows have 5 chunks, so every sequence's last wave has one
