@@ -1549,8 +1549,8 @@ struct LinearLauncher {
   }
 };
 
-// Walk workgroups: 1024 threads when the tokens are known; 512 for the lazy
-// walk, whose draw needs more registers per thread.
+// Walk workgroups: 1024 threads, so that one pass of WALK_BATCH nodes per thread
+// covers trees of up to 8192 nodes.
 template <int DT, bool STOCH>
 struct TreeLauncher {
   static sv_status run(const TreeParams& P, size_t smem, hipStream_t s) {
@@ -1574,7 +1574,7 @@ struct TreeLauncher {
     if (launch_status() != SV_OK) return SV_EHIP;
     if (Q.wave_walk) return SV_OK;   // the streaming launch has walked every tree
     if (STOCH && !eager) {
-      hipLaunchKernelGGL((tree_walk_kernel<DT, WM_LAZY, 512>), trees, dim3(512), smem, s, P);
+      hipLaunchKernelGGL((tree_walk_kernel<DT, WM_LAZY, 1024>), trees, dim3(1024), smem, s, P);
     } else {
       hipLaunchKernelGGL((tree_walk_kernel<DT, WM_KNOWN, 1024>), trees, dim3(1024), smem, s, P);
     }
@@ -1596,7 +1596,7 @@ struct TypicalLauncher {
       hipLaunchKernelGGL((tree_stream_kernel<DT, TD_TYPICAL, false>), dim3(blocks_for(Q.n_gather + P.n_stream)),
                          dim3(BLOCK), 0, s, Q);
     if (launch_status() != SV_OK) return SV_EHIP;
-    hipLaunchKernelGGL((tree_walk_kernel<DT, WM_TYPICAL, 512>), dim3((unsigned)P.B), dim3(512), smem, s, Q);
+    hipLaunchKernelGGL((tree_walk_kernel<DT, WM_TYPICAL, 1024>), dim3((unsigned)P.B), dim3(1024), smem, s, Q);
     return launch_status();
   }
 };
