@@ -1,9 +1,10 @@
 """GPU parity on random shapes: linear verification over random batch sizes, draft
 lengths, vocabulary sizes (below, at and past chunk boundaries), dtypes, modes and
-temperatures, and tree verification over random recursive trees (across the
+temperatures; tree verification over random recursive trees (across the
 256-node bound of the in-stream walk and the 4096-row bound of row waves) in
-greedy, stochastic and typical modes. Seeded; every case against the oracle, to
-the bar of the other parity tests."""
+greedy, stochastic and typical modes; the sampler over random row counts and
+vocabulary sizes; and tree masks of random trees up to 4681 nodes. Seeded; every
+case against the oracle, to the bar of the other parity tests."""
 import dataclasses
 
 import numpy as np
@@ -69,3 +70,42 @@ def test_random_trees():
             g = G.run_tree(w, None)
             o = G.oracle_tree(w)
         G.compare_tree(g, o)
+
+
+def test_random_sampler_and_tree_mask_shapes():
+    import torch
+    import acceptance_row_softmax_amd as sv
+    rng = np.random.default_rng(11)
+    for c in range(30):
+        mode = "stochastic" if rng.random() < 0.7 else "greedy"
+        dtype = int(rng.choice([gen.DT_F32, gen.DT_BF16, gen.DT_F16]))
+        V = int(rng.choice([1, 9, 4095, 4096, 4097, 20001, 70000]))
+        rows = int(rng.integers(1, max(1, min(600, int(20e6 // V))) + 1))
+        T = float(rng.choice([0.6, 1.0, 1.7]))
+        G.say(f"random sampler {c}: mode={mode} dtype={dtype} rows={rows} V={V} T={T}")
+        x = gen.normal_pair(gen.key(98, V, c), 2.5, 0, 0.0, rows * V, dtype, want_b=False)[0].reshape(rows, V)
+        u = gen.uniforms(gen.key(98, V, 100 + c), rows).astype(np.float32)
+        g = sv.sample(G.to_dev(x, dtype), G.to_dev(u) if mode == "stochastic" else None, mode=mode, temperature=T)
+        torch.cuda.synchronize()
+        o = oracle.sample(mode, T, x, u, V, dtype)
+        gt = g["tokens"].cpu().numpy()
+        np.testing.assert_array_equal(g["err_flags"].cpu().numpy(), o["err_flags"])
+        differ = gt != o["tokens"]
+        assert not (differ & (o["near_tie"] == 0)).any()
+        if mode == "greedy":
+            assert not differ.any()
+        G._record(differ, o["near_tie"], np.full(rows, 1 if mode == "stochastic" else 0))
+    for c in range(30):
+        n = int(rng.choice([1, 2, 31, 32, 33, 64, 65, 300, 2000, 4681]))
+        trees = int(rng.integers(1, 6))
+        par = np.stack([np.array([-1] + [int(rng.integers(max(0, i - 1 - int(rng.integers(0, 6))), i))
+                                         if rng.random() < 0.6 else int(rng.integers(0, i)) for i in range(1, n)],
+                                 np.int32) for _ in range(trees)])
+        G.say(f"random tree mask {c}: trees={trees} n={n}")
+        r = sv.tree_mask(G.to_dev(par))
+        torch.cuda.synchronize()
+        assert not r["err_flags"].cpu().numpy().any()
+        w = r["mask"].cpu().numpy().view(np.uint32)
+        bits = ((w[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(trees, n, -1)[..., :n]
+        for t in range(trees):
+            np.testing.assert_array_equal(bits[t].astype(np.uint8), oracle.tree_mask(par[t]))
