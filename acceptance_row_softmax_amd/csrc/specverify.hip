@@ -1,7 +1,7 @@
 // libspecverify: speculative-decoding verification kernels for gfx950 and the C ABI
 // declared in include/specverify.h.
 //
-// Linear drafts: one launch per call. Its workgroups hold four independent waves;
+// Linear drafts: one launch per call. Its workgroups hold two independent waves;
 // in dispatch order the waves are
 //  * streaming waves, one per (row, 8 KiB chunk), rows in position order (the
 //    target/draft rows of position 0 of every sequence, then position 1, ...,

@@ -1,6 +1,6 @@
 // Device building blocks for libspecverify (gfx950, wave64).
 //
-// Work is split into waves, not workgroups: a 256-thread workgroup holds four
+// Work is split into waves, not workgroups: a 128-thread workgroup holds two
 // wave64s that never synchronise with each other, so one wave's arithmetic
 // overlaps the others' memory traffic. A wave streams one chunk of one row: lane l
 // owns the 16-byte units u0 + j*64 + l (j < CU), so every load instruction reads
@@ -23,7 +23,7 @@
 namespace sv {
 
 constexpr int WAVE = 64;
-constexpr int BLOCK = 256;
+constexpr int BLOCK = 128;
 constexpr int WPB = BLOCK / WAVE;               // independent waves per workgroup
 #ifndef SV_CU
 #define SV_CU 8
@@ -438,7 +438,7 @@ __device__ __forceinline__ double pow2_neg(double d) {
 // Streaming waves of one launch: rows are processed in groups of 8 consecutive
 // rows, and every chunk of a row runs on the same XCD (workgroups are dispatched
 // round-robin over the 8 XCDs): row q on XCD q % 8. The chunks of a row are
-// padded to a multiple of 4 waves (CP) so that no workgroup spans two rows;
+// padded to a multiple of WPB waves (CP) so that no workgroup spans two rows;
 // padding waves have c >= C and do nothing. RQ rows.
 __device__ __forceinline__ void stream_coords(uint32_t w, uint32_t CP, uint32_t RQ, uint32_t& q, uint32_t& c) {
   const uint32_t bpr = CP / WPB;           // workgroups per row
