@@ -27,6 +27,14 @@ MUT_TREE_NO_ANCESTOR = 5
 MUT_TEMPERATURE_IGNORED = 6
 MUT_LSE_WITHOUT_MAX = 7
 MUT_COMMIT_REJECTED_DRAFT = 8
+MUT_NEAR_LO_ONLY = 9
+MUT_NEVAL_ALL = 10
+MUT_ACCEPT_TIE_OFF = 11
+
+# near_tie bits: a near tie that can change the accepted length, one that can
+# change only the final token
+NT_DECISION = 1
+NT_FINAL = 2
 
 
 def build(force: bool = True) -> str:

@@ -26,7 +26,16 @@ enum {
   MUT_TEMPERATURE_IGNORED = 6, // softmax at T = 1 whatever T is
   MUT_LSE_WITHOUT_MAX = 7,     // lse missing the m/T term
   MUT_COMMIT_REJECTED_DRAFT = 8,  // commit keeps the rejected draft x_L in place of the target's token
+  MUT_NEAR_LO_ONLY = 9,        // a draw's near tie checked against the lower bin edge only
+  MUT_NEVAL_ALL = 10,          // every draw counted as evaluated, also those the result ignores
+  MUT_ACCEPT_TIE_OFF = 11,     // accept-test near ties not flagged
 };
+
+// near_tie bits: a draw within tie_eps of its threshold that can change the
+// accepted length (and so every output), and one that can change only the final
+// token.
+constexpr int32_t NT_DECISION = 1;
+constexpr int32_t NT_FINAL = 2;
 
 const double kNaN = std::numeric_limits<double>::quiet_NaN();
 const double kInf = std::numeric_limits<double>::infinity();
@@ -119,7 +128,10 @@ Draw invcdf(const std::vector<double>& w, double u) {
   return d;
 }
 
+// Whether u lies within eps of either edge of the bin it selected: a draw whose
+// outcome rounding could change.
 bool near_draw(double u, const Draw& d, double eps) {
+  if (g_mutation == MUT_NEAR_LO_ONLY) return std::fabs(u - d.lo) < eps;
   return std::fabs(u - d.lo) < eps || std::fabs(u - d.hi) < eps;
 }
 
@@ -182,7 +194,7 @@ int orc_sample(int mode, double T, int64_t rows, int64_t V, int dtype, const voi
       if (s.ok) {
         const Draw d = invcdf(s.z, (double)uniforms[r]);
         y = d.y;
-        nt = near_draw((double)uniforms[r], d, tie_eps) ? 1 : 0;
+        nt = near_draw((double)uniforms[r], d, tie_eps) ? NT_FINAL : 0;
       }
     }
     tokens[r] = (int32_t)y;
@@ -328,15 +340,15 @@ int orc_verify_tree_typical(double T, double epsilon, double delta, int64_t B, i
       }
       // the result depends on the test of every child of an accepted node
       for (int64_t i = 1; i < n_nodes; ++i)
-        if (acc[(size_t)par[i]]) {
+        if (acc[(size_t)par[i]] || g_mutation == MUT_NEVAL_ALL) {
           ++ne;
-          if (close[(size_t)i]) nt = 1;
+          if (close[(size_t)i] && g_mutation != MUT_ACCEPT_TIE_OFF) nt |= NT_DECISION;
         }
       const double u = (double)uniforms[b * n_nodes + best];
       const Draw d = invcdf(sm[(size_t)best].z, u);
       out[L] = (int32_t)d.y;
       ++ne;
-      if (near_draw(u, d, tie_eps)) nt = 1;
+      if (near_draw(u, d, tie_eps)) nt |= NT_FINAL;
     } else {
       accept_len[b] = -1;
     }
@@ -440,9 +452,11 @@ int orc_verify_linear(int mode, double T, int64_t B, int64_t k, int64_t V, int d
           const double thr = std::fmin(1.0, q);
           const bool accept = (double)u[i] < q;  // NaN ratio: reject
           ++ne;
-          if (!std::isnan(q) && std::fabs((double)u[i] - thr) < tie_eps) nt = 1;
+          if (!std::isnan(q) && std::fabs((double)u[i] - thr) < tie_eps && g_mutation != MUT_ACCEPT_TIE_OFF)
+            nt |= NT_DECISION;
           if (!accept) { L = i; break; }
         }
+        if (g_mutation == MUT_NEVAL_ALL) ne = (int32_t)k;
         std::vector<double> w((size_t)V);
         const Softmax& tL = st[(size_t)L];
         if (L < k && g_mutation != MUT_RESIDUAL_AS_TARGET) {
@@ -459,7 +473,7 @@ int orc_verify_linear(int mode, double T, int64_t B, int64_t k, int64_t V, int d
         }
         const Draw d = invcdf(w, (double)u[k]);
         ++ne;
-        if (near_draw((double)u[k], d, tie_eps)) nt = 1;
+        if (near_draw((double)u[k], d, tie_eps)) nt |= NT_FINAL;
         y = d.y;
         if (y < 0) err |= 2;
       }
@@ -560,10 +574,15 @@ int orc_verify_tree(int mode, double T, int64_t B, int64_t n_nodes, int64_t V, i
       }
       out[L] = (int32_t)y[(size_t)best];
       if (stochastic) {
+        // The draw at an accepted node decides which of its children are accepted
+        // (so the path's length), and at a leaf on the path only the final token.
+        std::vector<char> has_child((size_t)n_nodes, 0);
+        for (int64_t i = 1; i < n_nodes; ++i) has_child[(size_t)par[i]] = 1;
         for (int64_t i = 0; i < n_nodes; ++i) {
-          if (!acc[(size_t)i]) continue;
+          if (!acc[(size_t)i] && g_mutation != MUT_NEVAL_ALL) continue;
           ++ne;
-          if (near_draw((double)uniforms[b * n_nodes + i], draw[(size_t)i], tie_eps)) nt = 1;
+          if (near_draw((double)uniforms[b * n_nodes + i], draw[(size_t)i], tie_eps))
+            nt |= has_child[(size_t)i] ? NT_DECISION : NT_FINAL;
         }
       }
     } else {

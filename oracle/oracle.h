@@ -53,9 +53,14 @@ int64_t orc_invcdf(const double* w, int64_t n, double u, double* lo, double* hi)
 /* Linear verification for B sequences (see header comment). Outputs:
  *  accept_len[B] in [0,k] (-1 on a data error), out_tokens[B][k+1] (-1 padded),
  *  p_target/p_draft[B][k] (optional, NaN on error), err_flags[B]
- *  (bit0 token out of range, bit1 non-finite row), near_tie[B] (1 if an
- *  evaluated draw lies within tie_eps of its threshold), n_eval[B] (evaluated
- *  draws). Returns 0, or -1 on bad arguments. */
+ *  (bit0 token out of range, bit1 non-finite row), near_tie[B], n_eval[B].
+ * Evaluated draws (n_eval) are the ones the result depends on: the accept tests
+ *  of positions 0..L (0..k-1 when L = k) and the final draw, so min(L+1, k) + 1;
+ *  0 for greedy and for a sequence with a data error.
+ * near_tie bits: 1 if an evaluated accept test has |u_i - min(1, q_i)| < tie_eps
+ *  (it can change L and so every output), 2 if the final draw has u_k within
+ *  tie_eps of either edge of the bin it selected (it can change only the final
+ *  token). Returns 0, or -1 on bad arguments. */
 int orc_verify_linear(int mode, double T, int64_t B, int64_t k, int64_t V, int dtype,
                       const void* target, const void* draft, const int32_t* draft_tokens,
                       const float* uniforms, double tie_eps,
@@ -67,7 +72,11 @@ int orc_verify_linear(int mode, double T, int64_t B, int64_t k, int64_t V, int d
  * path_nodes[B][max_depth], out_tokens[B][max_depth+1], err_flags[B]
  * (bit0 candidate out of range, bit1 non-finite row, bit2 invalid tree or depth
  * above max_depth), near_tie[B], n_eval[B], and optional node_token[B][n_nodes]
- * (the per-node argmax / sampled token). */
+ * (the per-node argmax / sampled token). Stochastic: the evaluated draws are
+ * those at accepted nodes (each decides which of the node's children match); a
+ * near tie (u within tie_eps of an edge of its bin) sets bit 1 at a node with
+ * children (it can change the path) and bit 2 at a leaf (only the final token).
+ * Greedy: n_eval = near_tie = 0. */
 int orc_verify_tree(int mode, double T, int64_t B, int64_t n_nodes, int64_t V, int dtype,
                     const int32_t* parent, int64_t parent_stride, const int32_t* cand,
                     const void* logits, const float* uniforms, int64_t max_depth, double tie_eps,
@@ -96,8 +105,8 @@ int orc_commit_linear(int64_t B, int64_t k, const int32_t* accept_len, const int
 /* One token per row of x[rows][V]: greedy = argmax (lowest index), stochastic =
  * invcdf(softmax(x / T), u[row]) (Sonar page, sections "MTP" and "Ziel-Entwurf":
  * sampling shared by all schemes). tokens -1 and err bit1 for a row without a usable
- * entry; near_tie[row] (optional) 1 if u lies within tie_eps of an edge of the drawn
- * bin. */
+ * entry; near_tie[row] (optional) 2 if u lies within tie_eps of an edge of the drawn
+ * bin (the token is a final draw), else 0. */
 int orc_sample(int mode, double T, int64_t rows, int64_t V, int dtype, const void* x,
                const float* uniforms, double tie_eps, int32_t* tokens, int32_t* err_flags,
                int32_t* near_tie);
@@ -125,10 +134,10 @@ int64_t orc_tree_build_greedy(int64_t K, int64_t S, const double* acc, int64_t b
  * i >= 1 passes iff p_parent(cand_i) > min(epsilon, delta * exp(-H_parent)); it is
  * accepted iff it passes and its parent is accepted (the root always is); the
  * deepest accepted node (lowest index on ties) ends the path, and the final token is
- * invcdf(p_best, u[b][best]). near_tie[b]: a decisive pass test (one of a child of an
- * accepted node) within tie_eps (relative) of its threshold, or the final draw within
- * tie_eps of a bin edge. n_eval[b]: decisive tests plus the final draw. Errors as for
- * orc_verify_tree. */
+ * invcdf(p_best, u[b][best]). near_tie[b]: bit 1 if a decisive pass test (one of a
+ * child of an accepted node) lies within tie_eps (relative) of its threshold, bit 2 if
+ * the final draw lies within tie_eps of a bin edge. n_eval[b]: decisive tests plus the
+ * final draw. Errors as for orc_verify_tree. */
 int orc_verify_tree_typical(double T, double epsilon, double delta, int64_t B, int64_t n_nodes,
                             int64_t V, int dtype, const int32_t* parent, int64_t parent_stride,
                             const int32_t* cand, const void* logits, const float* uniforms,

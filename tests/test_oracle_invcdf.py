@@ -55,3 +55,15 @@ def test_chi_square_against_weights():
 def test_planted_off_by_one_is_caught():
     with oracle.mutation(oracle.MUT_INVCDF_GE):
         assert oracle.invcdf([0.0, 0.0, 2.0, 1.0], 0.0)[0] != 2
+
+
+def test_rounding_fallback_takes_the_last_positive_bin():
+    # u = 1 leaves no bin whose cumulative weight exceeds u*S (the case rounding can
+    # produce): the draw is the last entry of positive weight, trailing zeros skipped
+    w = [0.5, 2.0, 0.0, 1.5, 0.0, 0.0]
+    y, lo, hi = oracle.invcdf(w, 1.0)
+    assert y == 3
+    assert (lo, hi) == (2.5 / 4.0, 1.0)
+    assert oracle.invcdf([1.0, 1.0, 0.0, 0.0], 1.0)[0] == 1
+    # u just below 1 still crosses normally
+    assert oracle.invcdf(w, 1.0 - 2.0 ** -24)[0] == 3

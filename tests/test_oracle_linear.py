@@ -181,3 +181,130 @@ def test_data_errors_are_flagged():
     g = oracle.verify_linear("greedy", 1.0, t, None, x, None, V, F32)
     # greedy ignores NaN entries and never reads the draft rows
     assert list(g["err_flags"]) == [1, 0, 0, 0]
+
+
+# ------------------------------------------------------------------ exact laws
+def _acc_prob(pt, pd, x):
+    """min(1, p_t(x) / p_d(x)): the probability that draft token x is accepted."""
+    return min(1.0, pt[x] / pd[x])
+
+
+def _residual(pt, pd):
+    r = np.maximum(pt - pd, 0.0)
+    return r / r.sum()
+
+
+def _exact_outcomes_v2_k2(pt, pd):
+    """The law of (L, emitted tokens) for V = 2, k = 2, by enumerating the draft
+    draws and accept events: draft x_i ~ p_d,i, accepted w.p. min(1, p_t,i/p_d,i);
+    on the first reject at L the token comes from the normalised residual
+    max(0, p_t,L - p_d,L) (a point mass when V = 2); with both accepted it comes
+    from p_t,2."""
+    law = {}
+    r0, r1 = _residual(pt[0], pd[0]), _residual(pt[1], pd[1])
+    for x0 in range(2):
+        a0 = _acc_prob(pt[0], pd[0], x0)
+        for y in range(2):
+            law[(0, y)] = law.get((0, y), 0.0) + pd[0][x0] * (1 - a0) * r0[y]
+        for x1 in range(2):
+            a1 = _acc_prob(pt[1], pd[1], x1)
+            for y in range(2):
+                law[(1, x0, y)] = law.get((1, x0, y), 0.0) + pd[0][x0] * a0 * pd[1][x1] * (1 - a1) * r1[y]
+                law[(2, x0, x1, y)] = pd[0][x0] * a0 * pd[1][x1] * a1 * pt[2][y]
+    return law
+
+
+def _v2_k2_case(n, seed=77):
+    rng = np.random.default_rng(seed)
+    t = np.array([[0.3, -0.4], [1.2, 0.1], [-0.5, 0.6]], np.float32)
+    d = np.array([[-0.2, 0.5], [0.4, 0.9]], np.float32)
+    pt = [R.softmax(r.astype(np.float64), 1.0) for r in t]
+    pd = [R.softmax(r.astype(np.float64), 1.0) for r in d]
+    x = np.stack([(rng.random(n) >= pd[i][0]).astype(np.int32) for i in range(2)], axis=1)
+    u = _u24(rng, (n, 3))
+    target = np.ascontiguousarray(np.broadcast_to(t, (n, 3, 2)))
+    draft = np.ascontiguousarray(np.broadcast_to(d, (n, 2, 2)))
+    return pt, pd, x, u, target, draft
+
+
+def _outcome_counts(res, law):
+    keys = sorted(law)
+    idx = {k_: i for i, k_ in enumerate(keys)}
+    counts = np.zeros(len(keys) + 1)
+    for L, out in zip(res["accept_len"], res["out_tokens"]):
+        key = (int(L), *[int(v) for v in out[:L + 1]])
+        counts[idx.get(key, len(keys))] += 1
+    return counts, np.array([law[k_] for k_ in keys] + [0.0])
+
+
+def test_exact_outcome_law_v2_k2():
+    n = 200000
+    pt, pd, x, u, target, draft = _v2_k2_case(n)
+    law = _exact_outcomes_v2_k2(pt, pd)
+    assert abs(sum(law.values()) - 1.0) < 1e-12
+    res = oracle.verify_linear("stochastic", 1.0, target, draft, x, u, 2, F32)
+    counts, probs = _outcome_counts(res, law)
+    assert counts[-1] == 0, "an outcome outside the law"
+    assert R.chi2_pvalue(counts[:-1], probs[:-1]) > 1e-4
+
+
+@pytest.mark.parametrize("mut", [oracle.MUT_RESIDUAL_AS_TARGET, oracle.MUT_SWAPPED_RATIO, oracle.MUT_NO_BONUS])
+def test_planted_mistakes_fail_the_exact_law(mut):
+    n = 200000
+    pt, pd, x, u, target, draft = _v2_k2_case(n)
+    law = _exact_outcomes_v2_k2(pt, pd)
+    with oracle.mutation(mut):
+        res = oracle.verify_linear("stochastic", 1.0, target, draft, x, u, 2, F32)
+    counts, probs = _outcome_counts(res, law)
+    assert counts[-1] > 0 or R.chi2_pvalue(counts[:-1], probs[:-1]) < 1e-6
+
+
+def _fixed_draft_case(n, seed=91):
+    """Fixed logits and fixed draft tokens, fresh uniforms per trial: the accept
+    events are independent with P(accept_i) = min(1, q_i)."""
+    rng = np.random.default_rng(seed)
+    V, k, T = 6, 4, 0.8
+    t = rng.normal(0, 1.2, size=(k + 1, V)).astype(np.float32)
+    d = (t[:k] + rng.normal(0, 1.0, size=(k, V))).astype(np.float32)
+    # per position, the token whose ratio is closest to a spread of targets, so
+    # that the accept probabilities differ (one of them is 1)
+    ratios = [R.softmax(t[i].astype(np.float64), T) / R.softmax(d[i].astype(np.float64), T) for i in range(k)]
+    x = np.array([int(np.argmin(np.abs(r - want))) for r, want in zip(ratios, (0.8, 0.5, 1.6, 0.3))], np.int32)
+    q = np.array([ratios[i][x[i]] for i in range(k)])
+    u = _u24(rng, (n, k + 1))
+    target = np.ascontiguousarray(np.broadcast_to(t, (n, k + 1, V)))
+    draft = np.ascontiguousarray(np.broadcast_to(d, (n, k, V)))
+    xs = np.ascontiguousarray(np.broadcast_to(x, (n, k)))
+    return V, k, T, q, target, draft, xs, u
+
+
+def _check_accept_length_law(res, q, n, k):
+    L = res["accept_len"]
+    a = np.minimum(1.0, q)
+    for m in range(1, k + 1):
+        p = float(np.prod(a[:m]))
+        freq = float(np.mean(L >= m))
+        se = np.sqrt(max(p * (1 - p), 1e-12) / n)
+        if abs(freq - p) > 4 * se + 1e-12:
+            return False
+    mean = sum(float(np.prod(a[:m])) for m in range(1, k + 1))
+    se = np.std(L) / np.sqrt(n)
+    return abs(float(np.mean(L)) - mean) <= 4 * se + 1e-12
+
+
+def test_accept_length_law():
+    # P(L >= m) = prod_{i<m} min(1, q_i) for every m <= k, and E[L] = the sum of
+    # those products
+    n = 200000
+    V, k, T, q, target, draft, xs, u = _fixed_draft_case(n)
+    assert np.any(q < 0.9) and np.any(q > 0.2) and np.any(q > 1)
+    res = oracle.verify_linear("stochastic", T, target, draft, xs, u, V, F32)
+    assert _check_accept_length_law(res, q, n, k)
+
+
+def test_planted_swapped_ratio_fails_the_accept_length_law():
+    n = 200000
+    V, k, T, q, target, draft, xs, u = _fixed_draft_case(n)
+    with oracle.mutation(oracle.MUT_SWAPPED_RATIO):
+        res = oracle.verify_linear("stochastic", T, target, draft, xs, u, V, F32)
+    assert not _check_accept_length_law(res, q, n, k)

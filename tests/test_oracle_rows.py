@@ -94,3 +94,18 @@ def test_planted_row_mistakes_are_caught(mut):
         got = oracle.row_stats(enc, 500, R.DT_F32, 0.7)
     want = logsumexp(x / 0.7, axis=1)
     assert not np.allclose(got["lse"], want, rtol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lse_matches_two_pass_long_double(dtype):
+    # the textbook two-pass form: m = max x, then m/T + log(sum exp((x - m)/T)),
+    # each row summed in extended precision
+    rng = np.random.default_rng(2000 + dtype)
+    enc, x = _rows(rng, dtype, 5, 4099)
+    for T in (0.7, 1.3):
+        got = oracle.row_stats(enc, 4099, dtype, T)
+        for r in range(x.shape[0]):
+            xl = x[r].astype(np.longdouble)
+            m = xl.max()
+            want = m / np.longdouble(T) + np.log(np.sum(np.exp((xl - m) / np.longdouble(T))))
+            assert abs(float(got["lse"][r] - want)) <= 1e-13 * max(1.0, abs(float(want)))
