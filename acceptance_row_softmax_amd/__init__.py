@@ -136,31 +136,56 @@ def _need(t, name, dtype=None, device=None):
     return t
 
 
-def _stream(stream=None):
+def _torch_stream(stream=None):
+    """The torch stream a call runs on: `stream`, else the current stream."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def _stream(stream=None):
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
 
 
 class Workspace:
     """One zero-filled device workspace per (device, stream), grown on demand.
     Every call that completes leaves it all zeros, so it serves every entry point
-    and shape; calls on one stream never overlap, calls on two streams get two."""
+    and shape; calls on one stream never overlap, calls on two streams get two.
+    A buffer is allocated and zero-filled on the stream of the calls that use it,
+    so the fill is ordered before them and the allocator reuses a replaced buffer
+    only after that stream has passed it."""
 
     def __init__(self):
         self._bufs = {}
 
     def get(self, device, stream, nbytes: int):
         torch = _torch()
-        k = (str(device), stream.value)
+        k = (str(device), stream.cuda_stream)
         buf = self._bufs.get(k)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            with torch.cuda.stream(stream):
+                buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
             self._bufs[k] = buf
         return buf
 
 
 _WS = Workspace()
+
+
+def _check_out(out, shapes, dev):
+    """Preallocated outputs: each present tensor must be contiguous, on `dev` and of
+    its shape (int32, or float32 for the probabilities)."""
+    torch = _torch()
+    for name, shape in shapes.items():
+        t = out.get(name)
+        if t is None:
+            continue
+        want = torch.float32 if name in ("p_target", "p_draft") else torch.int32
+        _need(t, name, want, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"out[{name!r}] must have shape {shape}, got {tuple(t.shape)}")
+    for name in ("accept_len", "out_tokens"):
+        if out.get(name) is None:
+            raise ValueError(f"out must hold {name!r}")
 
 
 def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic",
@@ -206,28 +231,39 @@ def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic
             raise ValueError("uniforms must be [B][k+1]")
     else:
         uniforms = None
-    if out is None:
-        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
-               "out_tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
-               "err_flags": torch.empty(B, dtype=torch.int32, device=dev) if err_flags else None}
-        if stoch and with_probs:
-            out["p_target"] = torch.empty((B, k), dtype=torch.float32, device=dev)
-            out["p_draft"] = torch.empty((B, k), dtype=torch.float32, device=dev)
-    L = lib()
-    mcode = SV_STOCHASTIC if stoch else SV_GREEDY
-    nbytes = L.spec_verify_linear_workspace(B, k, V, dt, mcode)
-    s = _stream(stream)
-    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    ts = _torch_stream(stream)
     if seq_len is not None:
         _need(seq_len, "seq_len", torch.int32, dev)
+        if tuple(seq_len.shape) != (B,):
+            raise ValueError("seq_len must be [B]")
         cap = 0
         if history is not None:
             _need(history, "history", torch.int32, dev)
+            if history.dim() != 2 or history.shape[0] != B:
+                raise ValueError("history must be [B][capacity]")
             cap = history.shape[-1]
-        if shifted and "shifted" not in out:
-            out["shifted"] = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-        if "next_token" not in out:
-            out["next_token"] = torch.empty(B, dtype=torch.int32, device=dev)
+    if out is None:
+        with torch.cuda.stream(ts):
+            out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+                   "out_tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                   "err_flags": torch.empty(B, dtype=torch.int32, device=dev) if err_flags else None}
+            if stoch and with_probs:
+                out["p_target"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+                out["p_draft"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, {"accept_len": (B,), "out_tokens": (B, k + 1), "err_flags": (B,), "p_target": (B, k),
+                         "p_draft": (B, k), "shifted": (B, k + 1), "next_token": (B,)}, dev)
+    L = lib()
+    mcode = SV_STOCHASTIC if stoch else SV_GREEDY
+    nbytes = L.spec_verify_linear_workspace(B, k, V, dt, mcode)
+    s = ctypes.c_void_p(ts.cuda_stream)
+    ws = workspace if workspace is not None else _WS.get(dev, ts, nbytes)
+    if seq_len is not None:
+        with torch.cuda.stream(ts):
+            if shifted and "shifted" not in out:
+                out["shifted"] = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+            if "next_token" not in out:
+                out["next_token"] = torch.empty(B, dtype=torch.int32, device=dev)
         st = L.spec_verify_linear_commit(
             mcode, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
             _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("p_target")), _ptr(out.get("p_draft")),
@@ -283,15 +319,19 @@ def verify_tree(parent, cand_tokens, logits, uniforms, max_depth: int, mode: str
             raise ValueError("uniforms must be [B][n_nodes]")
     else:
         uniforms = None
-    acc = torch.empty(B, dtype=torch.int32, device=dev)
-    path = torch.empty((B, max_depth), dtype=torch.int32, device=dev)
-    out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
-    ef = torch.empty(B, dtype=torch.int32, device=dev)
+    if int(max_depth) < 0:
+        raise ValueError("max_depth must be >= 0")
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        path = torch.empty((B, max_depth), dtype=torch.int32, device=dev)
+        out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+        ef = torch.empty(B, dtype=torch.int32, device=dev)
     L = lib()
     mcode = SV_STOCHASTIC if stoch else SV_GREEDY
     nbytes = L.spec_verify_tree_workspace(B, N, V, dt, mcode)
-    s = _stream(stream)
-    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    s = ctypes.c_void_p(ts.cuda_stream)
+    ws = workspace if workspace is not None else _WS.get(dev, ts, nbytes)
     if typical:
         st = L.spec_verify_tree_typical(float(temperature), float(epsilon), float(delta), B, N, V, dt,
                                         _ptr(parent), stride, _ptr(cand_tokens), _ptr(logits),
@@ -316,14 +356,16 @@ def row_stats(x, temperature: float = 1.0, *, workspace=None, stream=None):
     V = x.shape[-1]
     rows = x.numel() // V
     dt = sv_dtype(x)
-    m = torch.empty(rows, dtype=torch.float32, device=dev)
-    lse = torch.empty(rows, dtype=torch.float32, device=dev)
-    am = torch.empty(rows, dtype=torch.int32, device=dev)
-    ef = torch.empty(rows, dtype=torch.int32, device=dev)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        m = torch.empty(rows, dtype=torch.float32, device=dev)
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+        am = torch.empty(rows, dtype=torch.int32, device=dev)
+        ef = torch.empty(rows, dtype=torch.int32, device=dev)
     L = lib()
     nbytes = L.spec_row_stats_workspace(rows, V, dt)
-    s = _stream(stream)
-    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    s = ctypes.c_void_p(ts.cuda_stream)
+    ws = workspace if workspace is not None else _WS.get(dev, ts, nbytes)
     st = L.spec_row_stats(dt, float(temperature), rows, V, _ptr(x), _ptr(m), _ptr(lse), _ptr(am),
                           _ptr(ef), _ptr(ws), ws.numel(), s)
     _check(st, "spec_row_stats")
@@ -337,20 +379,33 @@ def commit_linear(accept_len, out_tokens, draft_tokens, seq_len, history=None, *
     torch = _torch()
     i32 = torch.int32
     _need(accept_len, "accept_len", i32)
-    _need(out_tokens, "out_tokens", i32)
-    _need(seq_len, "seq_len", i32)
     dev = accept_len.device
+    _need(out_tokens, "out_tokens", i32, dev)
+    _need(seq_len, "seq_len", i32, dev)
+    if accept_len.dim() != 1:
+        raise ValueError("accept_len must be [B]")
     B = accept_len.shape[0]
+    if out_tokens.dim() != 2 or out_tokens.shape[0] != B or out_tokens.shape[1] < 1:
+        raise ValueError("out_tokens must be [B][k+1]")
     k = out_tokens.shape[-1] - 1
+    if tuple(seq_len.shape) != (B,):
+        raise ValueError("seq_len must be [B]")
     if draft_tokens is not None:
-        _need(draft_tokens, "draft_tokens", i32)
+        _need(draft_tokens, "draft_tokens", i32, dev)
+        if tuple(draft_tokens.shape) != (B, k):
+            raise ValueError("draft_tokens must be [B][k]")
+    elif shifted and k > 0:
+        raise ValueError("the shifted row needs draft_tokens [B][k]")
     cap = 0
     if history is not None:
-        _need(history, "history", i32)
+        _need(history, "history", i32, dev)
+        if history.dim() != 2 or history.shape[0] != B:
+            raise ValueError("history must be [B][capacity]")
         cap = history.shape[-1]
-    sh = torch.empty((B, k + 1), dtype=i32, device=dev) if shifted else None
-    nxt = torch.empty(B, dtype=i32, device=dev)
-    ef = torch.empty(B, dtype=i32, device=dev)
+    with torch.cuda.stream(_torch_stream(stream)):
+        sh = torch.empty((B, k + 1), dtype=i32, device=dev) if shifted else None
+        nxt = torch.empty(B, dtype=i32, device=dev)
+        ef = torch.empty(B, dtype=i32, device=dev)
     st = lib().spec_commit_linear(B, k, _ptr(accept_len), _ptr(out_tokens), _ptr(draft_tokens),
                                   _ptr(seq_len), _ptr(history), cap, _ptr(sh), _ptr(nxt), _ptr(ef),
                                   _stream(stream))
@@ -362,20 +417,28 @@ def sample(logits, uniforms=None, mode: str = "stochastic", temperature: float =
            stream=None):
     """One token per row of logits [..., V] (spec_sample); returns {"tokens", "err_flags"}."""
     torch = _torch()
+    if mode not in ("stochastic", "greedy"):
+        raise ValueError("mode must be 'greedy' or 'stochastic'")
     _need(logits, "logits")
     dev = logits.device
     V = logits.shape[-1]
     rows = logits.numel() // V
     m = SV_STOCHASTIC if mode == "stochastic" else SV_GREEDY
     if m == SV_STOCHASTIC:
-        _need(uniforms, "uniforms", torch.float32)
-    tok = torch.empty(rows, dtype=torch.int32, device=dev)
-    ef = torch.empty(rows, dtype=torch.int32, device=dev)
+        if uniforms is None:
+            raise ValueError("stochastic sampling needs uniforms")
+        _need(uniforms, "uniforms", torch.float32, dev)
+        if uniforms.numel() != rows:
+            raise ValueError(f"uniforms must hold one value per row ({rows}), got {uniforms.numel()}")
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        tok = torch.empty(rows, dtype=torch.int32, device=dev)
+        ef = torch.empty(rows, dtype=torch.int32, device=dev)
     L = lib()
     dt = sv_dtype(logits)
     nbytes = L.spec_sample_workspace(rows, V, dt)
-    s = _stream(stream)
-    ws = workspace if workspace is not None else _WS.get(dev, s, nbytes)
+    s = ctypes.c_void_p(ts.cuda_stream)
+    ws = workspace if workspace is not None else _WS.get(dev, ts, nbytes)
     st = L.spec_sample(m, float(temperature), rows, V, dt, _ptr(logits),
                        _ptr(uniforms) if m == SV_STOCHASTIC else None, _ptr(tok), _ptr(ef), _ptr(ws),
                        ws.numel(), s)
@@ -389,13 +452,18 @@ def tree_mask(parent, n_trees: int = 1, *, stream=None):
     torch = _torch()
     _need(parent, "parent", torch.int32)
     dev = parent.device
+    if parent.dim() not in (1, 2):
+        raise ValueError("parent must be [n] or [n_trees][n]")
     n = parent.shape[-1]
     stride = 0 if parent.dim() == 1 else n
     if parent.dim() > 1:
         n_trees = parent.shape[0]
+    if n_trees < 1 or n < 1:
+        raise ValueError("need at least one tree of at least one node")
     W = (n + 31) // 32
-    mask = torch.empty((n_trees, n, W), dtype=torch.int32, device=dev)
-    ef = torch.empty(n_trees, dtype=torch.int32, device=dev)
+    with torch.cuda.stream(_torch_stream(stream)):
+        mask = torch.empty((n_trees, n, W), dtype=torch.int32, device=dev)
+        ef = torch.empty(n_trees, dtype=torch.int32, device=dev)
     st = lib().spec_tree_mask(n_trees, n, _ptr(parent), stride, _ptr(mask), _ptr(ef), _stream(stream))
     _check(st, "spec_tree_mask")
     return {"mask": mask, "err_flags": ef}

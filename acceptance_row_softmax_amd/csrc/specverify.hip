@@ -151,7 +151,7 @@ struct LinearParams {
   uint32_t* res_cnt;    // [B]      residual waves done per sequence
   uint32_t* errw;       // [B]      error bits per sequence
   int64_t B, k, V;
-  int C, CP, R;         // chunks per row, streaming waves per row (C rounded up to 4), rows per sequence
+  int C, CP, R;         // chunks per row, streaming waves per row (C rounded up to a multiple of WPB), rows per sequence
   int G;                // chunks per residual wave (1 or 2; the kernel's template argument)
   float c0;
   uint32_t tag;
