@@ -79,6 +79,9 @@ def lib():
         L.spec_sample.argtypes = [i32, f32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]
         L.spec_tree_mask.restype = i32
         L.spec_tree_mask.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+        L.spec_verify_linear_static.restype = i32
+        L.spec_verify_linear_static.argtypes = [i32, f32, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, vp]
         L.spec_tree_build_greedy.restype = i64
         L.spec_tree_build_greedy.argtypes = [i64, i64, vp, i64, vp, vp, vp, vp]
         _lib = L
@@ -89,7 +92,8 @@ EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_t
             "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
             "spec_workspace_clear", "spec_verify_status_string", "spec_commit_linear",
             "spec_sample_workspace", "spec_sample", "spec_tree_mask", "spec_tree_build_greedy",
-            "spec_verify_tree_typical", "spec_verify_linear_commit")
+            "spec_verify_tree_typical", "spec_verify_linear_commit", "spec_verify_linear_static")
+SV_MAX_STATIC_WORKSPACE = 8 * 1024 * 1024
 
 
 def status_string(status: int) -> str:
@@ -275,6 +279,62 @@ def verify_linear(target, draft, draft_tokens, uniforms, mode: str = "stochastic
             _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("p_target")),
             _ptr(out.get("p_draft")), _ptr(out.get("err_flags")), _ptr(ws), ws.numel(), s)
     _check(st, "spec_verify_linear")
+    return out
+
+
+def verify_linear_static(target, draft, draft_tokens, uniforms, mode: str = "stochastic",
+                         temperature: float = 1.0, *, with_probs: bool = True, stream=None, out=None):
+    """verify_linear through spec_verify_linear_static: the library's own per-GPU
+    scratch array instead of a workspace (no device allocation by the library; the
+    outputs are allocated here unless ``out`` holds them). Calls that overlap on one
+    GPU race."""
+    torch = _torch()
+    stoch = mode == "stochastic"
+    if mode not in ("stochastic", "greedy"):
+        raise ValueError("mode must be 'greedy' or 'stochastic'")
+    _need(target, "target")
+    dev = target.device
+    if target.dim() != 3:
+        raise ValueError("target must be [B][k+1][V]")
+    B, k1, V = target.shape
+    k = k1 - 1
+    dt = sv_dtype(target)
+    if stoch and k > 0:
+        _need(draft, "draft", target.dtype, dev)
+        if tuple(draft.shape) != (B, k, V):
+            raise ValueError("draft must be [B][k][V]")
+    else:
+        draft = None
+    if k > 0:
+        _need(draft_tokens, "draft_tokens", torch.int32, dev)
+        if tuple(draft_tokens.shape) != (B, k):
+            raise ValueError("draft_tokens must be [B][k]")
+    else:
+        draft_tokens = None
+    if stoch:
+        _need(uniforms, "uniforms", torch.float32, dev)
+        if tuple(uniforms.shape) != (B, k + 1):
+            raise ValueError("uniforms must be [B][k+1]")
+    else:
+        uniforms = None
+    ts = _torch_stream(stream)
+    if out is None:
+        with torch.cuda.stream(ts):
+            out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+                   "out_tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                   "err_flags": torch.empty(B, dtype=torch.int32, device=dev)}
+            if stoch and with_probs:
+                out["p_target"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+                out["p_draft"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, {"accept_len": (B,), "out_tokens": (B, k + 1), "err_flags": (B,), "p_target": (B, k),
+                         "p_draft": (B, k)}, dev)
+    st = lib().spec_verify_linear_static(
+        SV_STOCHASTIC if stoch else SV_GREEDY, float(temperature), B, k, V, dt, _ptr(target), _ptr(draft),
+        _ptr(draft_tokens), _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("p_target")), _ptr(out.get("p_draft")), _ptr(out.get("err_flags")),
+        ctypes.c_void_p(ts.cuda_stream))
+    _check(st, "spec_verify_linear_static")
     return out
 
 

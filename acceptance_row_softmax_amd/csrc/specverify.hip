@@ -49,8 +49,14 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 using namespace sv;
+
+// Workspace of spec_verify_linear_static, one copy per GPU. In host code the name
+// stands for the host-side shadow, not a device address: only the address from
+// hipGetSymbolAddress (static_scratch()) is ever passed to a kernel or a fill.
+static __device__ __align__(256) unsigned char scratch[SV_MAX_STATIC_WORKSPACE];
 
 namespace {
 
@@ -1862,6 +1868,64 @@ sv_status spec_row_stats(sv_dtype dtype, float temperature, int64_t rows, int64_
   if (P.n_stream > MAX_WAVES) return SV_ELIMIT;
   P.tag = next_tag();
   return dispatch<RowStatsLauncher>(dtype, false, P, reinterpret_cast<hipStream_t>(stream));
+}
+
+// Device address of `scratch` on the GPU of `stream` (the current device for the
+// null stream), looked up once per device with that device current.
+constexpr int STATIC_MAX_DEVICES = 64;
+static void* g_scratch_addr[STATIC_MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+static sv_status static_scratch(hipStream_t s, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SV_EHIP;
+  int dev = cur;
+  if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) return SV_EHIP;
+  if (dev < 0 || dev >= STATIC_MAX_DEVICES) return SV_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return SV_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return SV_EHIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SV_OK;
+}
+
+sv_status spec_verify_linear_static(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                    sv_dtype dtype, const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* uniforms, int32_t* accept_len,
+                                    int32_t* out_tokens, float* p_target, float* p_draft, int32_t* err_flags,
+                                    sv_stream_t stream) {
+  // every check that needs no device comes first, so a rejected call touches nothing
+  if (!dtype_ok(dtype)) return SV_EDTYPE;
+  if (mode != SV_GREEDY && mode != SV_STOCHASTIC) return SV_EINVAL;
+  if (B < 0 || k < 0 || V < 1) return SV_EINVAL;
+  if (k > SV_MAX_K || !shape_ok(V, dtype)) return SV_ELIMIT;
+  if (B == 0) return SV_OK;
+  const size_t need = linear_layout(B, k, V, dtype, mode).total;
+  if (need > (size_t)SV_MAX_STATIC_WORKSPACE) return SV_ELIMIT;
+  LinearParams P{};
+  // arguments checked against a stand-in for the array: nothing is launched yet
+  sv_status st = linear_setup(P, mode, temperature, B, k, V, dtype, target_logits, draft_logits, draft_tokens,
+                              uniforms, accept_len, out_tokens, p_target, p_draft, err_flags,
+                              reinterpret_cast<void*>((uintptr_t)256), (size_t)SV_MAX_STATIC_WORKSPACE);
+  if (st != SV_OK) return st;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = static_scratch(hs, &ws);
+  if (st != SV_OK) return st;
+  // the previous call on this GPU normally leaves the region zero; a fill makes the
+  // call independent of how that one ended
+  st = spec_workspace_clear(ws, need, stream);
+  if (st != SV_OK) return st;
+  st = linear_setup(P, mode, temperature, B, k, V, dtype, target_logits, draft_logits, draft_tokens, uniforms,
+                    accept_len, out_tokens, p_target, p_draft, err_flags, ws, (size_t)SV_MAX_STATIC_WORKSPACE);
+  if (st != SV_OK) return st;
+  return dispatch<LinearLauncher>(dtype, mode == SV_STOCHASTIC, P, hs);
 }
 
 sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream) {

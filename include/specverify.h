@@ -292,6 +292,29 @@ int64_t spec_tree_build_greedy(int64_t K, int64_t S, const double* accuracy, int
 /* Zero-fill `bytes` of a 16-byte aligned workspace on `stream` with a fill kernel (no host sync). */
 sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream);
 
+/* ---------------------------------------------------------------- linear drafts, no allocation
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, outputs
+ * and results as spec_verify_linear, without the workspace: the kernels use a
+ * scratch array of SV_MAX_STATIC_WORKSPACE bytes that the library holds on each
+ * GPU it runs on until the process ends (its device address is looked up once per
+ * device, on the first call there). Each call zero-fills the part of that array it
+ * uses with a fill kernel on `stream` (no memset node) and then launches the
+ * verification there: two launches, no allocation, no host synchronisation.
+ * Shapes whose workspace (spec_verify_linear_workspace) exceeds the array return
+ * SV_ELIMIT before anything is launched; SV_EHIP if the array's address cannot be
+ * obtained. All calls on one GPU share its array: calls that overlap on one GPU
+ * (on different streams, or from different host threads) race and must not be
+ * issued.
+ */
+enum { SV_MAX_STATIC_WORKSPACE = 8 * 1024 * 1024 };
+
+sv_status spec_verify_linear_static(sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
+                                    sv_dtype dtype, const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* uniforms,
+                                    int32_t* accept_len, int32_t* out_tokens, float* p_target,
+                                    float* p_draft, int32_t* err_flags, sv_stream_t stream);
+
 /* Static description of a status code. */
 const char* spec_verify_status_string(sv_status status);
 
