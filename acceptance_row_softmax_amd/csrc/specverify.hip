@@ -74,6 +74,15 @@ struct Decision {
 };
 constexpr int DEC_WORDS = RecWords<Decision>::N;   // 8
 
+// Statistics of the (target, draft) row pair of one position, kept for the wave
+// that settles the first rejected position when that is another position.
+struct PairStat {
+  double Zt, Zd;
+  float Mt, Md;
+  int okt, okd;
+};
+constexpr int PST_WORDS = RecWords<PairStat>::N;   // 8
+
 struct ResPart {
   double s;
 };
@@ -134,6 +143,24 @@ __device__ __forceinline__ double residual_raw_sum(const Raw& rt, const Raw& rd,
 }
 
 // ------------------------------------------------------------------ linear drafts
+// Streaming waves: one per 8 KiB chunk of a row. A streaming wave reduces its
+// chunk to a partial, writes it as the chunk's record with a single store
+// instruction (lane j stores word j), adds one to its combine group's counter, and
+// ends: it never waits for either (greedy has no counter). Every word of a record
+// is a 32-bit value with the call's 32-bit tag (see put_rec):
+//   stochastic: word 0 the chunk's max (f32 bits), words 1 and 2 the low and high
+//               halves of its f64 weight sum relative to fl32(max*c0), word 3 the
+//               row's draft-token logit if the chunk holds that token, else
+//               NOT_HELD (a NaN pattern no decoded logit has)
+//   greedy:     word 0 the chunk's max, word 1 its lowest argmax
+// A combine group is finished by a wave of its own, dispatched after the group's
+// chunks: in stochastic mode it polls the group's counter (one lane) until every
+// chunk has counted, then reads the records, polling each word until it carries the
+// tag (a count can land before the record it follows); in greedy mode it polls the
+// records directly. It clears them behind the read. Groups:
+// greedy, every chunk of a sequence; stochastic, the target and draft rows of one
+// position (the pair finish runs that position's acceptance test), and the target
+// row after the last draft (the bonus draw).
 struct LinearParams {
   const char* target;
   const char* draft;
@@ -144,25 +171,27 @@ struct LinearParams {
   float* p_target;
   float* p_draft;
   int32_t* err_flags;
-  uint64_t* parts;      // [RQ][C]  Partial records
-  uint64_t* rows;       // [RQ]     RowStat records
+  uint64_t* seg;        // [RQ][C][RW] chunk records
+  uint64_t* pst;        // [B][k]   PairStat records (stochastic)
+  uint64_t* rks;        // [B]      RowStat records of target rows k (stochastic)
   uint64_t* dec;        // [B]      Decision records
   uint64_t* res;        // [B][C]   ResPart records
   uint64_t* tok;        // [B]      Token records
   uint64_t* prob;       // [B][k]   Probs records (stochastic)
-  uint32_t* row_cnt;    // [RQ]     chunks done per row
-  uint64_t* pair;       // [B][k]   per (target, draft) pair: each row's draft-token probability
-  uint64_t* state;      // [B]      sequence state words
-  uint32_t* fin;        // [B]      events per sequence
+  uint32_t* grp_cnt;    // [groups] segments counted per combine group
+  uint64_t* state;      // [B]      sequence state words (stochastic)
+  uint32_t* fin;        // [B]      events per sequence (stochastic)
   uint32_t* res_cnt;    // [B]      residual waves done per sequence
   uint32_t* errw;       // [B]      error bits per sequence
   int64_t B, k, V;
-  int C, CP, R;         // chunks per row, streaming waves per row (C rounded up to a multiple of WPB), rows per sequence
+  int C;                // chunks per row
+  int RW;               // words per chunk record
+  int EV;               // events per sequence (stochastic): k pair combines, target row k, the final token
   int G;                // chunks per residual wave (1 or 2; the kernel's template argument)
   float c0;
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
-  uint32_t res0, res1, tk0;   // stochastic, k > 0: first residual wave, end of the residual waves, first wave of target rows k
+  uint32_t tk0, res0;   // stochastic: first wave of the target rows k, first residual wave
   // optional commit by the emitting wave (spec_verify_linear_commit)
   int32_t* seq_len;     // [B] in/out
   int32_t* history;     // [B][capacity]
@@ -181,6 +210,29 @@ __device__ __forceinline__ int64_t row_q(const LinearParams& P, int64_t b, int64
   return 2 * P.k * P.B + b;
 }
 
+template <bool STOCH>
+__device__ __forceinline__ void row_of_q(const LinearParams& P, uint32_t q, int64_t& b, int64_t& i, int& which) {
+  if constexpr (STOCH) {
+    const uint32_t twoB = (uint32_t)(2 * P.B);
+    const uint32_t pairs = (uint32_t)P.k * twoB;
+    if (q < pairs) {
+      i = q / twoB;
+      const uint32_t rem = q - (uint32_t)i * twoB;
+      b = rem >> 1;
+      which = (int)(rem & 1u);
+    } else {
+      i = P.k;
+      b = q - pairs;
+      which = 0;
+    }
+  } else {
+    const uint32_t B32 = (uint32_t)P.B;
+    i = q / B32;
+    b = q - (uint32_t)i * B32;
+    which = 0;
+  }
+}
+
 template <int DT, bool STOCH>
 __device__ __forceinline__ const char* row_ptr(const LinearParams& P, int64_t b, int64_t i, int which) {
   constexpr int E = DTraits<DT>::E;
@@ -188,9 +240,89 @@ __device__ __forceinline__ const char* row_ptr(const LinearParams& P, int64_t b,
   return P.target + ((b * (P.k + 1) + i) * P.V) * E;
 }
 
-// Writes every output of sequence b (its last event): the first rejected
-// position from the state word, the final token from the token record, the
-// error bits, and the accepted drafts.
+__device__ __forceinline__ uint64_t seg_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void seg_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return ((uint64_t)tag << 32) | v; }
+
+// Waits (lane 0) until `total` segments have counted into a group counter, then
+// resets it; false on timeout.
+__device__ __forceinline__ bool wait_group(uint32_t* cnt, uint32_t total) {
+  bool ok = true;
+  if (lane_id() == 0) {
+    ok = false;
+    for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= total) { ok = true; break; }
+      __builtin_amdgcn_s_sleep(4);
+    }
+    counter_reset(cnt);
+  }
+  return __shfl((int)ok, 0) != 0;
+}
+
+constexpr uint32_t NOT_HELD = 0x7fffffffu;
+
+// The chunk partials of NR consecutive rows q0, q0+1 (stochastic records; lane l
+// holding chunks l + 64 t of each row, and the draft token's logit if some chunk of
+// the row holds it), each word polled until it carries the call's tag, then zeroed.
+// false on timeout.
+template <int NR>
+__device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, RowParts (&rp)[NR]) {
+  const int lane = lane_id();
+  uint64_t w[NR][MAX_ROUNDS][4];
+  bool ok = false;
+  for (int spin = 0; spin < SPIN_LIMIT && !ok; ++spin) {
+    bool mine = true;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int t = 0; t < MAX_ROUNDS; ++t) {
+        if (t * WAVE >= P.C) break;
+        const int c = t * WAVE + lane;
+        if (c < P.C) {
+          const uint64_t* q = P.seg + ((q0 + r) * P.C + c) * P.RW;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[r][t][e] = seg_load(q + e);
+            mine = mine && (uint32_t)(w[r][t][e] >> 32) == P.tag;
+          }
+        }
+      }
+    }
+    ok = __ballot(!mine) == 0ull;
+    if (!ok) __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    int xin = 0;
+    uint32_t xv = 0;
+#pragma unroll
+    for (int t = 0; t < MAX_ROUNDS; ++t) {
+      const int c = t * WAVE + lane;
+      const bool in = t * WAVE < P.C && c < P.C;
+      rp[r].m[t] = in ? __uint_as_float((uint32_t)w[r][t][0]) : -INFINITY;
+      rp[r].idx[t] = INT_SENTINEL;
+      rp[r].s[t] = in ? __longlong_as_double((long long)(((uint64_t)(uint32_t)w[r][t][2] << 32) |
+                                                        (uint32_t)w[r][t][1])) : 0.0;
+      if (in && (uint32_t)w[r][t][3] != NOT_HELD) {
+        xin = 1;
+        xv = (uint32_t)w[r][t][3];
+      }
+    }
+    const unsigned long long xm = __ballot(xin != 0);
+    rp[r].xin = xm != 0ull;
+    rp[r].xv = __uint_as_float((uint32_t)__shfl((int)xv, xm ? first_lane(xm) : 0));
+    rp[r].got = ok;
+    // leave the records zero for the next call
+    uint64_t* base = P.seg + (q0 + r) * P.C * P.RW;
+    for (int64_t o = lane; o < (int64_t)P.C * P.RW; o += WAVE) seg_store(base + o, 0);
+  }
+  return ok;
+}
+
 constexpr int TOKEN_UNKNOWN = INT_SENTINEL;
 
 // What the emission of sequence b reads (per lane), and the reading: issued as
@@ -223,15 +355,13 @@ __device__ __forceinline__ EmitIn emit_load(const LinearParams& P, int64_t b, bo
   if (STOCH && has) {
     in.pg = get_rec(P.prob + (b * k + lane) * PROB_WORDS, in.pr, P.tag);
     clear_rec<Probs>(P.prob + (b * k + lane) * PROB_WORDS);
+    clear_rec<PairStat>(P.pst + (b * k + lane) * PST_WORDS);
   }
   // leave the sequence's words and records zero for the next call
   if (lane == 0) counter_reset(P.state + b * SSTRIDE);
   if (lane == 1) counter_reset(P.errw + b * CSTRIDE);
   if (lane == 2 && !token_known) clear_rec<Token>(P.tok + b);
-  if (lane < P.R) {
-    const int64_t i = lane <= k ? lane : lane - k - 1;
-    clear_rec<RowStat>(P.rows + row_q<STOCH>(P, b, i, lane <= k ? 0 : 1) * ROW_WORDS);
-  }
+  if (STOCH && lane == 3) clear_rec<RowStat>(P.rks + b * ROW_WORDS);
   return in;
 }
 
@@ -298,12 +428,13 @@ struct Ev {
   int y;
 };
 
-// Counts n events of sequence b (R row combines and the final token); the last
-// one writes the outputs. The token event carries the token: if it is not the
-// last event, the token goes to the token record for the wave that will be.
+// Counts n events of sequence b (k pair combines, target row k and the final
+// token); the last one writes the outputs. The token event carries the token: if
+// it is not the last event, the token goes to the token record for the wave that
+// will be.
 template <int DT, bool STOCH>
 __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, bool token, int y, uint32_t n) {
-  const uint32_t total = (uint32_t)P.R + 1u;
+  const uint32_t total = (uint32_t)P.EV;
   uint32_t old = 0;
   if (lane_id() == 0) old = counter_add(P.fin + b * CSTRIDE, n);
   old = bcast(old);
@@ -319,228 +450,279 @@ __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, b
   linear_emit<DT, STOCH>(P, b, token ? y : TOKEN_UNKNOWN);
 }
 
-// Called after the state update old -> now by the wave that combined row
-// (mi, mwhich) with statistics `mine`. If this update settles L: in stochastic
-// mode with L < k, hand rows t_L, d_L to the residual waves; otherwise the final
-// token is known (the bonus draw, or argmax of t_L in greedy mode): return true
-// with it in y_out, for the caller to count with its own event.
-// `other` (lane 0, when have_other): the statistics of the other row of position
-// mi, which the pair combine has just read.
-template <int DT, bool STOCH>
+// Greedy finish of sequence b: polls the chunk records of its k+1 target rows
+// until every one carries the call's tag (greedy records are few, so no counter). Lane r holds the argmax of target row r (rows read two at a time); the
+// first position whose draft is not that argmax is L,
+// and the target's token is the argmax of row L. The sequence's outputs are
+// written here, with the same rules as the stochastic emission.
+template <int DT>
+__device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) {
+  const int lane = lane_id();
+  const int64_t k = P.k;
+  const int R = (int)k + 1;
+  bool ok = true;
+  int am = -1;
+#pragma unroll 1
+  for (int r0 = 0; r0 < R; r0 += 2) {
+    // two rows at a time, lane l reading chunks l + 64 t of each
+    uint64_t w[2][MAX_ROUNDS][2];
+    bool got = false;
+    for (int spin = 0; spin < SPIN_LIMIT && !got; ++spin) {
+      bool mine = true;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int t = 0; t < MAX_ROUNDS; ++t) {
+          const int c = t * WAVE + lane;
+          w[j][t][0] = tagged(__float_as_uint(-INFINITY), P.tag);
+          w[j][t][1] = tagged((uint32_t)INT_SENTINEL, P.tag);
+          if (t * WAVE < P.C && r0 + j < R && c < P.C) {
+            const uint64_t* p = P.seg + (row_q<false>(P, b, r0 + j, 0) * P.C + c) * P.RW;
+            w[j][t][0] = seg_load(p);
+            w[j][t][1] = seg_load(p + 1);
+          }
+          mine = mine && (uint32_t)(w[j][t][0] >> 32) == P.tag && (uint32_t)(w[j][t][1] >> 32) == P.tag;
+        }
+      }
+      got = __ballot(!mine) == 0ull;
+      if (!got) __builtin_amdgcn_s_sleep(4);
+    }
+    ok = ok && got;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float m = -INFINITY;
+      int idx = INT_SENTINEL;
+#pragma unroll
+      for (int t = 0; t < MAX_ROUNDS; ++t) {
+        if (t * WAVE >= P.C) break;
+        const int c = t * WAVE + lane;
+        if (r0 + j < R && c < P.C) {
+          uint64_t* p = P.seg + (row_q<false>(P, b, r0 + j, 0) * P.C + c) * P.RW;
+          seg_store(p, 0);
+          seg_store(p + 1, 0);
+        }
+        argmax_combine(m, idx, __uint_as_float((uint32_t)w[j][t][0]), (int)(uint32_t)w[j][t][1]);
+      }
+      wave_argmax(m, idx);
+      if (lane == r0 + j) am = (m > -INFINITY && idx != INT_SENTINEL) ? idx : -1;
+    }
+  }
+  const bool has = lane < k;
+  EmitIn in;
+  in.x = has ? P.tokens[b * k + lane] : 0;
+  in.ew = __ballot(lane < R && am < 0) ? (uint32_t)SV_ERR_ROW : 0u;
+  const unsigned long long miss = __ballot(has && in.x != am);
+  const int L = miss ? first_lane(miss) : (int)k;
+  in.s = L < k ? (1ull << (32 + L)) : 0ull;
+  in.t.y = ok ? -1 : -2;    // -2: a wait timed out (SV_ERR_INTERNAL)
+  in.tg = true;
+  in.pg = true;
+  in.pr.pt = in.pr.pd = NAN;
+  const int y = ok ? __shfl(am, L) : -2;
+  emit_store<DT, false>(P, b, in, y);
+}
+
+// Called after the state update old -> now of sequence b by the pair combine of
+// position mi (whose statistics are `mine`). If this update settles L < k, hand
+// rows t_L, d_L to the residual waves; if it settles L = k (every draft accepted
+// and the bonus drawn), the bonus token is final: return true with it in y_out,
+// for the caller to count with its own event.
+template <int DT>
 __device__ __forceinline__ bool linear_settle(const LinearParams& P, int64_t b, uint64_t old, uint64_t now,
-                                              const RowStat& mine, int64_t mi, int mwhich,
-                                              const RowStat& other, bool have_other, bool other_got, int& y_out) {
+                                              int64_t mi, const PairStat& mine, bool published, int& y_out) {
   const int k = (int)P.k;
   const int Ln = settled_L(now, k);
   if (Ln < 0 || settled_L(old, k) >= 0) return false;
-  const bool here = mi == Ln;
-  RowStat tl = mine;
-  bool got = true;
-  if (!(here && mwhich == 0)) {
-    if (here && have_other) {
-      tl = other;
-      got = other_got;
-    } else if (lane_id() == 0) {
-      got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 0) * ROW_WORDS, tl, P.tag);
-    }
-  }
-  if (STOCH && Ln < k) {
-    RowStat dl = mine;
-    if (!(here && mwhich == 1)) {
-      if (here && have_other) {
-        dl = other;
-        got = other_got && got;
-      } else if (lane_id() == 0) {
-        got = get_rec(P.rows + row_q<STOCH>(P, b, Ln, 1) * ROW_WORDS, dl, P.tag) && got;
-      }
-    }
-    if (lane_id() == 0) {
+  if (Ln < k) {
+    if (lane_id() == 0 && !published) {
+      PairStat ps = mine;
+      bool got = true;
+      if (Ln != mi) got = get_rec(P.pst + (b * k + Ln) * PST_WORDS, ps, P.tag);
       Decision d;
       d.L = Ln;
-      d.kind = (got && tl.ok == 1 && dl.ok == 1) ? 1 : 2;
-      d.Mt = tl.M;
-      d.Md = dl.M;
-      d.Zt = tl.Z;
-      d.Zd = dl.Z;
+      d.kind = (got && ps.okt && ps.okd) ? 1 : 2;
+      d.Mt = ps.Mt;
+      d.Md = ps.Md;
+      d.Zt = ps.Zt;
+      d.Zd = ps.Zd;
       put_rec(P.dec + b * DEC_WORDS, d, P.tag);
     }
     return false;   // the residual waves draw the token
   }
   int y = 0;
-  if (lane_id() == 0) y = !got ? -2 : (tl.ok != 1 ? -1 : (STOCH ? tl.y : tl.argmax));
+  if (lane_id() == 0) {
+    RowStat rk;
+    const bool got = get_rec(P.rks + b * ROW_WORDS, rk, P.tag);
+    y = !got ? -2 : (rk.ok != 1 ? -1 : rk.y);
+  }
   y_out = bcast(y);
-  return true;   // the final token is known
+  return true;
 }
 
-// Combines row q (b, position i, target/draft) once its last chunk is done.
-template <int DT, bool STOCH>
-__device__ __forceinline__ Ev linear_combine(const LinearParams& P, int64_t q, int64_t b, int64_t i, int which) {
+// Stochastic, position i < k of sequence b: combines rows t_i and d_i once all of
+// their segments are in, and runs the acceptance test u_i < p_t,i(x_i) / p_d,i(x_i).
+template <int DT>
+__device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int64_t i) {
   const int lane = lane_id();
   const int64_t k = P.k, V = P.V;
-  const char* row = row_ptr<DT, STOCH>(P, b, i, which);
-  // the draft token of this position; its logit in this row comes with the partials
-  const int x = (i < k) ? P.tokens[b * k + i] : -1;
-  // target row k: the sequence's state, read with the partials (an earlier
-  // position already rejected makes the bonus draw useless)
-  uint64_t sn = 0;
-  if (STOCH && i == k && lane == 0) sn = state_load(P.state + b * SSTRIDE);
-  const RowParts rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
-  const float xv = rp.xv;
+  const int x = P.tokens[b * k + i];
+  const int64_t qt = row_q<true>(P, b, i, 0);
+  bool got = wait_group(P.grp_cnt + (b * k + i) * CSTRIDE, (uint32_t)(2 * P.C));
+  // the state as it is now, read with the records: if every earlier position is
+  // already accepted, a rejection here settles L = i without the state update's
+  // round trip
+  uint64_t se = 0;
+  if (lane == 0 && i > 0) se = state_load(P.state + b * SSTRIDE);
+  RowParts rp[2];
+  got = read_rows<2>(P, qt, rp) && got;
   double wl[MAX_ROUNDS];
-  const RowSums rs = row_sums<STOCH>(rp, P.c0, wl);
+  const RowSums st = row_sums<true, false>(rp[0], P.c0, wl, P.C);
+  const RowSums sd = row_sums<true, false>(rp[1], P.c0, wl, P.C);
+  const RowParts& rt = rp[0];
+  const RowParts& rd = rp[1];
+  const bool okt = got && st.M > -INFINITY && __builtin_isfinite(st.Z) && st.Z > 0.0;
+  const bool okd = got && sd.M > -INFINITY && __builtin_isfinite(sd.Z) && sd.Z > 0.0;
+  const bool xok = x >= 0 && x < V;
+  double pxt = NAN, pxd = NAN;
+  if (okt && xok && rt.xin) pxt = exp2(((double)rt.xv - (double)st.M) * (double)P.c0) / st.Z;
+  if (okd && xok && rd.xin) pxd = exp2(((double)rd.xv - (double)sd.M) * (double)P.c0) / sd.Z;
+  // Both probabilities as fp32: the ratio keeps about 1e-7 relative. Below the
+  // smallest normal fp32 (or at zero) that no longer holds, and the test takes both
+  // in fp64.
+  const float ft = okt ? (float)pxt : NAN, fd = okd ? (float)pxd : NAN;
+  double pt = (double)ft, pd = (double)fd;
+  if (ft < FLT_MIN || fd < FLT_MIN) {   // NaN (an unusable row) compares false
+    pt = okt ? pxt : (double)NAN;
+    pd = okd ? pxd : (double)NAN;
+  }
+  double qr;
+  if (pd > 0.0) qr = pt / pd;
+  else qr = (pt > 0.0) ? INFINITY : NAN;
+  const bool ok = !isnan(pt) && !isnan(pd);   // an unusable row rejects
+  const bool acc = ok && (double)P.uniforms[b * (k + 1) + i] < qr;   // NaN ratio rejects
+  const uint64_t bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
+  PairStat ps;
+  ps.Zt = st.Z;
+  ps.Zd = sd.Z;
+  ps.Mt = st.M;
+  ps.Md = sd.M;
+  ps.okt = okt;
+  ps.okd = okd;
+  se = bcast(se);
+  const uint64_t before = (1ull << i) - 1;
+  const bool early = !acc && (se & before) == before && ((se >> 32) & before) == 0;
+  if (early) {
+    // this wave's state update is the one that settles L = i (see linear_settle)
+    Decision d;
+    d.L = (int)i;
+    d.kind = (okt && okd) ? 1 : 2;
+    d.Mt = ps.Mt;
+    d.Md = ps.Md;
+    d.Zt = ps.Zt;
+    d.Zd = ps.Zd;
+    put_rec_wave(P.dec + b * DEC_WORDS, d, P.tag);
+  }
+  // The state update first: an atomic whose result the wave waits for also waits
+  // for every store the wave issued before it, and the records below are read by
+  // polling, so they may land later.
+  uint64_t olds = 0;
+  if (lane == 0) {
+    if (!got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
+    else if (!okt || !okd) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_ROW);
+    olds = state_or(P.state + b * SSTRIDE, bits);
+  }
+  Probs pr;
+  pr.pt = (float)pt;
+  pr.pd = (float)pd;
+  put_rec_wave(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
+  put_rec_wave(P.pst + (b * k + i) * PST_WORDS, ps, P.tag);
+  olds = bcast(olds);
+  if (lane == 0) {
+    // The update that decides the last position with none rejected tells the
+    // residual waves that L = k (they have nothing to draw), without waiting for
+    // target row k: those waves are dispatched before it.
+    const uint64_t mk = (1ull << k) - 1, now = olds | bits;
+    if ((now & mk) == mk && ((now >> 32) & mk) == 0 && (olds & mk) != mk) {
+      Decision d;
+      d.L = (int)k;
+      d.kind = 0;
+      d.Mt = d.Md = 0.0f;
+      d.Zt = d.Zd = 0.0;
+      put_rec(P.dec + b * DEC_WORDS, d, P.tag);
+    }
+  }
+  Ev ev{b, 1u, false, 0};
+  if (linear_settle<DT>(P, b, olds, olds | bits, i, ps, early, ev.y)) {
+    ev.token = true;   // and the final token
+    ev.n = 2;
+  }
+  return ev;
+}
+
+// Stochastic, target row k of sequence b (the row after the last draft): combined
+// once all of its segments are in; draws the bonus token from p_t,k unless an
+// earlier position is already rejected.
+template <int DT>
+__device__ __forceinline__ Ev rowk_finish(const LinearParams& P, int64_t b) {
+  const int lane = lane_id();
+  const int64_t k = P.k, V = P.V;
+  bool got = wait_group(P.grp_cnt + (P.B * k + b) * CSTRIDE, (uint32_t)P.C);
+  uint64_t sn = 0;
+  if (lane == 0) sn = state_load(P.state + b * SSTRIDE);   // read with the records
+  RowParts rpa[1];
+  got = read_rows<1>(P, row_q<true>(P, b, k, 0), rpa) && got;
+  const RowParts& rp = rpa[0];
+  double wl[MAX_ROUNDS];
+  const RowSums rs = row_sums<true, false>(rp, P.c0, wl, P.C);
   RowStat st;
   st.Z = rs.Z;
   st.M = rs.M;
   st.argmax = rs.argmax;
   st.px = NAN;
   st.y = -1;
-  const bool usable = STOCH ? (rs.M > -INFINITY && __builtin_isfinite(rs.Z) && rs.Z > 0.0) : (rs.argmax >= 0);
-  st.ok = rp.got ? (usable ? 1 : 0) : -1;
-  if (STOCH && i < k && st.ok == 1 && x >= 0 && x < V && rp.xin)
-    st.px = exp2(((double)xv - (double)rs.M) * (double)P.c0) / rs.Z;
-  if (STOCH && i == k && st.ok == 1) {
-    // the bonus draw, unless an earlier position has already been rejected
-    sn = bcast(sn);
-    if (settled_L(sn, (int)k) < 0)
-      st.y = softmax_draw<DT>(row, V, P.C, P.c0, P.uniforms[b * (k + 1) + k], rp, rs, wl);
-  }
+  st.ok = !got ? -1 : ((rs.M > -INFINITY && __builtin_isfinite(rs.Z) && rs.Z > 0.0) ? 1 : 0);
+  sn = bcast(sn);
+  if (st.ok == 1 && settled_L(sn, (int)k) < 0)
+    st.y = softmax_draw<DT>(row_ptr<DT, true>(P, b, k, 0), V, P.C, P.c0, P.uniforms[b * (k + 1) + k], rp, rs, wl);
+  uint64_t olds = 0;
   if (lane == 0) {
     if (st.ok != 1) error_or(P.errw + b * CSTRIDE, (uint32_t)(st.ok < 0 ? SV_ERR_INTERNAL : SV_ERR_ROW));
-    put_rec(P.rows + q * ROW_WORDS, st, P.tag);
+    olds = state_or(P.state + b * SSTRIDE, BONUS_BIT);   // before the record (see pair_finish)
   }
-
-  uint64_t bits = 0;
-  bool update = true;
-  RowStat other;            // stochastic pair: the other row of position i (lane 0)
-  bool have_other = false, other_got = true;
-  bool read_early = false;  // its record was read for the acceptance test
-  if (i == k) {
-    bits = BONUS_BIT;   // the row after the last draft is combined (and drawn)
-  } else if constexpr (!STOCH) {
-    const bool acc = st.ok == 1 && x == st.argmax;
-    bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
-  } else {
-    // Each row of the pair ORs its probability of the draft token (fp32, sign bit
-    // set as the mark that it is there; NaN for an unusable row) into its half of
-    // the pair's word; the atomic's old value gives the second row the first's.
-    const float pxf = st.ok == 1 ? (float)st.px : NAN;
-    const uint64_t half = (uint64_t)(0x80000000u | (__float_as_uint(pxf) & 0x7fffffffu)) << (32 * which);
-    uint64_t* pw = P.pair + (b * k + i) * SSTRIDE;
-    uint64_t oldw = 0;
-    if (lane == 0) oldw = state_or(pw, half);
-    oldw = bcast(oldw);
-    const uint32_t oh = (uint32_t)(oldw >> (32 * (1 - which)));
-    update = (oh & 0x80000000u) != 0;
-    if (update) {
-      // second row of the pair: the acceptance test of position i
-      have_other = true;
-      // Both probabilities as fp32, whichever row arrives second: the ratio keeps
-      // about 1e-7 relative. Below the smallest normal fp32 (or at zero) that no
-      // longer holds, and the test takes both in fp64, the other's from its record.
-      const float of = __uint_as_float(oh & 0x7fffffffu);
-      double opx = (double)of;
-      double mpx = (double)pxf;
-      if (pxf < FLT_MIN || of < FLT_MIN) {   // NaN (an unusable row) compares false
-        read_early = true;
-        double o = NAN;
-        if (lane == 0) {
-          other_got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);
-          if (other_got && other.ok == 1) o = other.px;
-          if (!other_got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
-        }
-        opx = __shfl(o, 0);
-        mpx = st.ok == 1 ? st.px : (double)NAN;
-      }
-      const double pt = which == 0 ? mpx : opx;
-      const double pd = which == 0 ? opx : mpx;
-      double qr;
-      if (pd > 0.0) qr = pt / pd;
-      else qr = (pt > 0.0) ? INFINITY : NAN;
-      const bool ok = !isnan(pt) && !isnan(pd);   // an unusable row rejects
-      const bool acc = ok && (double)P.uniforms[b * (k + 1) + i] < qr;   // NaN ratio rejects
-      bits = (1ull << i) | (acc ? 0ull : (1ull << (32 + i)));
-      if (lane == 0) {
-        counter_reset(pw);
-        Probs pr;
-        pr.pt = (float)pt;
-        pr.pd = (float)pd;
-        put_rec(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
-      }
-    }
-  }
-  Ev ev;
-  ev.b = b;
-  ev.n = 1;   // the row's combine
-  ev.token = false;
-  ev.y = 0;
-  if (update) {
-    uint64_t olds = 0;
-    if (lane == 0) olds = state_or(P.state + b * SSTRIDE, bits);
-    if (STOCH && have_other && !read_early && lane == 0) {
-      // the other row's statistics, for a decision settled here; read while the
-      // state update is in flight
-      other_got = get_rec(P.rows + row_q<true>(P, b, i, 1 - which) * ROW_WORDS, other, P.tag);
-      if (!other_got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
-    }
-    olds = bcast(olds);
-    if (STOCH && i < k && lane == 0) {
-      // The update that decides the last position with none rejected tells the
-      // residual waves that L = k (they have nothing to draw), without waiting for
-      // target row k: those waves are dispatched before it.
-      const uint64_t mk = (1ull << k) - 1, now = olds | bits;
-      if ((now & mk) == mk && ((now >> 32) & mk) == 0 && (olds & mk) != mk) {
-        Decision d;
-        d.L = (int)k;
-        d.kind = 0;
-        d.Mt = d.Md = 0.0f;
-        d.Zt = d.Zd = 0.0;
-        put_rec(P.dec + b * DEC_WORDS, d, P.tag);
-      }
-    }
-    if (linear_settle<DT, STOCH>(P, b, olds, olds | bits, st, i, which, other, have_other, other_got, ev.y)) {
-      ev.token = true;   // and the final token
-      ev.n = 2;
-    }
-  }
-  return ev;
+  put_rec_wave(P.rks + b * ROW_WORDS, st, P.tag);
+  olds = bcast(olds);
+  const int Ln = settled_L(olds | BONUS_BIT, (int)k);
+  if (Ln == (int)k && settled_L(olds, (int)k) < 0) return Ev{b, 2u, true, st.y};   // the bonus token is final
+  return Ev{b, 1u, false, 0};
 }
 
+// Streaming wave of chunk c of row q: the chunk's partial goes out as its record,
+// then one count into its combine group. Nothing here waits for another wave.
 template <int DT, bool STOCH>
-__device__ __forceinline__ Ev linear_stream_wave(const LinearParams& P, uint32_t q32, uint32_t c32) {
-  const int64_t q = q32, c = c32;
+__device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_t q32, uint32_t c32) {
+  const int lane = lane_id();
   int64_t b, i;
   int which;
-  if constexpr (STOCH) {
-    const uint32_t twoB = (uint32_t)(2 * P.B);
-    const uint32_t pairs = (uint32_t)(P.k) * twoB;
-    if (q32 < pairs) {
-      i = q32 / twoB;
-      const uint32_t rem = q32 - (uint32_t)i * twoB;
-      b = rem >> 1;
-      which = (int)(rem & 1u);
-    } else {
-      i = P.k;
-      b = q32 - pairs;
-      which = 0;
-    }
-  } else {
-    const uint32_t B32 = (uint32_t)P.B;
-    i = q32 / B32;
-    b = q32 - (uint32_t)i * B32;
-    which = 0;
-  }
+  row_of_q<STOCH>(P, q32, b, i, which);
   const char* row = row_ptr<DT, STOCH>(P, b, i, which);
   const int64_t x = (STOCH && i < P.k) ? (int64_t)P.tokens[b * P.k + i] : -1;
-  const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c, P.c0, x);
-  uint32_t old = 0;
-  if (lane_id() == 0) {
-    put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
-    old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
+  const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c32, P.c0, x);
+  uint64_t* rec = P.seg + ((int64_t)q32 * P.C + c32) * P.RW;
+  if constexpr (STOCH) {
+    const uint64_t sb = (uint64_t)__double_as_longlong(p.s);
+    const uint32_t word = lane == 0 ? __float_as_uint(p.m)
+                        : lane == 1 ? (uint32_t)sb
+                        : lane == 2 ? (uint32_t)(sb >> 32)
+                        : (p.xin ? __float_as_uint(p.xv) : NOT_HELD);
+    if (lane < 4) seg_store(rec + lane, tagged(word, P.tag));
+  } else {
+    if (lane < 2) seg_store(rec + lane, tagged(lane == 0 ? __float_as_uint(p.m) : (uint32_t)p.idx, P.tag));
   }
-  old = bcast(old);
-  if (old + 1 != (uint32_t)P.C) return Ev{0, 0u, false, 0};
-  if (lane_id() == 0) counter_reset(P.row_cnt + q * CSTRIDE);
-  return linear_combine<DT, STOCH>(P, q, b, i, which);
+  if constexpr (STOCH) {
+    const uint32_t grp = (uint32_t)(i < P.k ? b * P.k + i : P.B * P.k + b);
+    if (lane == 0) (void)__hip_atomic_fetch_add(P.grp_cnt + (int64_t)grp * CSTRIDE, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Residual wave (b, g), dispatched after the streaming waves of every row a
@@ -619,7 +801,7 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
         clear_rec<ResPart>(rec);
       }
     }
-    const bool last = bcast(fo) + 1 == (uint32_t)P.R + 1u;
+    const bool last = bcast(fo) + 1 == (uint32_t)P.EV;
     const float u = P.uniforms[b * (k + 1) + k];
     ChunkPick pk;
     pk.c = -1;
@@ -683,59 +865,89 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
 }
 
-constexpr int64_t RESID_GROUP_WAVES = 4096;
-
-// Wave roles of a linear launch: the streaming waves (rows in order, see
-// stream_coords); in stochastic mode with k > 0 the streaming waves of the rows of
-// positions 0..k-1, one residual wave per (sequence, G chunks), idle waves up to a
-// multiple of 8 workgroups, and the streaming waves of the target rows k. Residual
-// waves follow every row their decision depends on.
+// Wave roles of a linear launch, in dispatch order. Greedy: the chunk waves of
+// every row (rows of position 0 of every sequence, then position 1, ...), then one
+// finishing wave per sequence. Stochastic: for each position i < k, the chunk
+// waves of its target and draft rows followed by one pair-finishing wave per
+// sequence; then the chunk waves of the target rows k, each row followed by the
+// wave that finishes it; then the residual waves, one per (sequence, G chunks).
+// Every wave that waits follows the waves it waits for. The residual waves come
+// last so that they hold no slot while rows stream: by then most of them find
+// their decision made, and those of sequences that rejected nothing end at once.
+enum RoleKind { ROLE_IDLE = 0, ROLE_STREAM, ROLE_RESID, ROLE_PAIR, ROLE_ROWK, ROLE_GREEDY };
 struct Role {
-  int kind;       // 0 idle, 1 streaming (q, c), 2 residual (b, c)
-  uint32_t q, b, c;
+  int kind;
+  uint32_t q, b, c;   // stream: row q, chunk c; residual: sequence b, group c; finishers: sequence b, position c
 };
 
 template <bool STOCH, int G>
 __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
   Role r;
-  r.kind = 0;
+  r.kind = ROLE_IDLE;
   r.q = r.b = r.c = 0;
-  const uint32_t CP = (uint32_t)P.CP;
-  const uint32_t C = (uint32_t)P.C;
-  if (!STOCH || P.k == 0) {
-    stream_coords(w, CP, (uint32_t)(P.B * P.R), r.q, r.c);
-    r.kind = r.c < C ? 1 : 0;
-  } else if (w < P.res0) {
-    // the rows of positions 0..k-1
-    stream_coords(w, CP, (uint32_t)(2 * P.k * P.B), r.q, r.c);
-    r.kind = r.c < C ? 1 : 0;
-  } else if (w < P.res1) {
-    const uint32_t v = w - P.res0;
-    const uint32_t CG = (C + G - 1) / G;
-    r.b = v / CG;
-    r.c = v - r.b * CG;
-    r.kind = 2;
-  } else if (w >= P.tk0) {
-    // target rows k, from a multiple of 8 workgroups so that rows keep to one XCD
-    stream_coords(w - P.tk0, CP, (uint32_t)P.B, r.q, r.c);
-    r.q += (uint32_t)(2 * P.k * P.B);
-    r.kind = r.c < C ? 1 : 0;
+  const uint32_t NS = (uint32_t)P.C, B = (uint32_t)P.B;
+  if constexpr (!STOCH) {
+    const uint32_t ns = (uint32_t)(P.k + 1) * B * NS;
+    if (w < ns) {
+      r.q = w / NS;
+      r.c = w - r.q * NS;
+      r.kind = ROLE_STREAM;
+    } else {
+      r.b = w - ns;
+      r.kind = ROLE_GREEDY;
+    }
+  } else {
+    if (w < P.tk0) {
+      const uint32_t PS = 2 * B * NS + B;   // waves per position
+      const uint32_t pos = w / PS, v = w - pos * PS;
+      if (v < 2 * B * NS) {
+        r.q = pos * 2 * B + v / NS;
+        r.c = v % NS;
+        r.kind = ROLE_STREAM;
+      } else {
+        r.b = v - 2 * B * NS;
+        r.c = pos;
+        r.kind = ROLE_PAIR;
+      }
+    } else if (w < P.res0) {
+      // per sequence: the C chunk waves of its target row k, then its finisher
+      const uint32_t v = w - P.tk0;
+      r.b = v / (NS + 1);
+      const uint32_t e = v - r.b * (NS + 1);
+      if (e < NS) {
+        r.q = (uint32_t)(2 * P.k) * B + r.b;
+        r.c = e;
+        r.kind = ROLE_STREAM;
+      } else {
+        r.kind = ROLE_ROWK;
+      }
+    } else {
+      const uint32_t CG = ((uint32_t)P.C + G - 1) / G;
+      const uint32_t v = w - P.res0;
+      r.b = v / CG;
+      r.c = v - r.b * CG;
+      r.kind = ROLE_RESID;
+    }
   }
   return r;
 }
 
 template <int DT, bool STOCH, int G>
-__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void linear_kernel(LinearParams P) {
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(3))) void linear_kernel(LinearParams P) {
   const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
   if (w >= P.n_waves) return;
   const Role r = linear_role<STOCH, G>(P, (uint32_t)w);
   Ev ev{0, 0u, false, 0};
-  if (r.kind == 1) {
-    ev = linear_stream_wave<DT, STOCH>(P, r.q, r.c);
-  } else if (r.kind == 2) {
-    if constexpr (STOCH) ev = linear_residual_wave<DT, G>(P, r.b, r.c);
+  if (r.kind == ROLE_STREAM) {
+    linear_chunk_wave<DT, STOCH>(P, r.q, r.c);
+  } else if constexpr (STOCH) {
+    if (r.kind == ROLE_PAIR) ev = pair_finish<DT>(P, r.b, r.c);
+    else if (r.kind == ROLE_ROWK) ev = rowk_finish<DT>(P, r.b);
+    else if (r.kind == ROLE_RESID) ev = linear_residual_wave<DT, G>(P, r.b, r.c);
+  } else {
+    if (r.kind == ROLE_GREEDY) greedy_finish<DT>(P, r.b);
   }
-  if (ev.n) linear_event<DT, STOCH>(P, ev.b, ev.token, ev.y, ev.n);
+  if (STOCH && ev.n) linear_event<DT, STOCH>(P, ev.b, ev.token, ev.y, ev.n);
 }
 
 // ------------------------------------------------------------------ trees
@@ -1519,13 +1731,26 @@ __global__ __launch_bounds__(BLOCK) void clear_kernel(unsigned char* p, size_t b
 }
 
 // ------------------------------------------------------------------ host side
+struct LinearShape {
+  int64_t R, RQ, C, RW, groups;
+};
+
+inline LinearShape linear_shape(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
+  LinearShape s;
+  const bool stoch = mode == SV_STOCHASTIC;
+  s.R = stoch ? 2 * k + 1 : k + 1;
+  s.RQ = B * s.R;
+  s.C = chunks_per_row(V, dt);
+  s.RW = stoch ? 4 : 2;
+  s.groups = stoch ? B * (k + 1) : B;
+  return s;
+}
+
 Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
-  const int64_t R = (mode == SV_STOCHASTIC) ? 2 * k + 1 : k + 1;
-  const int64_t RQ = B * R;
-  const int64_t C = chunks_per_row(V, dt);
-  return make_layout({(size_t)(RQ * C) * PART_WORDS * 8, (size_t)RQ * ROW_WORDS * 8, (size_t)B * DEC_WORDS * 8,
-                      (size_t)(B * C) * RES_WORDS * 8, (size_t)B * 8, (size_t)(RQ * CSTRIDE) * 4,
-                      (size_t)(B * k * SSTRIDE) * 8, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
+  const LinearShape s = linear_shape(B, k, V, dt, mode);
+  return make_layout({(size_t)(s.RQ * s.C * s.RW) * 8, (size_t)(B * k) * PST_WORDS * 8, (size_t)B * ROW_WORDS * 8,
+                      (size_t)B * DEC_WORDS * 8, (size_t)(B * s.C) * RES_WORDS * 8, (size_t)B * 8,
+                      (size_t)(s.groups * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
                       (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8});
 }
 
@@ -1544,12 +1769,6 @@ Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
 template <int DT, bool STOCH>
 struct LinearLauncher {
   static sv_status run(const LinearParams& P, hipStream_t s) {
-    if constexpr (STOCH) {
-      if (P.G == 2) {
-        hipLaunchKernelGGL((linear_kernel<DT, true, 2>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
-        return launch_status();
-      }
-    }
     hipLaunchKernelGGL((linear_kernel<DT, STOCH, 1>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
     return launch_status();
   }
@@ -1641,14 +1860,15 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.p_target = stoch ? p_target : nullptr;
   P.p_draft = stoch ? p_draft : nullptr;
   P.err_flags = err_flags;
+  const LinearShape sh = linear_shape(B, k, V, dtype, mode);
   char* ws = static_cast<char*>(workspace);
-  P.parts = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
-  P.rows = reinterpret_cast<uint64_t*>(ws + lay.off[1]);
-  P.dec = reinterpret_cast<uint64_t*>(ws + lay.off[2]);
-  P.res = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
-  P.tok = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
-  P.row_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[5]);
-  P.pair = reinterpret_cast<uint64_t*>(ws + lay.off[6]);
+  P.seg = reinterpret_cast<uint64_t*>(ws + lay.off[0]);
+  P.pst = reinterpret_cast<uint64_t*>(ws + lay.off[1]);
+  P.rks = reinterpret_cast<uint64_t*>(ws + lay.off[2]);
+  P.dec = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
+  P.res = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
+  P.tok = reinterpret_cast<uint64_t*>(ws + lay.off[5]);
+  P.grp_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[6]);
   P.state = reinterpret_cast<uint64_t*>(ws + lay.off[7]);
   P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
   P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
@@ -1657,24 +1877,21 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.B = B;
   P.k = k;
   P.V = V;
-  P.R = (int)(stoch ? 2 * k + 1 : k + 1);
-  P.C = (int)chunks_per_row(V, dtype);
-  P.CP = (P.C + WPB - 1) / WPB * WPB;
+  P.C = (int)sh.C;
+  P.RW = (int)sh.RW;
+  P.EV = (int)(k + 2);
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  // residual waves: one per chunk, or one per two chunks when a launch would have
-  // more than RESID_GROUP_WAVES of them (then their dispatch sets the time)
-  P.G = (stoch && B * P.C > RESID_GROUP_WAVES) ? 2 : 1;
-  P.n_waves = B * P.R * P.CP;
-  P.res0 = P.res1 = P.tk0 = 0;
-  if (stoch && k > 0) {
-    // rows of positions 0..k-1, residual waves, padding to a multiple of 8
-    // workgroups, target rows k
-    const int64_t r0 = 2 * k * B * P.CP, r1 = r0 + B * ((P.C + P.G - 1) / P.G);
-    const int64_t t0 = (r1 + 8 * WPB - 1) / (8 * WPB) * (8 * WPB);
-    P.n_waves = t0 + B * P.CP;
-    P.res0 = (uint32_t)r0;
-    P.res1 = (uint32_t)r1;
-    P.tk0 = (uint32_t)t0;
+  // residual waves: one per chunk (they come after every streaming wave)
+  P.G = 1;
+  // see linear_role for the order of the waves
+  if (!stoch) {
+    P.n_waves = sh.RQ * sh.C + B;
+    P.tk0 = P.res0 = 0;
+  } else {
+    const int64_t CG = k > 0 ? (P.C + P.G - 1) / P.G : 0;
+    P.tk0 = (uint32_t)(k * (2 * B * sh.C + B));
+    P.res0 = (uint32_t)(P.tk0 + B * (sh.C + 1));
+    P.n_waves = P.res0 + B * CG;
   }
   if (P.n_waves > MAX_WAVES) return SV_ELIMIT;
   P.commit = false;

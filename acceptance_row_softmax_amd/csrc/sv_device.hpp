@@ -655,6 +655,22 @@ __device__ __forceinline__ void put_rec(uint64_t* dst, const T& v, uint32_t tag)
     __hip_atomic_store(dst + i, ((uint64_t)tag << 32) | w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The same record written by the whole wave with one store instruction: lane i
+// stores word i. v must be the same in every lane.
+template <class T>
+__device__ __forceinline__ void put_rec_wave(uint64_t* dst, const T& v, uint32_t tag) {
+  constexpr int N = RecWords<T>::N;
+  static_assert(N <= WAVE, "one word per lane");
+  uint32_t w[N];
+  __builtin_memcpy(w, &v, sizeof(T));
+  const int lane = lane_id();
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (lane == i) mine = w[i];
+  if (lane < N) __hip_atomic_store(dst + lane, ((uint64_t)tag << 32) | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Waits until all words of the record carry `tag`; false on timeout (v undefined).
 template <class T>
 __device__ __forceinline__ bool get_rec(const uint64_t* src, T& v, uint32_t tag) {

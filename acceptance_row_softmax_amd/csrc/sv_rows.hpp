@@ -68,24 +68,35 @@ struct RowSums {
   double Z;     // relative to 2^(M*c0); 0 if not computed
 };
 
-// Combines the partials; wl receives each chunk's weight relative to 2^(M*c0).
-template <bool SUM>
-__device__ __forceinline__ RowSums row_sums(const RowParts& rp, float c0, double (&wl)[MAX_ROUNDS]) {
+// Combines the partials of a row of C chunks; wl receives each chunk's weight
+// relative to 2^(M*c0). Rounds past C (lane-strided chunk groups no lane of which
+// holds a chunk) are skipped with a wave-uniform branch. ARG = false: the max only
+// (argmax -1).
+template <bool SUM, bool ARG = true>
+__device__ __forceinline__ RowSums row_sums(const RowParts& rp, float c0, double (&wl)[MAX_ROUNDS],
+                                            int C = MAX_CHUNKS) {
   float M = -INFINITY;
   int arg = INT_SENTINEL;
 #pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) argmax_combine(M, arg, rp.m[t], rp.idx[t]);
-  wave_argmax(M, arg);
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    if (t * WAVE >= C) break;
+    if constexpr (ARG) argmax_combine(M, arg, rp.m[t], rp.idx[t]);
+    else M = fmaxf(M, rp.m[t]);
+  }
+  if constexpr (ARG) wave_argmax(M, arg);
+  else M = wave_max(M);
   RowSums r;
   r.M = M;
-  r.argmax = (M > -INFINITY && arg != INT_SENTINEL) ? arg : -1;
+  r.argmax = (ARG && M > -INFINITY && arg != INT_SENTINEL) ? arg : -1;
   r.Z = 0.0;
   if constexpr (SUM) {
     const double Mc0 = (double)M * (double)c0;
     double local = 0.0;
 #pragma unroll
     for (int t = 0; t < MAX_ROUNDS; ++t) {
-      wl[t] = (rp.m[t] == -INFINITY) ? 0.0 : rp.s[t] * pow2_neg((double)chunk_mc0(rp.m[t], c0) - Mc0);
+      wl[t] = 0.0;
+      if (t * WAVE >= C) continue;
+      if (rp.m[t] != -INFINITY) wl[t] = rp.s[t] * pow2_neg((double)chunk_mc0(rp.m[t], c0) - Mc0);
       local += wl[t];
     }
     r.Z = wave_sum(local);
