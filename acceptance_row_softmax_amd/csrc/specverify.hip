@@ -125,22 +125,26 @@ __device__ __forceinline__ ResidW make_residw(const Decision& d, float c0) {
   return rw;
 }
 
-// Residual sum over a loaded chunk of rows t_L, d_L (same value in every lane).
+// Residual sum over a loaded chunk of rows t_L, d_L (same value in every lane);
+// us receives this lane's unit sums, as the in-chunk search forms them.
 template <int DT>
-__device__ __forceinline__ double residual_raw_sum(const Raw& rt, const Raw& rd, const ResidW& rw) {
-  constexpr int W = DTraits<DT>::W;
+__device__ __forceinline__ double residual_raw_sum(const Raw& rt, const Raw& rd, const ResidW& rw, float (&us)[CU]) {
+  chunk_unit_sums<DT, true>(rt, rd, rw, us);
   double s = 0.0;
 #pragma unroll
-  for (int j = 0; j < CU; ++j) {
-    float xt[W], xd[W];
-    unit_values<DT>(rt, j, xt);
-    unit_values<DT>(rd, j, xd);
-#pragma unroll
-    for (int e = 0; e < W; ++e) xt[e] = rw(xt[e], xd[e]);
-    s += (double)pairwise_sum<W>(xt);
-  }
+  for (int j = 0; j < CU; ++j) s += (double)us[j];
   return wave_sum(s);
 }
+
+// The last residual wave's verdict on one chunk, for the wave holding it (hold
+// mode): kind 0 not picked, 1 picked (draw from the residual), 2 picked with no
+// residual mass (draw from p_t,L); th the threshold inside the chunk.
+struct Verdict {
+  int kind;
+  int pad;
+  double th;
+};
+constexpr int VERD_WORDS = RecWords<Verdict>::N;   // 4
 
 // ------------------------------------------------------------------ linear drafts
 // Streaming waves: one per 8 KiB chunk of a row. A streaming wave reduces its
@@ -174,8 +178,9 @@ struct LinearParams {
   uint64_t* seg;        // [RQ][C][RW] chunk records
   uint64_t* pst;        // [B][k]   PairStat records (stochastic)
   uint64_t* rks;        // [B]      RowStat records of target rows k (stochastic)
-  uint64_t* dec;        // [B]      Decision records
+  uint64_t* dec;        // [B][C]   Decision records, one copy per residual wave
   uint64_t* res;        // [B][C]   ResPart records
+  uint64_t* verd;       // [B][C]   Verdict records (hold mode)
   uint64_t* tok;        // [B]      Token records
   uint64_t* prob;       // [B][k]   Probs records (stochastic)
   uint32_t* grp_cnt;    // [groups] segments counted per combine group
@@ -187,11 +192,12 @@ struct LinearParams {
   int C;                // chunks per row
   int RW;               // words per chunk record
   int EV;               // events per sequence (stochastic): k pair combines, target row k, the final token
-  int G;                // chunks per residual wave (1 or 2; the kernel's template argument)
+  int G;                // chunks per residual wave (1; the kernel's template argument)
+  bool hold;            // residual waves keep their chunk until the draw is placed (see linear_residual_wave)
   float c0;
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
-  uint32_t tk0, res0;   // stochastic: first wave of the target rows k, first residual wave
+  uint32_t tk0;         // stochastic: first wave of the sequence blocks (target row k, its finisher, residual waves)
   // optional commit by the emitting wave (spec_verify_linear_commit)
   int32_t* seq_len;     // [B] in/out
   int32_t* history;     // [B][capacity]
@@ -522,6 +528,25 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
   emit_store<DT, false>(P, b, in, y);
 }
 
+// The decision of sequence b, written once for each of its residual waves (each
+// polls a copy of its own: one line polled by every residual wave of a sequence
+// serialises the polls). d must be the same in every lane.
+__device__ __forceinline__ void publish_decision(const LinearParams& P, int64_t b, const Decision& d) {
+  uint32_t w[DEC_WORDS];
+  __builtin_memcpy(w, &d, sizeof(Decision));
+  const int lane = lane_id();
+  const int n = P.C * DEC_WORDS;
+  for (int e0 = 0; e0 < n; e0 += WAVE) {
+    const int e = e0 + lane;
+    const int j = e % DEC_WORDS;
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < DEC_WORDS; ++i) if (j == i) v = w[i];
+    if (e < n) __hip_atomic_store(P.dec + b * P.C * DEC_WORDS + e, ((uint64_t)P.tag << 32) | v, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Called after the state update old -> now of sequence b by the pair combine of
 // position mi (whose statistics are `mine`). If this update settles L < k, hand
 // rows t_L, d_L to the residual waves; if it settles L = k (every draft accepted
@@ -534,10 +559,19 @@ __device__ __forceinline__ bool linear_settle(const LinearParams& P, int64_t b, 
   const int Ln = settled_L(now, k);
   if (Ln < 0 || settled_L(old, k) >= 0) return false;
   if (Ln < k) {
-    if (lane_id() == 0 && !published) {
+    if (!published) {
       PairStat ps = mine;
       bool got = true;
-      if (Ln != mi) got = get_rec(P.pst + (b * k + Ln) * PST_WORDS, ps, P.tag);
+      if (Ln != mi) {
+        if (lane_id() == 0) got = get_rec(P.pst + (b * k + Ln) * PST_WORDS, ps, P.tag);
+        got = bcast((int)got) != 0;
+        ps.Zt = bcast(ps.Zt);
+        ps.Zd = bcast(ps.Zd);
+        ps.Mt = bcast(ps.Mt);
+        ps.Md = bcast(ps.Md);
+        ps.okt = bcast(ps.okt);
+        ps.okd = bcast(ps.okd);
+      }
       Decision d;
       d.L = Ln;
       d.kind = (got && ps.okt && ps.okd) ? 1 : 2;
@@ -545,7 +579,7 @@ __device__ __forceinline__ bool linear_settle(const LinearParams& P, int64_t b, 
       d.Md = ps.Md;
       d.Zt = ps.Zt;
       d.Zd = ps.Zd;
-      put_rec(P.dec + b * DEC_WORDS, d, P.tag);
+      publish_decision(P, b, d);
     }
     return false;   // the residual waves draw the token
   }
@@ -620,7 +654,7 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
     d.Md = ps.Md;
     d.Zt = ps.Zt;
     d.Zd = ps.Zd;
-    put_rec_wave(P.dec + b * DEC_WORDS, d, P.tag);
+    publish_decision(P, b, d);
   }
   // The state update first: an atomic whose result the wave waits for also waits
   // for every store the wave issued before it, and the records below are read by
@@ -637,10 +671,10 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
   put_rec_wave(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
   put_rec_wave(P.pst + (b * k + i) * PST_WORDS, ps, P.tag);
   olds = bcast(olds);
-  if (lane == 0) {
+  {
     // The update that decides the last position with none rejected tells the
     // residual waves that L = k (they have nothing to draw), without waiting for
-    // target row k: those waves are dispatched before it.
+    // target row k.
     const uint64_t mk = (1ull << k) - 1, now = olds | bits;
     if ((now & mk) == mk && ((now >> 32) & mk) == 0 && (olds & mk) != mk) {
       Decision d;
@@ -648,7 +682,7 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
       d.kind = 0;
       d.Mt = d.Md = 0.0f;
       d.Zt = d.Zd = 0.0;
-      put_rec(P.dec + b * DEC_WORDS, d, P.tag);
+      publish_decision(P, b, d);
     }
   }
   Ev ev{b, 1u, false, 0};
@@ -726,21 +760,28 @@ __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_
 }
 
 // Residual wave (b, g), dispatched after the streaming waves of every row a
-// decision depends on (positions 0..k-1): waits for the decision of sequence b;
-// if a draft was rejected, sums the residual over chunks G g ... G g + G - 1 of
-// rows t_L, d_L. The sequence's last residual wave picks the chunk holding u*S,
-// scans it and records the token.
+// decision depends on: waits for the decision of sequence b; if a draft was
+// rejected, sums the residual max(0, p_t,L - p_d,L) over chunk g of rows t_L,
+// d_L. The sequence's last residual wave to count picks the chunk that holds u*S.
+// Without hold mode it reloads that chunk and scans it. In hold mode (a launch
+// whose residual waves can all be resident at once, so that none waits for a
+// wave that cannot start) every residual wave keeps its chunk and its unit sums
+// and waits for the last one's verdict; the wave holding the picked chunk scans it
+// from its registers.
 template <int DT, int G>
 __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
+  static_assert(G == 1, "one chunk per residual wave");
   const int lane = lane_id();
-  const uint32_t CG = (uint32_t)((P.C + G - 1) / G);   // residual waves per sequence
+  const uint32_t CG = (uint32_t)P.C;   // residual waves per sequence
   const int64_t k = P.k;
   Decision d;
   d.L = 0;
   d.kind = 2;
   d.Mt = d.Md = 0.0f;
   d.Zt = d.Zd = 0.0;
-  if (!poll_rec(P.dec + b * DEC_WORDS, d, P.tag)) d.kind = 3;   // 3: the decision never arrived
+  uint64_t* dr = P.dec + (b * P.C + g) * DEC_WORDS;   // this wave's copy of the decision
+  if (!poll_rec(dr, d, P.tag)) d.kind = 3;   // 3: the decision never arrived
+  if (lane == 0) clear_rec<Decision>(dr);
   const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);
@@ -749,131 +790,171 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   // wait for any that are not written yet.
   uint32_t old = 0;
   if (lane == 0) old = counter_add(P.res_cnt + b * CSTRIDE, 1u);
+  Raw rt, rd;
+  Chunk kg;
+  float us[CU];
   if (d.kind == 1) {
-    if constexpr (G == 1) {
-      Raw rt, rd;
-      load_chunk<DT>(trow, P.V, g, rt);
-      load_chunk<DT>(drow, P.V, g, rd);
-      ResPart r;
-      r.s = residual_raw_sum<DT>(rt, rd, rw);
-      if (lane == 0) put_rec(P.res + (b * P.C + g) * RES_WORDS, r, P.tag);
-    } else {
-#pragma unroll 1
-      for (int64_t c = g * G; c < min(g * G + G, (int64_t)P.C); ++c) {
-        Raw rt, rd;
-        load_chunk<DT>(trow, P.V, c, rt);
-        load_chunk<DT>(drow, P.V, c, rd);
-        ResPart r;
-        r.s = residual_raw_sum<DT>(rt, rd, rw);
-        if (lane == 0) put_rec(P.res + (b * P.C + c) * RES_WORDS, r, P.tag);
-      }
-    }
+    kg = load_chunk<DT>(trow, P.V, g, rt);
+    load_chunk<DT>(drow, P.V, g, rd);
+    ResPart r;
+    r.s = residual_raw_sum<DT>(rt, rd, rw, us);
+    put_rec_wave(P.res + (b * P.C + g) * RES_WORDS, r, P.tag);
   }
   old = bcast(old);
-  if (old + 1 != CG) return Ev{0, 0u, false, 0};
-  // last residual wave of the sequence: draw the correction token
-  if (lane == 0) {
-    counter_reset(P.res_cnt + b * CSTRIDE);
-    clear_rec<Decision>(P.dec + b * DEC_WORDS);
-  }
-  if (d.kind == 0) return Ev{0, 0u, false, 0};   // no draft rejected: the bonus token is recorded already
-  int y = (d.kind == 3) ? -2 : -1;
-  if (d.kind == 1) {
-    // Round trips overlap: the token event's count goes out with the reads of the
-    // residual sums; after the pick, the chosen chunk's reloads go out with the
-    // emission's reads (if this is the sequence's last event, which the count
-    // tells); then the scan. Otherwise the last event's wave waits for the token
-    // record.
+  const float u = P.uniforms[b * (k + 1) + k];
+  if (old + 1 != CG) {
+    if (!(P.hold && d.kind == 1)) return Ev{0, 0u, false, 0};
+    // hold mode: wait for the verdict on this chunk
+    uint64_t* vr = P.verd + (b * P.C + g) * VERD_WORDS;
+    Verdict v;
+    v.kind = 0;
+    v.th = 0.0;
+    const bool got = poll_rec(vr, v, P.tag);
+    if (lane == 0) clear_rec<Verdict>(vr);
+    if (!got || v.kind == 0) return Ev{0, 0u, false, 0};
+    // the token event is counted before the scan, so that its round trip overlaps it
     uint32_t fo = 0;
     if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
-    double wl[MAX_ROUNDS];
-    bool ok = true;
-#pragma unroll
-    for (int t = 0; t < MAX_ROUNDS; ++t) {
-      wl[t] = 0.0;
-      const int cc = t * WAVE + lane;
-      if (cc < P.C) {
-        ResPart r;
-        uint64_t* rec = P.res + (b * P.C + cc) * RES_WORDS;
-        const bool g = get_rec(rec, r, P.tag);
-        ok = ok && g;
-        wl[t] = g ? r.s : 0.0;
-        clear_rec<ResPart>(rec);
-      }
-    }
-    const bool last = bcast(fo) + 1 == (uint32_t)P.EV;
-    const float u = P.uniforms[b * (k + 1) + k];
-    ChunkPick pk;
-    pk.c = -1;
     ResidW rx = rw;
-    const char* dx = drow;
-    const bool rec_ok = __ballot(!ok) == 0ull;
-    if (!rec_ok) {
-      y = -2;
+    int yh;
+    if (v.kind == 2) {
+      // no residual mass: p_t,L's weights (the draft's zeroed, taken from row t_L)
+      rx.mc0d = rx.mc0t;
+      rx.izd = 0.0f;
+      chunk_unit_sums<DT, true>(rt, rt, rx, us);
+      yh = (int)chunk_invcdf_us<DT, true>(kg, rt, rt, us, v.th, rx);
     } else {
-      // The draw from the residual. With no residual mass (the rows agree up to
-      // rounding) it is taken from p_t,L instead: the same pick and scan with the
-      // draft's weights zeroed (and taken from row t_L, so that they stay finite),
-      // over chunk sums formed here.
-      double tot = 0.0;
-#pragma unroll
-      for (int t = 0; t < MAX_ROUNDS; ++t) tot += wl[t];
-      tot = wave_sum(tot);
-      pk = pick_chunk(P.C, (double)u, wl);
-      if (pk.c < 0 && tot == 0.0) {
-        rx.mc0d = rx.mc0t;
-        rx.izd = 0.0f;
-        dx = trow;
-#pragma unroll
-        for (int t = 0; t < MAX_ROUNDS; ++t) wl[t] = 0.0;
-#pragma unroll 1
-        for (int c = 0; c < P.C; ++c) {
-          Raw rt;
-          load_chunk<DT>(trow, P.V, c, rt);
-          const double sc = residual_raw_sum<DT>(rt, rt, rx);
-#pragma unroll
-          for (int t = 0; t < MAX_ROUNDS; ++t)
-            if (t * WAVE + lane == c) wl[t] = sc;
-        }
-        pk = pick_chunk(P.C, (double)u, wl);
-      }
+      yh = (int)chunk_invcdf_us<DT, true>(kg, rt, rd, us, v.th, rx);
     }
-    Raw rt, rd;
-    Chunk kt;
-    if (pk.c >= 0) {
-      kt = load_chunk<DT>(trow, P.V, pk.c, rt);
-      load_chunk<DT>(dx, P.V, pk.c, rd);
-    }
-    EmitIn ein;
-    if (last) {
+    if (bcast(fo) + 1 == (uint32_t)P.EV) {
       if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-      ein = emit_load<DT, true>(P, b, true);
-    }
-    if (pk.c >= 0) {
-      const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
-      y = (int)chunk_invcdf<DT, true>(kt, rt, rd, th, rx);
-    }
-    if (last) {
-      emit_store<DT, true>(P, b, ein, y);
+      linear_emit<DT, true>(P, b, yh);
     } else if (lane == 0) {
       Token t;
-      t.y = y;
+      t.y = yh;
       put_rec(P.tok + b, t, P.tag);
     }
     return Ev{0, 0u, false, 0};
   }
-  return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
+  // last residual wave of the sequence: draw the correction token
+  if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
+  if (d.kind == 0) return Ev{0, 0u, false, 0};   // no draft rejected: the bonus token is recorded already
+  int y = (d.kind == 3) ? -2 : -1;
+  if (d.kind != 1) return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
+  // Round trips overlap: without hold mode the token event's count goes out with
+  // the reads of the residual sums; after the pick, the chosen chunk's reloads go
+  // out with the emission's reads (if this is the sequence's last event, which the
+  // count tells); then the scan. Otherwise the last event's wave waits for the token
+  // record.
+  uint32_t fo = 0;
+  if (!P.hold && lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
+  double wl[MAX_ROUNDS];
+  bool ok = true;
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
+    wl[t] = 0.0;
+    if (t * WAVE >= P.C) continue;
+    const int cc = t * WAVE + lane;
+    if (cc < P.C) {
+      ResPart r;
+      uint64_t* rec = P.res + (b * P.C + cc) * RES_WORDS;
+      const bool gr = get_rec(rec, r, P.tag);
+      ok = ok && gr;
+      wl[t] = gr ? r.s : 0.0;
+      clear_rec<ResPart>(rec);
+    }
+  }
+  const bool last = !P.hold && bcast(fo) + 1 == (uint32_t)P.EV;
+  ChunkPick pk;
+  pk.c = -1;
+  ResidW rx = rw;
+  const char* dx = drow;
+  bool zero = false;   // no residual mass: the draw comes from p_t,L
+  const bool rec_ok = __ballot(!ok) == 0ull;
+  if (!rec_ok) {
+    y = -2;
+  } else {
+    // The draw from the residual. With no residual mass (the rows agree up to
+    // rounding) it is taken from p_t,L instead: the same pick and scan with the
+    // draft's weights zeroed (and taken from row t_L, so that they stay finite),
+    // over chunk sums formed here.
+    double tot = 0.0;
+#pragma unroll
+    for (int t = 0; t < MAX_ROUNDS; ++t) tot += wl[t];
+    tot = wave_sum(tot);
+    pk = pick_chunk(P.C, (double)u, wl);
+    if (pk.c < 0 && tot == 0.0) {
+      zero = true;
+      rx.mc0d = rx.mc0t;
+      rx.izd = 0.0f;
+      dx = trow;
+#pragma unroll
+      for (int t = 0; t < MAX_ROUNDS; ++t) wl[t] = 0.0;
+      // (this wave's own chunk registers serve as the buffer)
+#pragma unroll 1
+      for (int c = 0; c < P.C; ++c) {
+        load_chunk<DT>(trow, P.V, c, rt);
+        const double sc = residual_raw_sum<DT>(rt, rt, rx, us);
+#pragma unroll
+        for (int t = 0; t < MAX_ROUNDS; ++t)
+          if (t * WAVE + lane == c) wl[t] = sc;
+      }
+      pk = pick_chunk(P.C, (double)u, wl);
+    }
+  }
+  const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
+  if (P.hold) {
+    // every other residual wave of the sequence waits for its verdict (one store
+    // instruction: lane c writes chunk c's kind, the picked chunk's record whole)
+    const int pc = pk.c;
+    for (int c0 = 0; c0 < P.C; c0 += WAVE) {
+      const int c = c0 + lane;
+      if (c < P.C && c != g) {
+        Verdict v;
+        v.kind = c == pc ? (zero ? 2 : 1) : 0;
+        v.pad = 0;
+        v.th = th;
+        put_rec(P.verd + (b * P.C + c) * VERD_WORDS, v, P.tag);
+      }
+    }
+    if (pc < 0) return Ev{b, 1u, true, rec_ok ? -1 : -2};   // nothing to draw from
+    if (pc != g) return Ev{0, 0u, false, 0};               // the holder counts the token
+    // the pick is this wave's own chunk, whose registers were not kept: the reload
+    // below serves
+  }
+  // the picked chunk, reloaded into this wave's own chunk registers
+  if (pk.c >= 0) {
+    kg = load_chunk<DT>(trow, P.V, pk.c, rt);
+    load_chunk<DT>(dx, P.V, pk.c, rd);
+  }
+  EmitIn ein;
+  if (last) {
+    if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+    ein = emit_load<DT, true>(P, b, true);
+  }
+  if (pk.c >= 0) y = (int)chunk_invcdf<DT, true>(kg, rt, rd, th, rx);
+  if (P.hold) return Ev{b, 1u, true, y};
+  if (last) {
+    emit_store<DT, true>(P, b, ein, y);
+  } else if (lane == 0) {
+    Token t;
+    t.y = y;
+    put_rec(P.tok + b, t, P.tag);
+  }
+  return Ev{0, 0u, false, 0};
 }
 
 // Wave roles of a linear launch, in dispatch order. Greedy: the chunk waves of
 // every row (rows of position 0 of every sequence, then position 1, ...), then one
-// finishing wave per sequence. Stochastic: for each position i < k, the chunk
-// waves of its target and draft rows followed by one pair-finishing wave per
-// sequence; then the chunk waves of the target rows k, each row followed by the
-// wave that finishes it; then the residual waves, one per (sequence, G chunks).
-// Every wave that waits follows the waves it waits for. The residual waves come
-// last so that they hold no slot while rows stream: by then most of them find
-// their decision made, and those of sequences that rejected nothing end at once.
+// finishing wave per sequence. Stochastic: for each position i < k and each
+// sequence, the chunk waves of its target and draft rows (chunk by chunk,
+// alternating) and the wave that finishes the pair; then for each sequence the
+// chunk waves of its target row k, the wave that finishes that row, and its
+// residual waves (one per chunk). Every wave that waits follows the waves it waits
+// for. Each finishing wave comes right after its own rows, so that decisions are
+// made while later rows still stream, and a sequence's residual waves come after
+// all of its pairs: most of them find their decision made and either draw at once
+// (overlapping the remaining stream) or, if nothing was rejected, end at once.
 enum RoleKind { ROLE_IDLE = 0, ROLE_STREAM, ROLE_RESID, ROLE_PAIR, ROLE_ROWK, ROLE_GREEDY };
 struct Role {
   int kind;
@@ -898,35 +979,36 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
     }
   } else {
     if (w < P.tk0) {
-      const uint32_t PS = 2 * B * NS + B;   // waves per position
-      const uint32_t pos = w / PS, v = w - pos * PS;
-      if (v < 2 * B * NS) {
-        r.q = pos * 2 * B + v / NS;
-        r.c = v % NS;
+      // position blocks of B pair blocks of 2C + 1 waves
+      const uint32_t QP = 2 * NS + 1;
+      const uint32_t blk = w / QP, e = w - blk * QP;
+      const uint32_t pos = blk / B;
+      r.b = blk - pos * B;
+      if (e < 2 * NS) {
+        r.q = pos * 2 * B + 2 * r.b + (e & 1u);
+        r.c = e >> 1;
         r.kind = ROLE_STREAM;
       } else {
-        r.b = v - 2 * B * NS;
         r.c = pos;
         r.kind = ROLE_PAIR;
       }
-    } else if (w < P.res0) {
-      // per sequence: the C chunk waves of its target row k, then its finisher
+    } else {
+      // sequence blocks: C chunk waves of target row k, its finisher, CG residual waves
+      const uint32_t CG = P.k > 0 ? ((uint32_t)P.C + G - 1) / G : 0u;
+      const uint32_t Q = NS + 1 + CG;
       const uint32_t v = w - P.tk0;
-      r.b = v / (NS + 1);
-      const uint32_t e = v - r.b * (NS + 1);
+      r.b = v / Q;
+      const uint32_t e = v - r.b * Q;
       if (e < NS) {
         r.q = (uint32_t)(2 * P.k) * B + r.b;
         r.c = e;
         r.kind = ROLE_STREAM;
-      } else {
+      } else if (e == NS) {
         r.kind = ROLE_ROWK;
+      } else {
+        r.c = e - NS - 1;
+        r.kind = ROLE_RESID;
       }
-    } else {
-      const uint32_t CG = ((uint32_t)P.C + G - 1) / G;
-      const uint32_t v = w - P.res0;
-      r.b = v / CG;
-      r.c = v - r.b * CG;
-      r.kind = ROLE_RESID;
     }
   }
   return r;
@@ -1749,9 +1831,10 @@ inline LinearShape linear_shape(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv
 Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
   const LinearShape s = linear_shape(B, k, V, dt, mode);
   return make_layout({(size_t)(s.RQ * s.C * s.RW) * 8, (size_t)(B * k) * PST_WORDS * 8, (size_t)B * ROW_WORDS * 8,
-                      (size_t)B * DEC_WORDS * 8, (size_t)(B * s.C) * RES_WORDS * 8, (size_t)B * 8,
+                      (size_t)(B * s.C) * DEC_WORDS * 8, (size_t)(B * s.C) * RES_WORDS * 8, (size_t)B * 8,
                       (size_t)(s.groups * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
-                      (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8});
+                      (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8,
+                      (size_t)(B * s.C) * VERD_WORDS * 8});
 }
 
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
@@ -1834,6 +1917,30 @@ struct RowStatsLauncher {
   }
 };
 
+// Waves of the stochastic linear kernel for dtype `dt` that can be resident on
+// the current device at once (0 if the runtime cannot tell), cached per device.
+constexpr int CAP_DEVICES = 64;
+static std::atomic<int64_t> g_capacity[CAP_DEVICES][3];
+
+inline int64_t stochastic_wave_capacity(sv_dtype dt) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= CAP_DEVICES || !dtype_ok(dt)) return 0;
+  const int64_t c = g_capacity[dev][dt].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  const void* fn = dt == SV_F32 ? reinterpret_cast<const void*>(&linear_kernel<DT_F32, true, 1>)
+                 : dt == SV_BF16 ? reinterpret_cast<const void*>(&linear_kernel<DT_BF16, true, 1>)
+                                 : reinterpret_cast<const void*>(&linear_kernel<DT_F16, true, 1>);
+  int blocks = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, BLOCK, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int64_t cap = (int64_t)blocks * cus * WPB;
+  g_capacity[dev][dt].store(cap, std::memory_order_relaxed);
+  return cap;
+}
+
 // Checks and fills the parameters of the linear entry points (B == 0: SV_OK with
 // nothing to launch).
 sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t B, int64_t k, int64_t V,
@@ -1874,6 +1981,7 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
   P.errw = reinterpret_cast<uint32_t*>(ws + lay.off[10]);
   P.prob = reinterpret_cast<uint64_t*>(ws + lay.off[11]);
+  P.verd = reinterpret_cast<uint64_t*>(ws + lay.off[12]);
   P.B = B;
   P.k = k;
   P.V = V;
@@ -1881,17 +1989,18 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.RW = (int)sh.RW;
   P.EV = (int)(k + 2);
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  // residual waves: one per chunk (they come after every streaming wave)
+  // residual waves: one per chunk (they come after every streaming wave); hold mode
+  // when all of them fit on the GPU at once, with room to spare
   P.G = 1;
+  P.hold = stoch && k > 0 && B * P.C <= stochastic_wave_capacity(dtype) / 2;
   // see linear_role for the order of the waves
   if (!stoch) {
     P.n_waves = sh.RQ * sh.C + B;
-    P.tk0 = P.res0 = 0;
+    P.tk0 = 0;
   } else {
     const int64_t CG = k > 0 ? (P.C + P.G - 1) / P.G : 0;
-    P.tk0 = (uint32_t)(k * (2 * B * sh.C + B));
-    P.res0 = (uint32_t)(P.tk0 + B * (sh.C + 1));
-    P.n_waves = P.res0 + B * CG;
+    P.tk0 = (uint32_t)(k * B * (2 * sh.C + 1));
+    P.n_waves = P.tk0 + B * (sh.C + 1 + CG);
   }
   if (P.n_waves > MAX_WAVES) return SV_ELIMIT;
   P.commit = false;

@@ -495,17 +495,23 @@ __device__ __forceinline__ void unit_weights(const Raw& ra, const Raw& rb, int j
 // j whose running total crosses th (fp64 wave totals), then the lane inside it
 // (one fp64 prefix scan), then the element inside that unit.
 template <int DT, bool PAIR, class WT>
-__device__ __forceinline__ int64_t chunk_invcdf(const Chunk& k, const Raw& ra, const Raw& rb, double th,
-                                                const WT& wt) {
+__device__ __forceinline__ void chunk_unit_sums(const Raw& ra, const Raw& rb, const WT& wt, float (&us)[CU]) {
   constexpr int W = DTraits<DT>::W;
-  const int lane = lane_id();
-  float us[CU];
 #pragma unroll
   for (int j = 0; j < CU; ++j) {
     float w[W];
     unit_weights<DT, PAIR>(ra, rb, j, wt, w);
     us[j] = pairwise_sum<W>(w);
   }
+}
+
+// The same search from this lane's unit weight sums us[j] (unit j*64 + lane, as
+// chunk_unit_sums forms them), which the caller may already hold.
+template <int DT, bool PAIR, class WT>
+__device__ __forceinline__ int64_t chunk_invcdf_us(const Chunk& k, const Raw& ra, const Raw& rb, const float (&us)[CU],
+                                                   double th, const WT& wt) {
+  constexpr int W = DTraits<DT>::W;
+  const int lane = lane_id();
   double off = 0.0, offj = 0.0;
   int hj = -1;
 #pragma unroll
@@ -566,6 +572,14 @@ __device__ __forceinline__ int64_t chunk_invcdf(const Chunk& k, const Raw& ra, c
   }
   pick = __shfl(pick, kl);
   return (k.u0 + kj * WAVE + kl) * W + pick;
+}
+
+template <int DT, bool PAIR, class WT>
+__device__ __forceinline__ int64_t chunk_invcdf(const Chunk& k, const Raw& ra, const Raw& rb, double th,
+                                                const WT& wt) {
+  float us[CU];
+  chunk_unit_sums<DT, PAIR>(ra, rb, wt, us);
+  return chunk_invcdf_us<DT, PAIR>(k, ra, rb, us, th, wt);
 }
 
 // ------------------------------------------------------------------ chunk selection over a row
