@@ -126,24 +126,31 @@ STEP_CONFIGS = ("sample_c2_step", "sample_c3", "commit_c3", "tree_mask_c5")
 
 
 def _graph_time(torch, calls, copies, steps, warmup):
-    """Warm up, capture `copies` calls in one graph, replay it; returns
-    (K, wall ms per call, event ms per call)."""
+    """Warm up, then time exactly `steps` calls: a graph over the `copies` calls
+    replayed as often as it fits, then one over the first (steps mod copies) of
+    them; returns (K, wall ms per call, event ms per call)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         calls(i % copies)
     torch.cuda.synchronize()
-    K = max(copies, (steps // copies) * copies)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(copies):
-            calls(i)
-    graph.replay()
+    K = max(1, steps)
+    reps, rem = divmod(K, copies)
+    graphs = []
+    for n in ((copies,) if reps else ()) + ((rem,) if rem else ()):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                calls(i)
+        g.replay()
+        graphs.append(g)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(K // copies):
-        graph.replay()
+    for _ in range(reps):
+        graphs[0].replay()
+    if rem:
+        graphs[-1].replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -398,7 +405,7 @@ def main():
         g_out = first["out_tokens"].cpu().numpy()
         differ = (g_acc != o["accept_len"]) | np.any(g_out != o["out_tokens"], axis=1)
     else:
-        sample = list(range(min(w.B, 2 if w.n_nodes > 1000 else w.B)))
+        sample = list(range(w.B))          # every tree of the batch
         if w.mode == "typical":
             o = oracle.verify_tree_typical(w.temperature, TYPICAL_EPS, TYPICAL_DELTA, w.parent, w.cand[sample],
                                            w.logits[sample], w.uniforms[sample], w.V, w.dtype, w.max_depth)
@@ -429,22 +436,29 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed region
-    K = max(copies, (args.steps // copies) * copies)
+    # exactly --steps launches: a graph over all the input copies, replayed as often
+    # as it fits, then one over the first (steps mod copies) of them
+    K = max(1, args.steps)
     stream = torch.cuda.current_stream()
     if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(copies):
-                call(i)
-        graph.replay()
+        reps, rem = divmod(K, copies)
+        graphs = []
+        for n in ((copies,) if reps else ()) + ((rem,) if rem else ()):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    call(i)
+            g.replay()
+            graphs.append(g)
         torch.cuda.synchronize()
-        reps = K // copies
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record(stream)
         for _ in range(reps):
-            graph.replay()
+            graphs[0].replay()
+        if rem:
+            graphs[-1].replay()
         ev1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()

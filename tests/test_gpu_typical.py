@@ -62,9 +62,9 @@ def test_c4_sparse_trees():
     assert np.all(g["err_flags"] == 0)
 
 
-def test_c5_full_tree_sampled():
+def test_c5_full_tree():
     w = gen.c5_medusa_full(0, mode="stochastic")
-    g, o = _check(w, 0.09, 0.3, trees=[1])
+    g, o = _check(w, 0.09, 0.3)             # every tree of the batch against the oracle
 
 
 def test_errors():
