@@ -92,7 +92,16 @@ extern "C" {
 
 typedef struct ihipStream_t* sv_stream_t; /* the same type as hipStream_t; NULL = default stream */
 
-typedef enum {
+/* The enums below are int-sized in both languages. In C++ they get int as their
+ * fixed underlying type, so that any int a C caller passes (an unknown mode or
+ * dtype, which the calls reject) is a valid value rather than undefined behaviour. */
+#ifdef __cplusplus
+#define SV_ENUM_INT : int
+#else
+#define SV_ENUM_INT
+#endif
+
+typedef enum SV_ENUM_INT {
   SV_OK = 0,
   SV_EINVAL = 1,      /* bad size, NULL required pointer, bad temperature or mode */
   SV_EDTYPE = 2,      /* unknown dtype */
@@ -101,8 +110,8 @@ typedef enum {
   SV_ELIMIT = 5       /* shape beyond a documented limit */
 } sv_status;
 
-typedef enum { SV_GREEDY = 0, SV_STOCHASTIC = 1 } sv_mode;
-typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
+typedef enum SV_ENUM_INT { SV_GREEDY = 0, SV_STOCHASTIC = 1 } sv_mode;
+typedef enum SV_ENUM_INT { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
 
 enum { SV_ERR_TOKEN = 1, SV_ERR_ROW = 2, SV_ERR_TREE = 4, SV_ERR_INTERNAL = 8,
        SV_ERR_CAPACITY = 16, SV_ERR_UNVERIFIED = 32 };
