@@ -199,7 +199,11 @@ sv_status spec_verify_tree_typical(float temperature, double epsilon, double del
                                    sv_stream_t stream);
 
 /* ---------------------------------------------------------------- row statistics
- * The streaming row softmax the verifier is built on, exposed for diagnostics:
+ * [S-SD], [M-3]. The target's logits over the vocabulary define the next token's
+ * distribution (Sonar page, section "Spekulatives Decoding"); the Medusa page,
+ * section 三, turns a node's logits into that distribution by a softmax before the
+ * sampler takes its token. This is that reduction on its own -- the streaming row
+ * softmax the verifier is built on, exposed for diagnostics:
  * for rows x[rows][V], row_max = max_v x_v, row_lse = log sum_v exp(x_v / T),
  * row_argmax = lowest index of the maximum (-1 and SV_ERR_ROW if no entry exceeds
  * -inf). Any output pointer may be NULL. row_lse is NaN when the normaliser is not
