@@ -65,6 +65,8 @@ def lib():
         L.spec_row_stats.argtypes = [i32, f32, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.spec_workspace_clear.restype = i32
         L.spec_workspace_clear.argtypes = [vp, sz, vp]
+        L.spec_set_wait_limit.restype = i32
+        L.spec_set_wait_limit.argtypes = [ctypes.c_double]
         L.spec_verify_tree_typical.restype = i32
         L.spec_verify_tree_typical.argtypes = [f32, ctypes.c_double, ctypes.c_double, i64, i64, i64, i32, vp,
                                                i64, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp]
@@ -92,7 +94,8 @@ EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_t
             "spec_verify_tree", "spec_row_stats_workspace", "spec_row_stats",
             "spec_workspace_clear", "spec_verify_status_string", "spec_commit_linear",
             "spec_sample_workspace", "spec_sample", "spec_tree_mask", "spec_tree_build_greedy",
-            "spec_verify_tree_typical", "spec_verify_linear_commit", "spec_verify_linear_static")
+            "spec_verify_tree_typical", "spec_verify_linear_commit", "spec_verify_linear_static",
+            "spec_set_wait_limit")
 SV_MAX_STATIC_WORKSPACE = 8 * 1024 * 1024
 
 
@@ -527,6 +530,13 @@ def tree_mask(parent, n_trees: int = 1, *, stream=None):
     st = lib().spec_tree_mask(n_trees, n, _ptr(parent), stride, _ptr(mask), _ptr(ef), _stream(stream))
     _check(st, "spec_tree_mask")
     return {"mask": mask, "err_flags": ef}
+
+
+def set_wait_limit(seconds: float):
+    """spec_set_wait_limit: how long any wait between the waves of a launch may last
+    before it gives up with SV_ERR_INTERNAL, on the current device (a test hook;
+    default 0.25 s)."""
+    _check(lib().spec_set_wait_limit(float(seconds)), "spec_set_wait_limit")
 
 
 def tree_build_greedy(accuracy, budget: int):

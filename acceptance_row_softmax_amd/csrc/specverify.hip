@@ -259,9 +259,13 @@ __device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return ((
 __device__ __forceinline__ bool wait_group(uint32_t* cnt, uint32_t total) {
   bool ok = true;
   if (lane_id() == 0) {
-    ok = false;
-    for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
-      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= total) { ok = true; break; }
+    WaitClock clk;
+    for (;;) {
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= total) break;
+      if (!clk.more()) {
+        ok = false;
+        break;
+      }
       __builtin_amdgcn_s_sleep(4);
     }
     counter_reset(cnt);
@@ -280,7 +284,8 @@ __device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, Row
   const int lane = lane_id();
   uint64_t w[NR][MAX_ROUNDS][4];
   bool ok = false;
-  for (int spin = 0; spin < SPIN_LIMIT && !ok; ++spin) {
+  WaitClock clk;
+  for (bool go = true; go && !ok;) {
     bool mine = true;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -299,7 +304,10 @@ __device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, Row
       }
     }
     ok = __ballot(!mine) == 0ull;
-    if (!ok) __builtin_amdgcn_s_sleep(2);
+    if (!ok) {
+      go = clk.more();
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -473,7 +481,8 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
     // two rows at a time, lane l reading chunks l + 64 t of each
     uint64_t w[2][MAX_ROUNDS][2];
     bool got = false;
-    for (int spin = 0; spin < SPIN_LIMIT && !got; ++spin) {
+    WaitClock clk;
+    for (bool go = true; go && !got;) {
       bool mine = true;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -491,7 +500,10 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
         }
       }
       got = __ballot(!mine) == 0ull;
-      if (!got) __builtin_amdgcn_s_sleep(4);
+      if (!got) {
+        go = clk.more();
+        __builtin_amdgcn_s_sleep(4);
+      }
     }
     ok = ok && got;
 #pragma unroll
@@ -2252,6 +2264,12 @@ sv_status spec_verify_linear_static(sv_mode mode, float temperature, int64_t B, 
                     accept_len, out_tokens, p_target, p_draft, err_flags, ws, (size_t)SV_MAX_STATIC_WORKSPACE);
   if (st != SV_OK) return st;
   return dispatch<LinearLauncher>(dtype, mode == SV_STOCHASTIC, P, hs);
+}
+
+sv_status spec_set_wait_limit(double seconds) {
+  if (!(seconds >= 0.0 && seconds <= 60.0)) return SV_EINVAL;
+  const uint64_t ticks = (uint64_t)(seconds * 1e8);
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_wait_ticks), &ticks, sizeof(ticks)) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream) {

@@ -652,7 +652,26 @@ __device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&
 // Which wave is "last" is decided by device-scope atomic counters in the same
 // workspace; each is reset to zero by the wave that sees it reach its final count.
 // Waits are bounded; a timeout is reported as an error, never a hang.
-constexpr int SPIN_LIMIT = 1 << 18;
+//
+// A wait gives up once the GPU's constant 100 MHz clock has advanced by
+// g_wait_ticks since its first unsuccessful poll (a wait whose first poll succeeds
+// reads neither the clock nor the limit). The limit is per device; the host sets
+// it with spec_set_wait_limit (default 0.25 s).
+constexpr uint64_t WAIT_TICKS = 25000000;
+static __device__ uint64_t g_wait_ticks = WAIT_TICKS;
+
+struct WaitClock {
+  uint64_t end = 0;
+  // Called after an unsuccessful poll: false once the wait's time is up.
+  __device__ __forceinline__ bool more() {
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
+    if (end == 0) {
+      end = now + g_wait_ticks + 1;
+      return true;
+    }
+    return now <= end;
+  }
+};
 
 template <class T>
 struct RecWords {
@@ -689,7 +708,8 @@ __device__ __forceinline__ void put_rec_wave(uint64_t* dst, const T& v, uint32_t
 template <class T>
 __device__ __forceinline__ bool get_rec(const uint64_t* src, T& v, uint32_t tag) {
   uint32_t w[RecWords<T>::N];
-  for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
+  WaitClock clk;
+  for (;;) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < RecWords<T>::N; ++i) {
@@ -701,9 +721,9 @@ __device__ __forceinline__ bool get_rec(const uint64_t* src, T& v, uint32_t tag)
       __builtin_memcpy(&v, w, sizeof(T));
       return true;
     }
+    if (!clk.more()) return false;
     __builtin_amdgcn_s_sleep(2);
   }
-  return false;
 }
 
 // Polls a whole record with one load per word, lane i reading word i (one request
@@ -715,7 +735,8 @@ __device__ __forceinline__ bool poll_rec(const uint64_t* src, T& v, uint32_t tag
   constexpr int N = RecWords<T>::N;
   static_assert(N <= WAVE, "one word per lane");
   const int lane = lane_id();
-  for (int spin = 0; spin < SPIN_LIMIT; ++spin) {
+  WaitClock clk;
+  for (;;) {
     uint64_t x = 0;
     if (lane < N) x = __hip_atomic_load(src + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__ballot(lane < N && (uint32_t)(x >> 32) != tag) == 0ull) {
@@ -725,9 +746,9 @@ __device__ __forceinline__ bool poll_rec(const uint64_t* src, T& v, uint32_t tag
       __builtin_memcpy(&v, w, sizeof(T));
       return true;
     }
+    if (!clk.more()) return false;
     __builtin_amdgcn_s_sleep(8);
   }
-  return false;
 }
 
 template <class T>

@@ -72,7 +72,7 @@
  *      bit2 SV_ERR_TREE    parent[0] != -1, parent[i] outside [0, i), or a node
  *                          deeper than max_depth
  *      bit3 SV_ERR_INTERNAL a wait between workgroups of the launch gave up (after
- *                          2^18 polls, a fraction of a second: only if the GPU did
+ *                          0.25 s, see spec_set_wait_limit: only if the GPU did
  *                          not run the launch's workgroups in dispatch order, or a
  *                          concurrent call shared the workspace); outputs are not
  *                          valid, and a wait that gave up can also leave other
@@ -304,6 +304,17 @@ int64_t spec_tree_build_greedy(int64_t K, int64_t S, const double* accuracy, int
 
 /* Zero-fill `bytes` of a 16-byte aligned workspace on `stream` with a fill kernel (no host sync). */
 sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream);
+
+/* ---------------------------------------------------------------- wait limit (test hook)
+ * How long, in seconds of the GPU's constant 100 MHz clock, any wait between the
+ * waves of one launch may last before it gives up and reports SV_ERR_INTERNAL
+ * (bit3 above), on the current device: default 0.25, at most 60; 0 lets every
+ * wait give up after its second unsuccessful poll. For tests of the give-up path:
+ * set it between calls, never while this library's kernels run on the device, and
+ * clear the workspace of a call that gave up before its next use. A synchronous
+ * copy to the device; SV_EINVAL outside [0, 60] (or NaN), SV_EHIP if the copy fails.
+ */
+sv_status spec_set_wait_limit(double seconds);
 
 /* ---------------------------------------------------------------- linear drafts, no allocation
  * For callers that cannot allocate device memory: code under HIP graph capture,

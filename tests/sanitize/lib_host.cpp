@@ -203,6 +203,9 @@ static void row_checks() {
   CHECK(spec_commit_linear(0, 2, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr,
                            nullptr) == SV_OK);
   CHECK(spec_workspace_clear(nullptr, 256, nullptr) == SV_EINVAL);
+  CHECK(spec_set_wait_limit(-1.0) == SV_EINVAL);
+  CHECK(spec_set_wait_limit(61.0) == SV_EINVAL);
+  CHECK(spec_set_wait_limit(NAN) == SV_EINVAL);
   CHECK(spec_workspace_clear(reinterpret_cast<void*>(((uintptr_t)1 << 40) + 8), 256, nullptr) == SV_EINVAL);
 }
 
