@@ -192,7 +192,6 @@ struct LinearParams {
   int C;                // chunks per row
   int RW;               // words per chunk record
   int EV;               // events per sequence (stochastic): k pair combines, target row k, the final token
-  int G;                // chunks per residual wave (1; the kernel's template argument)
   bool hold;            // residual waves keep their chunk until the draw is placed (see linear_residual_wave)
   float c0;
   uint32_t tag;
@@ -780,9 +779,8 @@ __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_
 // wave that cannot start) every residual wave keeps its chunk and its unit sums
 // and waits for the last one's verdict; the wave holding the picked chunk scans it
 // from its registers.
-template <int DT, int G>
+template <int DT>
 __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
-  static_assert(G == 1, "one chunk per residual wave");
   const int lane = lane_id();
   const uint32_t CG = (uint32_t)P.C;   // residual waves per sequence
   const int64_t k = P.k;
@@ -973,7 +971,7 @@ struct Role {
   uint32_t q, b, c;   // stream: row q, chunk c; residual: sequence b, group c; finishers: sequence b, position c
 };
 
-template <bool STOCH, int G>
+template <bool STOCH>
 __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
   Role r;
   r.kind = ROLE_IDLE;
@@ -1006,7 +1004,7 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
       }
     } else {
       // sequence blocks: C chunk waves of target row k, its finisher, CG residual waves
-      const uint32_t CG = P.k > 0 ? ((uint32_t)P.C + G - 1) / G : 0u;
+      const uint32_t CG = P.k > 0 ? (uint32_t)P.C : 0u;
       const uint32_t Q = NS + 1 + CG;
       const uint32_t v = w - P.tk0;
       r.b = v / Q;
@@ -1026,18 +1024,18 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
   return r;
 }
 
-template <int DT, bool STOCH, int G>
+template <int DT, bool STOCH>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(3))) void linear_kernel(LinearParams P) {
   const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
   if (w >= P.n_waves) return;
-  const Role r = linear_role<STOCH, G>(P, (uint32_t)w);
+  const Role r = linear_role<STOCH>(P, (uint32_t)w);
   Ev ev{0, 0u, false, 0};
   if (r.kind == ROLE_STREAM) {
     linear_chunk_wave<DT, STOCH>(P, r.q, r.c);
   } else if constexpr (STOCH) {
     if (r.kind == ROLE_PAIR) ev = pair_finish<DT>(P, r.b, r.c);
     else if (r.kind == ROLE_ROWK) ev = rowk_finish<DT>(P, r.b);
-    else if (r.kind == ROLE_RESID) ev = linear_residual_wave<DT, G>(P, r.b, r.c);
+    else if (r.kind == ROLE_RESID) ev = linear_residual_wave<DT>(P, r.b, r.c);
   } else {
     if (r.kind == ROLE_GREEDY) greedy_finish<DT>(P, r.b);
   }
@@ -1864,7 +1862,7 @@ Layout rowstats_layout(int64_t rows, int64_t V, sv_dtype dt) {
 template <int DT, bool STOCH>
 struct LinearLauncher {
   static sv_status run(const LinearParams& P, hipStream_t s) {
-    hipLaunchKernelGGL((linear_kernel<DT, STOCH, 1>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
+    hipLaunchKernelGGL((linear_kernel<DT, STOCH>), dim3(blocks_for(P.n_waves)), dim3(BLOCK), 0, s, P);
     return launch_status();
   }
 };
@@ -1939,9 +1937,9 @@ inline int64_t stochastic_wave_capacity(sv_dtype dt) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= CAP_DEVICES || !dtype_ok(dt)) return 0;
   const int64_t c = g_capacity[dev][dt].load(std::memory_order_relaxed);
   if (c > 0) return c;
-  const void* fn = dt == SV_F32 ? reinterpret_cast<const void*>(&linear_kernel<DT_F32, true, 1>)
-                 : dt == SV_BF16 ? reinterpret_cast<const void*>(&linear_kernel<DT_BF16, true, 1>)
-                                 : reinterpret_cast<const void*>(&linear_kernel<DT_F16, true, 1>);
+  const void* fn = dt == SV_F32 ? reinterpret_cast<const void*>(&linear_kernel<DT_F32, true>)
+                 : dt == SV_BF16 ? reinterpret_cast<const void*>(&linear_kernel<DT_BF16, true>)
+                                 : reinterpret_cast<const void*>(&linear_kernel<DT_F16, true>);
   int blocks = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, BLOCK, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
@@ -2003,14 +2001,13 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
   // residual waves: one per chunk (they come after every streaming wave); hold mode
   // when all of them fit on the GPU at once, with room to spare
-  P.G = 1;
   P.hold = stoch && k > 0 && B * P.C <= stochastic_wave_capacity(dtype) / 2;
   // see linear_role for the order of the waves
   if (!stoch) {
     P.n_waves = sh.RQ * sh.C + B;
     P.tk0 = 0;
   } else {
-    const int64_t CG = k > 0 ? (P.C + P.G - 1) / P.G : 0;
+    const int64_t CG = k > 0 ? P.C : 0;
     P.tk0 = (uint32_t)(k * B * (2 * sh.C + 1));
     P.n_waves = P.tk0 + B * (sh.C + 1 + CG);
   }
