@@ -795,6 +795,9 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);
+  // No draft rejected: nothing to draw here (the bonus token is target row k's), so
+  // no count either; each residual wave has cleared its own copy of the decision.
+  if (d.kind == 0) return Ev{0, 0u, false, 0};
   // Counted before the sums: the count's round trip overlaps this wave's loads. The
   // last to count draws; it reads the others' records with polling reads, which
   // wait for any that are not written yet.
@@ -848,7 +851,6 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   }
   // last residual wave of the sequence: draw the correction token
   if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
-  if (d.kind == 0) return Ev{0, 0u, false, 0};   // no draft rejected: the bonus token is recorded already
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind != 1) return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
   // Round trips overlap: without hold mode the token event's count goes out with
