@@ -2,29 +2,29 @@
 // declared in include/specverify.h.
 //
 // Linear drafts: one launch per call. Its workgroups hold two independent waves;
-// in dispatch order the waves are
-//  * streaming waves, one per (row, 8 KiB chunk), rows in position order (the
-//    target/draft rows of position 0 of every sequence, then position 1, ...,
-//    the target rows after the last draft at the end). A streaming wave reduces its
-//    chunk to a partial (max, argmax or softmax sum) and writes it as a tagged
-//    record. The last wave to finish a row (an atomic counter per row) combines
-//    the row: max, argmax, normaliser, the probability of the draft token at that
-//    row, and, for the row after the last draft, the bonus draw.
-//  * per sequence, the second row combined of a (target, draft) pair runs that
-//    position's acceptance test and records the outcome in the sequence's state
-//    word; the wave whose update fixes the first rejected position L hands the
-//    rows t_L, d_L to the residual waves (or, if no draft is rejected, releases
-//    the bonus token);
-//  * residual waves (stochastic mode), one per (sequence, chunk), dispatched after
-//    the streaming waves of positions 0..k-1 and before those of the target rows
-//    k (the decision never depends on row k): each sums max(0, p_t,L - p_d,L)
-//    over its chunk; the last of a sequence picks the chunk holding u*S and draws
-//    the correction token by an inverse-CDF scan inside it;
+// in dispatch order:
+//  * greedy: one streaming wave per (target row, 8 KiB chunk), rows in position
+//    order, each writing its chunk's max and lowest argmax as a tagged record; then
+//    one finishing wave per sequence, which reads its rows' records, takes L as the
+//    first draft that is not its row's argmax and writes the outputs.
+//  * stochastic: for each position i < k and each sequence, the streaming waves of
+//    rows t_i and d_i (each writes its chunk's max, softmax weight sum and the draft
+//    token's logit as a tagged record and counts itself into the pair's counter
+//    without waiting), then the pair's finishing wave: it combines both rows, runs
+//    the acceptance test u_i < p_t,i(x_i) / p_d,i(x_i) and records the outcome in
+//    the sequence's state word; the update that settles the first rejected position
+//    L hands rows t_L, d_L to the residual waves. Then, per sequence, the streaming
+//    waves of target row k, that row's finishing wave (the bonus draw) and one
+//    residual wave per chunk: each sums max(0, p_t,L - p_d,L) over its chunk; the
+//    last of a sequence picks the chunk holding u*S, and the correction token is
+//    drawn by an inverse-CDF scan inside it (by the wave that holds that chunk in
+//    hold mode, else after a reload);
 //  * the last event of a sequence (an atomic counter per sequence) writes all of
 //    its outputs.
-// No wave ever waits for work that is dispatched after it: residual waves wait
-// for decisions of streaming waves dispatched before them, and a last event waits
-// only for a token whose wave has already counted itself.
+// No wave ever waits for work dispatched after it: finishing waves wait for the
+// streaming waves before them, residual waves for decisions of finishing waves
+// before them, and a last event only for a token whose wave has already counted
+// itself. Every wait is bounded in time.
 //
 // Trees: a streaming launch of the same kind reduces every node's row (greedy:
 // its argmax is the node's token; stochastic: for a small batch the token is
