@@ -125,14 +125,21 @@ __device__ __forceinline__ ResidW make_residw(const Decision& d, float c0) {
   return rw;
 }
 
-// Residual sum over a loaded chunk of rows t_L, d_L (same value in every lane);
-// us receives this lane's unit sums, as the in-chunk search forms them.
-template <int DT>
-__device__ __forceinline__ double residual_raw_sum(const Raw& rt, const Raw& rd, const ResidW& rw, float (&us)[CU]) {
+// Residual waves take half a chunk each (RH parts of HU units per lane): two rows'
+// halves are 32 registers per lane, where whole chunks would be 64, which would
+// set the occupancy of the whole launch.
+constexpr int RH = 2;
+constexpr int HU = CU / RH;
+
+// Residual sum over a loaded run of units of rows t_L, d_L (same value in every
+// lane); us receives this lane's unit sums, as the in-run search forms them.
+template <int DT, int NU>
+__device__ __forceinline__ double residual_raw_sum(const RawN<NU>& rt, const RawN<NU>& rd, const ResidW& rw,
+                                                   float (&us)[NU]) {
   chunk_unit_sums<DT, true>(rt, rd, rw, us);
   double s = 0.0;
 #pragma unroll
-  for (int j = 0; j < CU; ++j) s += (double)us[j];
+  for (int j = 0; j < NU; ++j) s += (double)us[j];
   return wave_sum(s);
 }
 
@@ -178,9 +185,9 @@ struct LinearParams {
   uint64_t* seg;        // [RQ][C][RW] chunk records
   uint64_t* pst;        // [B][k]   PairStat records (stochastic)
   uint64_t* rks;        // [B]      RowStat records of target rows k (stochastic)
-  uint64_t* dec;        // [B][C]   Decision records, one copy per residual wave
-  uint64_t* res;        // [B][C]   ResPart records
-  uint64_t* verd;       // [B][C]   Verdict records (hold mode)
+  uint64_t* dec;        // [B][CG]  Decision records, one copy per residual wave
+  uint64_t* res;        // [B][CG]  ResPart records
+  uint64_t* verd;       // [B][CG]  Verdict records (hold mode)
   uint64_t* tok;        // [B]      Token records
   uint64_t* prob;       // [B][k]   Probs records (stochastic)
   uint32_t* grp_cnt;    // [groups] segments counted per combine group
@@ -190,6 +197,7 @@ struct LinearParams {
   uint32_t* errw;       // [B]      error bits per sequence
   int64_t B, k, V;
   int C;                // chunks per row
+  int CG;               // residual waves per sequence: RH per chunk
   int RW;               // words per chunk record
   int EV;               // events per sequence (stochastic): k pair combines, target row k, the final token
   bool hold;            // residual waves keep their chunk until the draw is placed (see linear_residual_wave)
@@ -277,61 +285,79 @@ constexpr uint32_t NOT_HELD = 0x7fffffffu;
 // The chunk partials of NR consecutive rows q0, q0+1 (stochastic records; lane l
 // holding chunks l + 64 t of each row, and the draft token's logit if some chunk of
 // the row holds it), each word polled until it carries the call's tag, then zeroed.
-// false on timeout.
+// One round of 64 chunks at a time (for both rows), so that only one round's words
+// are held; every round's wait counts against the same time limit. false on timeout.
 template <int NR>
 __device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, RowParts (&rp)[NR]) {
   const int lane = lane_id();
-  uint64_t w[NR][MAX_ROUNDS][4];
-  bool ok = false;
+  bool ok = true;
   WaitClock clk;
-  for (bool go = true; go && !ok;) {
-    bool mine = true;
+  int xin[NR];
+  uint32_t xv[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    xin[r] = 0;
+    xv[r] = 0;
+  }
+#pragma unroll
+  for (int t = 0; t < MAX_ROUNDS; ++t) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
+      rp[r].m[t] = -INFINITY;
+      rp[r].idx[t] = INT_SENTINEL;
+      rp[r].s[t] = 0.0;
+    }
+    if (t * WAVE >= P.C) continue;
+    const int c = t * WAVE + lane;
+    const bool in = c < P.C;
+    uint64_t w[NR][4];
 #pragma unroll
-      for (int t = 0; t < MAX_ROUNDS; ++t) {
-        if (t * WAVE >= P.C) break;
-        const int c = t * WAVE + lane;
-        if (c < P.C) {
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[r][e] = 0;
+    bool got = false;
+    for (bool go = ok; go && !got;) {   // after a timeout, later rounds are not waited for
+      bool mine = true;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (in) {
           const uint64_t* q = P.seg + ((q0 + r) * P.C + c) * P.RW;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            w[r][t][e] = seg_load(q + e);
-            mine = mine && (uint32_t)(w[r][t][e] >> 32) == P.tag;
+            w[r][e] = seg_load(q + e);
+            mine = mine && (uint32_t)(w[r][e] >> 32) == P.tag;
           }
         }
       }
+      got = __ballot(!mine) == 0ull;
+      if (!got) {
+        go = clk.more();
+        __builtin_amdgcn_s_sleep(2);
+      }
     }
-    ok = __ballot(!mine) == 0ull;
-    if (!ok) {
-      go = clk.more();
-      __builtin_amdgcn_s_sleep(2);
+    ok = ok && got;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (in) {
+        rp[r].m[t] = __uint_as_float((uint32_t)w[r][0]);
+        rp[r].s[t] = __longlong_as_double((long long)(((uint64_t)(uint32_t)w[r][2] << 32) | (uint32_t)w[r][1]));
+        if ((uint32_t)w[r][3] != NOT_HELD) {
+          xin[r] = 1;
+          xv[r] = (uint32_t)w[r][3];
+        }
+        // leave the record zero for the next call
+        uint64_t* q = P.seg + ((q0 + r) * P.C + c) * P.RW;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) seg_store(q + e, 0);
+      }
     }
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    int xin = 0;
-    uint32_t xv = 0;
-#pragma unroll
-    for (int t = 0; t < MAX_ROUNDS; ++t) {
-      const int c = t * WAVE + lane;
-      const bool in = t * WAVE < P.C && c < P.C;
-      rp[r].m[t] = in ? __uint_as_float((uint32_t)w[r][t][0]) : -INFINITY;
-      rp[r].idx[t] = INT_SENTINEL;
-      rp[r].s[t] = in ? __longlong_as_double((long long)(((uint64_t)(uint32_t)w[r][t][2] << 32) |
-                                                        (uint32_t)w[r][t][1])) : 0.0;
-      if (in && (uint32_t)w[r][t][3] != NOT_HELD) {
-        xin = 1;
-        xv = (uint32_t)w[r][t][3];
-      }
-    }
-    const unsigned long long xm = __ballot(xin != 0);
+    const unsigned long long xm = __ballot(xin[r] != 0);
     rp[r].xin = xm != 0ull;
-    rp[r].xv = __uint_as_float((uint32_t)__shfl((int)xv, xm ? first_lane(xm) : 0));
+    rp[r].xv = __uint_as_float((uint32_t)__shfl((int)xv[r], xm ? first_lane(xm) : 0));
     rp[r].got = ok;
-    // leave the records zero for the next call
-    uint64_t* base = P.seg + (q0 + r) * P.C * P.RW;
-    for (int64_t o = lane; o < (int64_t)P.C * P.RW; o += WAVE) seg_store(base + o, 0);
   }
   return ok;
 }
@@ -546,14 +572,14 @@ __device__ __forceinline__ void publish_decision(const LinearParams& P, int64_t 
   uint32_t w[DEC_WORDS];
   __builtin_memcpy(w, &d, sizeof(Decision));
   const int lane = lane_id();
-  const int n = P.C * DEC_WORDS;
+  const int n = P.CG * DEC_WORDS;
   for (int e0 = 0; e0 < n; e0 += WAVE) {
     const int e = e0 + lane;
     const int j = e % DEC_WORDS;
     uint32_t v = 0;
 #pragma unroll
     for (int i = 0; i < DEC_WORDS; ++i) if (j == i) v = w[i];
-    if (e < n) __hip_atomic_store(P.dec + b * P.C * DEC_WORDS + e, ((uint64_t)P.tag << 32) | v, __ATOMIC_RELAXED,
+    if (e < n) __hip_atomic_store(P.dec + b * P.CG * DEC_WORDS + e, ((uint64_t)P.tag << 32) | v, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -782,14 +808,14 @@ __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_
 template <int DT>
 __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
   const int lane = lane_id();
-  const uint32_t CG = (uint32_t)P.C;   // residual waves per sequence
+  const uint32_t CG = (uint32_t)P.CG;   // residual waves per sequence
   const int64_t k = P.k;
   Decision d;
   d.L = 0;
   d.kind = 2;
   d.Mt = d.Md = 0.0f;
   d.Zt = d.Zd = 0.0;
-  uint64_t* dr = P.dec + (b * P.C + g) * DEC_WORDS;   // this wave's copy of the decision
+  uint64_t* dr = P.dec + (b * P.CG + g) * DEC_WORDS;   // this wave's copy of the decision
   if (!poll_rec(dr, d, P.tag)) d.kind = 3;   // 3: the decision never arrived
   if (lane == 0) clear_rec<Decision>(dr);
   const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
@@ -803,22 +829,24 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   // wait for any that are not written yet.
   uint32_t old = 0;
   if (lane == 0) old = counter_add(P.res_cnt + b * CSTRIDE, 1u);
-  Raw rt, rd;
+  // part g of the sequence's rows: chunk g / RH, half g % RH
+  const int64_t u0 = (g / RH) * CHUNK_UNITS + (g % RH) * (HU * WAVE);
+  RawN<HU> rt, rd;
   Chunk kg;
-  float us[CU];
+  float us[HU];
   if (d.kind == 1) {
-    kg = load_chunk<DT>(trow, P.V, g, rt);
-    load_chunk<DT>(drow, P.V, g, rd);
+    kg = load_units<DT, HU>(trow, P.V, u0, rt);
+    load_units<DT, HU>(drow, P.V, u0, rd);
     ResPart r;
     r.s = residual_raw_sum<DT>(rt, rd, rw, us);
-    put_rec_wave(P.res + (b * P.C + g) * RES_WORDS, r, P.tag);
+    put_rec_wave(P.res + (b * P.CG + g) * RES_WORDS, r, P.tag);
   }
   old = bcast(old);
   const float u = P.uniforms[b * (k + 1) + k];
   if (old + 1 != CG) {
     if (!(P.hold && d.kind == 1)) return Ev{0, 0u, false, 0};
     // hold mode: wait for the verdict on this chunk
-    uint64_t* vr = P.verd + (b * P.C + g) * VERD_WORDS;
+    uint64_t* vr = P.verd + (b * P.CG + g) * VERD_WORDS;
     Verdict v;
     v.kind = 0;
     v.th = 0.0;
@@ -853,23 +881,23 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind != 1) return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
-  // Round trips overlap: without hold mode the token event's count goes out with
-  // the reads of the residual sums; after the pick, the chosen chunk's reloads go
-  // out with the emission's reads (if this is the sequence's last event, which the
-  // count tells); then the scan. Otherwise the last event's wave waits for the token
-  // record.
+  // Without hold mode the token event's count goes out with the reads of the
+  // residual sums; after the pick the chosen part is reloaded and scanned, and if
+  // the count says this is the sequence's last event the wave writes the outputs.
+  // Otherwise the last event's wave waits for the token record.
   uint32_t fo = 0;
   if (!P.hold && lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
-  double wl[MAX_ROUNDS];
+  constexpr int RR = RH * MAX_ROUNDS;   // rounds of 64 parts
+  double wl[RR];
   bool ok = true;
 #pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
+  for (int t = 0; t < RR; ++t) {
     wl[t] = 0.0;
-    if (t * WAVE >= P.C) continue;
+    if (t * WAVE >= (int)CG) continue;
     const int cc = t * WAVE + lane;
-    if (cc < P.C) {
+    if (cc < (int)CG) {
       ResPart r;
-      uint64_t* rec = P.res + (b * P.C + cc) * RES_WORDS;
+      uint64_t* rec = P.res + (b * P.CG + cc) * RES_WORDS;
       const bool gr = get_rec(rec, r, P.tag);
       ok = ok && gr;
       wl[t] = gr ? r.s : 0.0;
@@ -892,26 +920,26 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     // over chunk sums formed here.
     double tot = 0.0;
 #pragma unroll
-    for (int t = 0; t < MAX_ROUNDS; ++t) tot += wl[t];
+    for (int t = 0; t < RR; ++t) tot += wl[t];
     tot = wave_sum(tot);
-    pk = pick_chunk(P.C, (double)u, wl);
+    pk = pick_chunk((int)CG, (double)u, wl);
     if (pk.c < 0 && tot == 0.0) {
       zero = true;
       rx.mc0d = rx.mc0t;
       rx.izd = 0.0f;
       dx = trow;
 #pragma unroll
-      for (int t = 0; t < MAX_ROUNDS; ++t) wl[t] = 0.0;
-      // (this wave's own chunk registers serve as the buffer)
+      for (int t = 0; t < RR; ++t) wl[t] = 0.0;
+      // (this wave's own registers serve as the buffer)
 #pragma unroll 1
-      for (int c = 0; c < P.C; ++c) {
-        load_chunk<DT>(trow, P.V, c, rt);
+      for (int c = 0; c < (int)CG; ++c) {
+        load_units<DT, HU>(trow, P.V, (c / RH) * CHUNK_UNITS + (c % RH) * (HU * WAVE), rt);
         const double sc = residual_raw_sum<DT>(rt, rt, rx, us);
 #pragma unroll
-        for (int t = 0; t < MAX_ROUNDS; ++t)
+        for (int t = 0; t < RR; ++t)
           if (t * WAVE + lane == c) wl[t] = sc;
       }
-      pk = pick_chunk(P.C, (double)u, wl);
+      pk = pick_chunk((int)CG, (double)u, wl);
     }
   }
   const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
@@ -919,14 +947,14 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     // every other residual wave of the sequence waits for its verdict (one store
     // instruction: lane c writes chunk c's kind, the picked chunk's record whole)
     const int pc = pk.c;
-    for (int c0 = 0; c0 < P.C; c0 += WAVE) {
+    for (int c0 = 0; c0 < (int)CG; c0 += WAVE) {
       const int c = c0 + lane;
-      if (c < P.C && c != g) {
+      if (c < (int)CG && c != g) {
         Verdict v;
         v.kind = c == pc ? (zero ? 2 : 1) : 0;
         v.pad = 0;
         v.th = th;
-        put_rec(P.verd + (b * P.C + c) * VERD_WORDS, v, P.tag);
+        put_rec(P.verd + (b * P.CG + c) * VERD_WORDS, v, P.tag);
       }
     }
     if (pc < 0) return Ev{b, 1u, true, rec_ok ? -1 : -2};   // nothing to draw from
@@ -934,20 +962,19 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     // the pick is this wave's own chunk, whose registers were not kept: the reload
     // below serves
   }
-  // the picked chunk, reloaded into this wave's own chunk registers
+  // the picked part, reloaded into this wave's own registers
   if (pk.c >= 0) {
-    kg = load_chunk<DT>(trow, P.V, pk.c, rt);
-    load_chunk<DT>(dx, P.V, pk.c, rd);
+    const int64_t pu = (pk.c / RH) * CHUNK_UNITS + (pk.c % RH) * (HU * WAVE);
+    kg = load_units<DT, HU>(trow, P.V, pu, rt);
+    load_units<DT, HU>(dx, P.V, pu, rd);
   }
-  EmitIn ein;
-  if (last) {
-    if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-    ein = emit_load<DT, true>(P, b, true);
-  }
+  // (the emission's reads follow the scan: issued before it, they would hold their
+  // registers through it, and those registers set the launch's occupancy)
   if (pk.c >= 0) y = (int)chunk_invcdf<DT, true>(kg, rt, rd, th, rx);
   if (P.hold) return Ev{b, 1u, true, y};
   if (last) {
-    emit_store<DT, true>(P, b, ein, y);
+    if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+    linear_emit<DT, true>(P, b, y);
   } else if (lane == 0) {
     Token t;
     t.y = y;
@@ -1006,7 +1033,7 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
       }
     } else {
       // sequence blocks: C chunk waves of target row k, its finisher, CG residual waves
-      const uint32_t CG = P.k > 0 ? (uint32_t)P.C : 0u;
+      const uint32_t CG = P.k > 0 ? (uint32_t)P.CG : 0u;
       const uint32_t Q = NS + 1 + CG;
       const uint32_t v = w - P.tk0;
       r.b = v / Q;
@@ -1843,10 +1870,10 @@ inline LinearShape linear_shape(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv
 Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
   const LinearShape s = linear_shape(B, k, V, dt, mode);
   return make_layout({(size_t)(s.RQ * s.C * s.RW) * 8, (size_t)(B * k) * PST_WORDS * 8, (size_t)B * ROW_WORDS * 8,
-                      (size_t)(B * s.C) * DEC_WORDS * 8, (size_t)(B * s.C) * RES_WORDS * 8, (size_t)B * 8,
+                      (size_t)(B * s.C * RH) * DEC_WORDS * 8, (size_t)(B * s.C * RH) * RES_WORDS * 8, (size_t)B * 8,
                       (size_t)(s.groups * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
                       (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8,
-                      (size_t)(B * s.C) * VERD_WORDS * 8});
+                      (size_t)(B * s.C * RH) * VERD_WORDS * 8});
 }
 
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
@@ -2003,13 +2030,14 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
   // residual waves: one per chunk (they come after every streaming wave); hold mode
   // when all of them fit on the GPU at once, with room to spare
-  P.hold = stoch && k > 0 && B * P.C <= stochastic_wave_capacity(dtype) / 2;
+  P.CG = RH * P.C;
+  P.hold = stoch && k > 0 && B * P.CG <= stochastic_wave_capacity(dtype) / 2;
   // see linear_role for the order of the waves
   if (!stoch) {
     P.n_waves = sh.RQ * sh.C + B;
     P.tk0 = 0;
   } else {
-    const int64_t CG = k > 0 ? P.C : 0;
+    const int64_t CG = k > 0 ? P.CG : 0;
     P.tk0 = (uint32_t)(k * B * (2 * sh.C + 1));
     P.n_waves = P.tk0 + B * (sh.C + 1 + CG);
   }

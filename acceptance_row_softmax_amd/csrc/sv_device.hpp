@@ -235,9 +235,12 @@ struct Chunk {
   int64_t u0;
 };
 
-struct Raw {
-  uint4 v[CU];
+// NU consecutive 16-byte units per lane: a whole chunk (CU) or a part of one.
+template <int NU>
+struct RawN {
+  uint4 v[NU];
 };
+using Raw = RawN<CU>;
 
 template <int DT>
 __device__ __forceinline__ uint32_t neg_inf_bits() {
@@ -271,25 +274,26 @@ __device__ __forceinline__ uint4 unit_by_elements(const char* row, int64_t V, in
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Loads this lane's CU units of chunk c.
-template <int DT>
-__device__ __forceinline__ Chunk load_chunk(const char* row, int64_t V, int64_t c, Raw& r) {
+// Loads this lane's NU units of the run of NU * WAVE units from unit u0 (this
+// lane's unit j is u0 + j * WAVE + lane).
+template <int DT, int NU>
+__device__ __forceinline__ Chunk load_units(const char* row, int64_t V, int64_t u0, RawN<NU>& r) {
   constexpr int W = DTraits<DT>::W;
   Chunk k;
   k.row = row;
   k.V = V;
-  k.u0 = c * CHUNK_UNITS;
+  k.u0 = u0;
   const int lane = lane_id();
   const bool aligned = row_aligned(row);
-  if (aligned && (k.u0 + CHUNK_UNITS) * W <= V) {
-    // the common case: the whole chunk is inside an aligned row
+  if (aligned && (k.u0 + NU * WAVE) * W <= V) {
+    // the common case: the whole run is inside an aligned row
     const uint4* p = reinterpret_cast<const uint4*>(row) + k.u0 + lane;
 #pragma unroll
-    for (int j = 0; j < CU; ++j) r.v[j] = p[j * WAVE];
+    for (int j = 0; j < NU; ++j) r.v[j] = p[j * WAVE];
   } else {
     const uint32_t ninf = neg_inf_bits<DT>();
 #pragma unroll
-    for (int j = 0; j < CU; ++j) {
+    for (int j = 0; j < NU; ++j) {
       const int64_t u = k.u0 + j * WAVE + lane;
       if (aligned && (u + 1) * W <= V) {
         r.v[j] = reinterpret_cast<const uint4*>(row)[u];
@@ -303,6 +307,12 @@ __device__ __forceinline__ Chunk load_chunk(const char* row, int64_t V, int64_t 
   return k;
 }
 
+// Loads this lane's CU units of chunk c.
+template <int DT>
+__device__ __forceinline__ Chunk load_chunk(const char* row, int64_t V, int64_t c, Raw& r) {
+  return load_units<DT, CU>(row, V, c * CHUNK_UNITS, r);
+}
+
 // The W values of this lane's unit j.
 template <int DT>
 __device__ __forceinline__ void unit_values(const Raw& r, int j, float (&x)[DTraits<DT>::W]) {
@@ -312,8 +322,21 @@ __device__ __forceinline__ void unit_values(const Raw& r, int j, float (&x)[DTra
 // Partial of a chunk (same value in every lane): max, with the lowest index
 // holding it if ARG (NaN never chosen), if SUM the weight sum relative to
 // fl32(max*c0), and the logit at row index x if the chunk holds it (x < 0: none).
+// Makes the compiler take the chunk's raw words as changed, so that logits it
+// decoded from them for one pass are not kept in registers for the next (it
+// decodes them again: one or two instructions per 32-bit word). fp32 words are the
+// logits themselves and need no barrier.
+template <int DT, int NU>
+__device__ __forceinline__ void decode_barrier(RawN<NU>& r) {
+  if constexpr (DT != DT_F32) {
+#pragma unroll
+    for (int j = 0; j < NU; ++j)
+      asm volatile("" : "+v"(r.v[j].x), "+v"(r.v[j].y), "+v"(r.v[j].z), "+v"(r.v[j].w));
+  }
+}
+
 template <int DT, bool SUM, bool ARG>
-__device__ __forceinline__ Partial chunk_reduce(const Chunk& k, const Raw& r, float c0, int64_t x) {
+__device__ __forceinline__ Partial chunk_reduce(const Chunk& k, Raw r, float c0, int64_t x) {
   constexpr int W = DTraits<DT>::W;
   float best = -INFINITY;
   int pos = INT_SENTINEL;
@@ -341,6 +364,7 @@ __device__ __forceinline__ Partial chunk_reduce(const Chunk& k, const Raw& r, fl
   }
   p.s = 0.0;
   if constexpr (SUM) {
+    decode_barrier<DT>(r);   // decode again for the sums rather than hold every logit
     const float mc0 = chunk_mc0(p.m, c0);
     double s = 0.0;
 #pragma unroll
@@ -475,8 +499,8 @@ struct ResidW {
 };
 
 // Weights of this lane's unit j (j a compile-time constant after unrolling).
-template <int DT, bool PAIR, class WT>
-__device__ __forceinline__ void unit_weights(const Raw& ra, const Raw& rb, int j, const WT& wt,
+template <int DT, bool PAIR, class WT, int NU>
+__device__ __forceinline__ void unit_weights(const RawN<NU>& ra, const RawN<NU>& rb, int j, const WT& wt,
                                              float (&w)[DTraits<DT>::W]) {
   constexpr int W = DTraits<DT>::W;
   float xa[W], xb[W];
@@ -494,11 +518,12 @@ __device__ __forceinline__ void unit_weights(const Raw& ra, const Raw& rb, int j
 // Units in row order are j-major, lane-minor. The search first finds the unit row
 // j whose running total crosses th (fp64 wave totals), then the lane inside it
 // (one fp64 prefix scan), then the element inside that unit.
-template <int DT, bool PAIR, class WT>
-__device__ __forceinline__ void chunk_unit_sums(const Raw& ra, const Raw& rb, const WT& wt, float (&us)[CU]) {
+template <int DT, bool PAIR, class WT, int NU>
+__device__ __forceinline__ void chunk_unit_sums(const RawN<NU>& ra, const RawN<NU>& rb, const WT& wt,
+                                                float (&us)[NU]) {
   constexpr int W = DTraits<DT>::W;
 #pragma unroll
-  for (int j = 0; j < CU; ++j) {
+  for (int j = 0; j < NU; ++j) {
     float w[W];
     unit_weights<DT, PAIR>(ra, rb, j, wt, w);
     us[j] = pairwise_sum<W>(w);
@@ -507,15 +532,15 @@ __device__ __forceinline__ void chunk_unit_sums(const Raw& ra, const Raw& rb, co
 
 // The same search from this lane's unit weight sums us[j] (unit j*64 + lane, as
 // chunk_unit_sums forms them), which the caller may already hold.
-template <int DT, bool PAIR, class WT>
-__device__ __forceinline__ int64_t chunk_invcdf_us(const Chunk& k, const Raw& ra, const Raw& rb, const float (&us)[CU],
+template <int DT, bool PAIR, class WT, int NU>
+__device__ __forceinline__ int64_t chunk_invcdf_us(const Chunk& k, RawN<NU> ra, RawN<NU> rb, const float (&us)[NU],
                                                    double th, const WT& wt) {
   constexpr int W = DTraits<DT>::W;
   const int lane = lane_id();
   double off = 0.0, offj = 0.0;
   int hj = -1;
 #pragma unroll
-  for (int j = 0; j < CU; ++j) {
+  for (int j = 0; j < NU; ++j) {
     const double t = wave_sum((double)us[j]);
     if (hj < 0 && off + t > th) { hj = j; offj = off; }
     off += t;
@@ -526,7 +551,7 @@ __device__ __forceinline__ int64_t chunk_invcdf_us(const Chunk& k, const Raw& ra
   if (hj >= 0) {
     float uj = us[0];
 #pragma unroll
-    for (int j = 1; j < CU; ++j) if (j == hj) uj = us[j];
+    for (int j = 1; j < NU; ++j) if (j == hj) uj = us[j];
     const double incl = wave_incl_scan((double)uj);
     const unsigned long long hit = __ballot(offj + incl > th);
     if (hit) {
@@ -542,18 +567,21 @@ __device__ __forceinline__ int64_t chunk_invcdf_us(const Chunk& k, const Raw& ra
   if (key < 0) {
     // no crossing: the last unit of positive weight in the chunk
 #pragma unroll
-    for (int j = 0; j < CU; ++j) if (us[j] > 0.0f) key = j * WAVE + lane;
+    for (int j = 0; j < NU; ++j) if (us[j] > 0.0f) key = j * WAVE + lane;
     key = wave_max_int(key);
     if (key < 0) return -1;
   }
   const int kj = key / WAVE, kl = key % WAVE;
+  // the crossing unit decoded again rather than every unit's logits held since the sums
+  decode_barrier<DT>(ra);
+  if constexpr (PAIR) decode_barrier<DT>(rb);
   // the unit's weights, selected by a branch per unit row (wave-uniform) so that
   // the register array is never indexed at run time
   float w[W];
 #pragma unroll
   for (int e = 0; e < W; ++e) w[e] = 0.0f;
 #pragma unroll
-  for (int j = 0; j < CU; ++j)
+  for (int j = 0; j < NU; ++j)
     if (j == kj) unit_weights<DT, PAIR>(ra, rb, j, wt, w);
   int pick = -1;
   if (lane == kl) {
@@ -574,16 +602,16 @@ __device__ __forceinline__ int64_t chunk_invcdf_us(const Chunk& k, const Raw& ra
   return (k.u0 + kj * WAVE + kl) * W + pick;
 }
 
-template <int DT, bool PAIR, class WT>
-__device__ __forceinline__ int64_t chunk_invcdf(const Chunk& k, const Raw& ra, const Raw& rb, double th,
+template <int DT, bool PAIR, class WT, int NU>
+__device__ __forceinline__ int64_t chunk_invcdf(const Chunk& k, const RawN<NU>& ra, const RawN<NU>& rb, double th,
                                                 const WT& wt) {
-  float us[CU];
+  float us[NU];
   chunk_unit_sums<DT, PAIR>(ra, rb, wt, us);
   return chunk_invcdf_us<DT, PAIR>(k, ra, rb, us, th, wt);
 }
 
 // ------------------------------------------------------------------ chunk selection over a row
-// Chunk weights held lane-strided: lane l holds chunks l + 64*t (t < MAX_ROUNDS),
+// Chunk weights held lane-strided: lane l holds chunks l + 64*t (t < R),
 // zero past C. Picks the first chunk (row order) whose inclusive prefix exceeds
 // u * total.
 struct ChunkPick {
@@ -593,34 +621,34 @@ struct ChunkPick {
   bool fallback;  // rounding left no crossing: c is the last chunk of positive weight
 };
 
-__device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&wl)[MAX_ROUNDS]) {
+template <int R = MAX_ROUNDS>
+__device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&wl)[R]) {
   const int lane = lane_id();
   ChunkPick r;
   r.c = -1;
   r.before = 0.0;
   r.theta = 0.0;
   r.fallback = false;
-  double tr[MAX_ROUNDS];
+  // the rounds' totals are formed twice (the same sums in the same order) rather
+  // than held, to keep the registers of large R down
   double tot = 0.0;
 #pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
-    tr[t] = (t * WAVE < C) ? wave_sum(wl[t]) : 0.0;
-    tot += tr[t];
-  }
+  for (int t = 0; t < R; ++t) tot += (t * WAVE < C) ? wave_sum(wl[t]) : 0.0;
   if (!(tot > 0.0) || !__builtin_isfinite(tot)) return r;
   const double theta = u * tot;
   r.theta = theta;
   double off = 0.0, offt = 0.0;
   int ht = -1;
 #pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
-    if (ht < 0 && off + tr[t] > theta) { ht = t; offt = off; }
-    off += tr[t];
+  for (int t = 0; t < R; ++t) {
+    const double tr = (t * WAVE < C) ? wave_sum(wl[t]) : 0.0;
+    if (ht < 0 && off + tr > theta) { ht = t; offt = off; }
+    off += tr;
   }
   if (ht >= 0) {
     double wt = wl[0];
 #pragma unroll
-    for (int t = 1; t < MAX_ROUNDS; ++t) if (t == ht) wt = wl[t];
+    for (int t = 1; t < R; ++t) if (t == ht) wt = wl[t];
     const double incl = wave_incl_scan(wt);
     const unsigned long long hit = __ballot(offt + incl > theta && ht * WAVE + lane < C);
     if (hit) {
@@ -632,7 +660,7 @@ __device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&
   }
   int last = -1;
 #pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t)
+  for (int t = 0; t < R; ++t)
     if (t * WAVE + lane < C && wl[t] > 0.0) last = t * WAVE + lane;
   r.c = wave_max_int(last);
   r.fallback = true;
