@@ -369,6 +369,9 @@ __device__ __forceinline__ Partial chunk_reduce(const Chunk& k, Raw r, float c0,
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < CU; ++j) {
+      // one unit decoded at a time: the compiler would otherwise decode
+      // them all ahead of the exponentials and hold the floats
+      if (j > 0) decode_barrier<DT>(r);
       float w[W];
       unit_values<DT>(r, j, w);
 #pragma unroll
