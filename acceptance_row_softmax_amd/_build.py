@@ -14,6 +14,7 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # packed fp32 instructions stay off
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wshadow",
 ]
 
 

@@ -65,10 +65,12 @@ constexpr double LN2 = 0.69314718055994530941723212145818;
 
 // What the residual waves of a sequence need. kind 0: no draft rejected (the bonus
 // token is final); 1: draw from the residual of rows t_L, d_L; 2: a draft was
-// rejected but its rows are unusable (data error, no draw).
+// rejected but its rows are unusable (data error, no draw). b is the sequence (the
+// residual waves of a queued launch learn it from here).
 struct Decision {
-  int L;
-  int kind;
+  int16_t L;
+  int16_t kind;
+  int32_t b;
   float Mt, Md;
   double Zt, Zd;
 };
@@ -185,7 +187,7 @@ struct LinearParams {
   uint64_t* seg;        // [RQ][C][RW] chunk records
   uint64_t* pst;        // [B][k]   PairStat records (stochastic)
   uint64_t* rks;        // [B]      RowStat records of target rows k (stochastic)
-  uint64_t* dec;        // [B][CG]  Decision records, one copy per residual wave
+  uint64_t* dec;        // [B][CG]  Decision records, one copy per residual wave (queued: [slot][CG])
   uint64_t* res;        // [B][CG]  ResPart records
   uint64_t* verd;       // [B][CG]  Verdict records (hold mode)
   uint64_t* tok;        // [B]      Token records
@@ -195,12 +197,14 @@ struct LinearParams {
   uint32_t* fin;        // [B]      events per sequence (stochastic)
   uint32_t* res_cnt;    // [B]      residual waves done per sequence
   uint32_t* errw;       // [B]      error bits per sequence
+  uint64_t* slots;      // [1]      queued: decisions placed so far, rejections (low half) and acceptances (high half)
   int64_t B, k, V;
   int C;                // chunks per row
   int CG;               // residual waves per sequence: RH per chunk
   int RW;               // words per chunk record
   int EV;               // events per sequence (stochastic): k pair combines, target row k, the final token
   bool hold;            // residual waves keep their chunk until the draw is placed (see linear_residual_wave)
+  bool queue;           // residual waves serve decision slots, not sequences (see publish_decision)
   float c0;
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
@@ -565,22 +569,43 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
   emit_store<DT, false>(P, b, in, y);
 }
 
+// Queued launches (more residual waves than can wait on the GPU at once) place
+// each decision in a slot, in the order the decisions are made: a rejection takes
+// the next slot from the front, a sequence with every draft accepted the next one
+// from the back. Their residual waves come last in the launch, in slot order, so
+// the waves of rejecting sequences start first and the back slots' waves, which
+// have nothing to draw, start last. Lane 0 takes the slot; publish_decision turns
+// the value returned into the slot.
+__device__ __forceinline__ uint64_t take_slot(const LinearParams& P, bool accepted) {
+  return __hip_atomic_fetch_add(P.slots, accepted ? (1ull << 32) : 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The decision of sequence b, written once for each of its residual waves (each
 // polls a copy of its own: one line polled by every residual wave of a sequence
-// serialises the polls). d must be the same in every lane.
-__device__ __forceinline__ void publish_decision(const LinearParams& P, int64_t b, const Decision& d) {
+// serialises the polls) at the sequence's own place, or at its slot in a queued
+// launch (`taken`: lane 0's take_slot value). d must be the same in every lane.
+__device__ __forceinline__ void publish_decision(const LinearParams& P, int64_t b, Decision d, uint64_t taken) {
+  const int lane = lane_id();
+  int64_t slot = b;
+  if (P.queue) {
+    taken = bcast(taken);
+    const int64_t nf = (int64_t)(uint32_t)taken, nb = (int64_t)(taken >> 32);
+    if (nf + nb >= P.B) return;   // more decisions than sequences: cannot happen, each is decided once
+    if (lane == 0 && nf + nb + 1 == P.B) counter_reset(P.slots);   // the last slot: zero for the next call
+    slot = d.kind == 0 ? P.B - 1 - nb : nf;
+  }
+  d.b = (int32_t)b;
   uint32_t w[DEC_WORDS];
   __builtin_memcpy(w, &d, sizeof(Decision));
-  const int lane = lane_id();
+  uint64_t* dst = P.dec + slot * P.CG * DEC_WORDS;   // CG copies of DEC_WORDS words
   const int n = P.CG * DEC_WORDS;
   for (int e0 = 0; e0 < n; e0 += WAVE) {
     const int e = e0 + lane;
-    const int j = e % DEC_WORDS;
+    const int word = e % DEC_WORDS;
     uint32_t v = 0;
 #pragma unroll
-    for (int i = 0; i < DEC_WORDS; ++i) if (j == i) v = w[i];
-    if (e < n) __hip_atomic_store(P.dec + b * P.CG * DEC_WORDS + e, ((uint64_t)P.tag << 32) | v, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < DEC_WORDS; ++i) if (word == i) v = w[i];
+    if (e < n) __hip_atomic_store(dst + e, ((uint64_t)P.tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -610,13 +635,15 @@ __device__ __forceinline__ bool linear_settle(const LinearParams& P, int64_t b, 
         ps.okd = bcast(ps.okd);
       }
       Decision d;
-      d.L = Ln;
+      d.L = (int16_t)Ln;
       d.kind = (got && ps.okt && ps.okd) ? 1 : 2;
       d.Mt = ps.Mt;
       d.Md = ps.Md;
       d.Zt = ps.Zt;
       d.Zd = ps.Zd;
-      publish_decision(P, b, d);
+      uint64_t taken = 0;
+      if (P.queue && lane_id() == 0) taken = take_slot(P, false);
+      publish_decision(P, b, d, taken);
     }
     return false;   // the residual waves draw the token
   }
@@ -681,27 +708,28 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
   ps.okd = okd;
   se = bcast(se);
   const uint64_t before = (1ull << i) - 1;
+  // if so, this wave's state update is the one that settles L = i (see linear_settle)
   const bool early = !acc && (se & before) == before && ((se >> 32) & before) == 0;
-  if (early) {
-    // this wave's state update is the one that settles L = i (see linear_settle)
-    Decision d;
-    d.L = (int)i;
-    d.kind = (okt && okd) ? 1 : 2;
-    d.Mt = ps.Mt;
-    d.Md = ps.Md;
-    d.Zt = ps.Zt;
-    d.Zd = ps.Zd;
-    publish_decision(P, b, d);
-  }
+  Decision de;
+  de.L = (int16_t)i;
+  de.kind = (okt && okd) ? 1 : 2;
+  de.Mt = ps.Mt;
+  de.Md = ps.Md;
+  de.Zt = ps.Zt;
+  de.Zd = ps.Zd;
+  if (early && !P.queue) publish_decision(P, b, de, 0);
   // The state update first: an atomic whose result the wave waits for also waits
   // for every store the wave issued before it, and the records below are read by
-  // polling, so they may land later.
-  uint64_t olds = 0;
+  // polling, so they may land later. A queued launch's early decision needs its
+  // slot first; that round trip overlaps the state update's.
+  uint64_t olds = 0, taken = 0;
   if (lane == 0) {
     if (!got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
     else if (!okt || !okd) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_ROW);
     olds = state_or(P.state + b * SSTRIDE, bits);
+    if (early && P.queue) taken = take_slot(P, false);
   }
+  if (early && P.queue) publish_decision(P, b, de, taken);
   Probs pr;
   pr.pt = (float)pt;
   pr.pd = (float)pd;
@@ -715,11 +743,13 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
     const uint64_t mk = (1ull << k) - 1, now = olds | bits;
     if ((now & mk) == mk && ((now >> 32) & mk) == 0 && (olds & mk) != mk) {
       Decision d;
-      d.L = (int)k;
+      d.L = (int16_t)k;
       d.kind = 0;
       d.Mt = d.Md = 0.0f;
       d.Zt = d.Zd = 0.0;
-      publish_decision(P, b, d);
+      uint64_t tk = 0;
+      if (P.queue && lane == 0) tk = take_slot(P, true);
+      publish_decision(P, b, d, tk);
     }
   }
   Ev ev{b, 1u, false, 0};
@@ -797,9 +827,9 @@ __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_
 }
 
 // Residual wave (b, g), dispatched after the streaming waves of every row a
-// decision depends on: waits for the decision of sequence b; if a draft was
-// rejected, sums the residual max(0, p_t,L - p_d,L) over chunk g of rows t_L,
-// d_L. The sequence's last residual wave to count picks the chunk that holds u*S.
+// decision depends on: waits for the decision of sequence b (in a queued launch:
+// the decision in slot b, which names its sequence); if a draft was rejected, sums
+// the residual max(0, p_t,L - p_d,L) over part g of rows t_L, d_L. The sequence's last residual wave to count picks the chunk that holds u*S.
 // Without hold mode it reloads that chunk and scans it. In hold mode (a launch
 // whose residual waves can all be resident at once, so that none waits for a
 // wave that cannot start) every residual wave keeps its chunk and its unit sums
@@ -813,11 +843,17 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   Decision d;
   d.L = 0;
   d.kind = 2;
+  d.b = (int32_t)b;
   d.Mt = d.Md = 0.0f;
   d.Zt = d.Zd = 0.0;
   uint64_t* dr = P.dec + (b * P.CG + g) * DEC_WORDS;   // this wave's copy of the decision
   if (!poll_rec(dr, d, P.tag)) d.kind = 3;   // 3: the decision never arrived
   if (lane == 0) clear_rec<Decision>(dr);
+  if (P.queue) {
+    // the slot's sequence; a slot whose decision never arrived names none
+    if (d.kind == 3 || d.b < 0 || d.b >= P.B) return Ev{0, 0u, false, 0};
+    b = d.b;
+  }
   const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);
@@ -988,16 +1024,18 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
 // finishing wave per sequence. Stochastic: for each position i < k and each
 // sequence, the chunk waves of its target and draft rows (chunk by chunk,
 // alternating) and the wave that finishes the pair; then for each sequence the
-// chunk waves of its target row k, the wave that finishes that row, and its
-// residual waves (one per chunk). Every wave that waits follows the waves it waits
-// for. Each finishing wave comes right after its own rows, so that decisions are
-// made while later rows still stream, and a sequence's residual waves come after
-// all of its pairs: most of them find their decision made and either draw at once
-// (overlapping the remaining stream) or, if nothing was rejected, end at once.
+// chunk waves of its target row k, the wave that finishes that row, and (hold
+// mode) its residual waves, RH per chunk. A queued launch has its residual waves
+// last instead, in slot order (see take_slot). Every wave that waits follows the
+// waves it waits for. Each finishing wave comes right after its own rows, so that
+// decisions are made while later rows still stream, and residual waves come after
+// all pairs of their sequence: most of them find their decision made and either
+// draw at once (overlapping the remaining stream) or, if nothing was rejected, end
+// at once.
 enum RoleKind { ROLE_IDLE = 0, ROLE_STREAM, ROLE_RESID, ROLE_PAIR, ROLE_ROWK, ROLE_GREEDY };
 struct Role {
   int kind;
-  uint32_t q, b, c;   // stream: row q, chunk c; residual: sequence b, group c; finishers: sequence b, position c
+  uint32_t q, b, c;   // stream: row q, chunk c; residual: sequence (queued: slot) b, part c; finishers: sequence b, position c
 };
 
 template <bool STOCH>
@@ -1032,20 +1070,29 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
         r.kind = ROLE_PAIR;
       }
     } else {
-      // sequence blocks: C chunk waves of target row k, its finisher, CG residual waves
-      const uint32_t CG = P.k > 0 ? (uint32_t)P.CG : 0u;
-      const uint32_t Q = NS + 1 + CG;
+      // sequence blocks: C chunk waves of target row k, its finisher and (hold
+      // mode) CG residual waves; a queued launch's residual waves after them
+      const uint32_t CG = (uint32_t)P.CG;
+      const uint32_t CGb = (P.k > 0 && !P.queue) ? CG : 0u;
+      const uint32_t Q = NS + 1 + CGb;
       const uint32_t v = w - P.tk0;
-      r.b = v / Q;
-      const uint32_t e = v - r.b * Q;
-      if (e < NS) {
-        r.q = (uint32_t)(2 * P.k) * B + r.b;
-        r.c = e;
-        r.kind = ROLE_STREAM;
-      } else if (e == NS) {
-        r.kind = ROLE_ROWK;
+      if (v < B * Q) {
+        r.b = v / Q;
+        const uint32_t e = v - r.b * Q;
+        if (e < NS) {
+          r.q = (uint32_t)(2 * P.k) * B + r.b;
+          r.c = e;
+          r.kind = ROLE_STREAM;
+        } else if (e == NS) {
+          r.kind = ROLE_ROWK;
+        } else {
+          r.c = e - NS - 1;
+          r.kind = ROLE_RESID;
+        }
       } else {
-        r.c = e - NS - 1;
+        const uint32_t x = v - B * Q;   // queued: slot x / CG, part x mod CG
+        r.b = x / CG;
+        r.c = x - r.b * CG;
         r.kind = ROLE_RESID;
       }
     }
@@ -1873,7 +1920,7 @@ Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode)
                       (size_t)(B * s.C * RH) * DEC_WORDS * 8, (size_t)(B * s.C * RH) * RES_WORDS * 8, (size_t)B * 8,
                       (size_t)(s.groups * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
                       (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8,
-                      (size_t)(B * s.C * RH) * VERD_WORDS * 8});
+                      (size_t)(B * s.C * RH) * VERD_WORDS * 8, (size_t)8});
 }
 
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
@@ -2018,6 +2065,7 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.state = reinterpret_cast<uint64_t*>(ws + lay.off[7]);
   P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
   P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
+  P.slots = reinterpret_cast<uint64_t*>(ws + lay.off[13]);
   P.errw = reinterpret_cast<uint32_t*>(ws + lay.off[10]);
   P.prob = reinterpret_cast<uint64_t*>(ws + lay.off[11]);
   P.verd = reinterpret_cast<uint64_t*>(ws + lay.off[12]);
@@ -2028,10 +2076,11 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.RW = (int)sh.RW;
   P.EV = (int)(k + 2);
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  // residual waves: one per chunk (they come after every streaming wave); hold mode
-  // when all of them fit on the GPU at once, with room to spare
+  // residual waves: RH per chunk (they come after every streaming wave); hold mode
+  // when all of them fit on the GPU at once, with room to spare, else queued
   P.CG = RH * P.C;
   P.hold = stoch && k > 0 && B * P.CG <= stochastic_wave_capacity(dtype) / 2;
+  P.queue = stoch && k > 0 && !P.hold;
   // see linear_role for the order of the waves
   if (!stoch) {
     P.n_waves = sh.RQ * sh.C + B;

@@ -342,15 +342,15 @@ __device__ __forceinline__ Partial chunk_reduce(const Chunk& k, Raw r, float c0,
   int pos = INT_SENTINEL;
 #pragma unroll
   for (int j = 0; j < CU; ++j) {
-    float x[W];
-    unit_values<DT>(r, j, x);
+    float v[W];
+    unit_values<DT>(r, j, v);
     if constexpr (ARG) {
       const int base = (int)((k.u0 + j * WAVE + lane_id()) * W);
 #pragma unroll
       for (int e = 0; e < W; ++e)
-        if (x[e] > best) { best = x[e]; pos = base + e; }
+        if (v[e] > best) { best = v[e]; pos = base + e; }
     } else {
-      best = fmaxf(best, max_of<W>(x));
+      best = fmaxf(best, max_of<W>(v));
     }
   }
   Partial p;

@@ -76,7 +76,10 @@
  *                          not run the launch's workgroups in dispatch order, or a
  *                          concurrent call shared the workspace); outputs are not
  *                          valid, and a wait that gave up can also leave other
- *                          sequences of that launch unwritten
+ *                          sequences of that launch unwritten (in a stochastic
+ *                          linear launch of many sequences, possibly with no bit
+ *                          set anywhere: a caller that must detect this fills
+ *                          accept_len with a sentinel before the call)
  *      bit4 SV_ERR_CAPACITY  (commit) the history buffer cannot take the new tokens
  *      bit5 SV_ERR_UNVERIFIED (commit) the sequence's verification reported an error
  */

@@ -112,6 +112,15 @@ def test_grouped_residual_waves_odd_chunks():
     assert 0.1 < np.mean(g["accept_len"] == 0) < 0.9
 
 
+def test_queued_launch_with_few_sequences():
+    # 2 MiB fp32 rows have 512 residual waves per sequence, so 8 sequences are more
+    # than the GPU keeps waiting at once: the launch is queued, and its decisions
+    # take slots (six rejections from the front, two full acceptances from the back)
+    w = gen.linear_draft_target(99, 3, 8, 2, 524288, gen.DT_F32, 3.0, 1.0, "stochastic", 0.8, "queued-few")
+    g, o, near, n_eval = _check(w)
+    assert np.sum(o["accept_len"] == 2) == 2 and np.sum(o["accept_len"] < 2) == 6
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_c2_draft_target_full_size(seed):
     w = gen.c2_linear(seed)            # B=32, k=4, V=128256, bf16, T=0.7
@@ -201,13 +210,14 @@ def test_workspace_left_zero_and_shared_across_shapes():
     wa = gen.c2_linear(9, B=16)
     wb = gen.linear_draft_target(71, 1, 7, 3, 20000, gen.DT_F16, 2.0, 0.5, "greedy", 1.0, "ws-b")
     wc = gen.linear_draft_target(72, 2, 5, 0, 3000, gen.DT_F32, 2.0, 0.5, "stochastic", 1.3, "ws-c")
+    wd = gen.c1_tiny(5, "stochastic", B=4000)   # a queued launch (decision slots)
     L = sv.lib()
     # the generator's dtype codes are the library's
     need = max(L.spec_verify_linear_workspace(w.B, w.k, w.V, w.dtype,
                                               sv.SV_STOCHASTIC if w.mode == "stochastic" else sv.SV_GREEDY)
-               for w in (wa, wb, wc))
+               for w in (wa, wb, wc, wd))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    for w in (wa, wb, wc, wa):
+    for w in (wa, wb, wc, wd, wa, wd):
         t = G.to_dev(w.target, w.dtype)
         d = G.to_dev(w.draft, w.dtype) if (w.mode == "stochastic" and w.k > 0) else None
         x = G.to_dev(w.draft_tokens) if w.k > 0 else None
