@@ -954,12 +954,8 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     // rounding) it is taken from p_t,L instead: the same pick and scan with the
     // draft's weights zeroed (and taken from row t_L, so that they stay finite),
     // over chunk sums formed here.
-    double tot = 0.0;
-#pragma unroll
-    for (int t = 0; t < RR; ++t) tot += wl[t];
-    tot = wave_sum(tot);
     pk = pick_chunk((int)CG, (double)u, wl);
-    if (pk.c < 0 && tot == 0.0) {
+    if (pk.c < 0 && pk.total == 0.0) {
       zero = true;
       rx.mc0d = rx.mc0t;
       rx.izd = 0.0f;

@@ -621,6 +621,7 @@ struct ChunkPick {
   int c;          // chosen chunk; -1 if the total is not a positive finite number
   double before;  // sum of the weights of the chunks before c
   double theta;   // u * total
+  double total;   // the weights' sum
   bool fallback;  // rounding left no crossing: c is the last chunk of positive weight
 };
 
@@ -631,12 +632,34 @@ __device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&
   r.c = -1;
   r.before = 0.0;
   r.theta = 0.0;
+  r.total = 0.0;
   r.fallback = false;
+  if (C <= WAVE) {
+    // one round: the inclusive scan gives the total (its last lane) and the crossing
+    const double w0 = lane < C ? wl[0] : 0.0;
+    const double incl = wave_incl_scan(w0);
+    const double tot = readlane_d(incl, WAVE - 1);
+    r.total = tot;
+    if (!(tot > 0.0) || !__builtin_isfinite(tot)) return r;
+    const double theta = u * tot;
+    r.theta = theta;
+    const unsigned long long hit = __ballot(incl > theta && lane < C);
+    if (hit) {
+      const int l = first_lane(hit);
+      r.c = l;
+      r.before = __shfl(incl, l) - __shfl(w0, l);
+      return r;
+    }
+    r.c = wave_max_int(lane < C && w0 > 0.0 ? lane : -1);
+    r.fallback = true;
+    return r;
+  }
   // the rounds' totals are formed twice (the same sums in the same order) rather
   // than held, to keep the registers of large R down
   double tot = 0.0;
 #pragma unroll
   for (int t = 0; t < R; ++t) tot += (t * WAVE < C) ? wave_sum(wl[t]) : 0.0;
+  r.total = tot;
   if (!(tot > 0.0) || !__builtin_isfinite(tot)) return r;
   const double theta = u * tot;
   r.theta = theta;
