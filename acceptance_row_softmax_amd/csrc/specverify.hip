@@ -463,13 +463,16 @@ __device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b, in
 
 // Events a wave counts when it is done: n of sequence b (n = 0: none), the final
 // token among them if `token`. Every role returns its events to the kernel body,
-// which counts them at one place.
+// which counts them at one place. An event that set error bits of its sequence
+// adds EV_ERR as well, so the count also tells the last event whether the error
+// word needs reading.
 struct Ev {
   int64_t b;
   uint32_t n;
   bool token;
   int y;
 };
+constexpr uint32_t EV_ERR = 1u << 16, EV_COUNT = EV_ERR - 1u;
 
 // Counts n events of sequence b (k pair combines, target row k and the final
 // token); the last one writes the outputs. The token event carries the token: if
@@ -481,7 +484,7 @@ __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, b
   uint32_t old = 0;
   if (lane_id() == 0) old = counter_add(P.fin + b * CSTRIDE, n);
   old = bcast(old);
-  if (old + n != total) {
+  if ((old & EV_COUNT) + (n & EV_COUNT) != total) {
     if (token && lane_id() == 0) {
       Token t;
       t.y = y;
@@ -491,6 +494,69 @@ __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, b
   }
   if (lane_id() == 0) counter_reset(P.fin + b * CSTRIDE);
   linear_emit<DT, STOCH>(P, b, token ? y : TOKEN_UNKNOWN);
+}
+
+// The emission's reads that do not depend on the sequence's other events, issued
+// by a wave that draws the final token together with its event's count, before its
+// draw, so that their round trip overlaps the draw: the drafts, and one read of
+// each position's probability record (polled for again if it was not there yet).
+struct EmitPre {
+  int x;
+  uint64_t w[PROB_WORDS];
+};
+__device__ __forceinline__ EmitPre emit_prefetch(const LinearParams& P, int64_t b) {
+  const int lane = lane_id();
+  EmitPre e;
+  e.x = 0;
+#pragma unroll
+  for (int i = 0; i < PROB_WORDS; ++i) e.w[i] = 0;
+  if (lane < P.k) {
+    e.x = P.tokens[b * P.k + lane];
+#pragma unroll
+    for (int i = 0; i < PROB_WORDS; ++i)
+      e.w[i] = __hip_atomic_load(P.prob + (b * P.k + lane) * PROB_WORDS + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return e;
+}
+
+// The emission of sequence b by the wave that drew its final token y after the
+// rejection at L (the decision's), once its event count `fo` (the value before its
+// own) shows it is the last event: L needs no read of the state word, and the error
+// word is read only if an earlier event set error bits.
+template <int DT>
+__device__ __forceinline__ void emit_drawn(const LinearParams& P, int64_t b, int L, int y, const EmitPre& pre,
+                                           uint32_t fo) {
+  const int lane = lane_id();
+  const int64_t k = P.k;
+  EmitIn in;
+  in.s = 1ull << (32 + L);   // L < k: the rejected position
+  in.ew = 0;
+  if (lane == 1 && (fo & ~EV_COUNT) != 0u)
+    in.ew = __hip_atomic_load(P.errw + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  in.t.y = y;
+  in.tg = true;
+  in.pg = true;
+  in.x = pre.x;
+  in.pr.pt = in.pr.pd = NAN;
+  if (lane < k) {
+    uint64_t* pr = P.prob + (b * k + lane) * PROB_WORDS;
+    bool here = true;
+    uint32_t w[PROB_WORDS];
+#pragma unroll
+    for (int i = 0; i < PROB_WORDS; ++i) {
+      here = here && (uint32_t)(pre.w[i] >> 32) == P.tag;
+      w[i] = (uint32_t)pre.w[i];
+    }
+    if (here) __builtin_memcpy(&in.pr, w, sizeof(Probs));
+    else in.pg = get_rec(pr, in.pr, P.tag);
+    clear_rec<Probs>(pr);
+    clear_rec<PairStat>(P.pst + (b * k + lane) * PST_WORDS);
+  }
+  // leave the sequence's words and records zero for the next call
+  if (lane == 0) counter_reset(P.state + b * SSTRIDE);
+  if (lane == 1) counter_reset(P.errw + b * CSTRIDE);
+  if (lane == 3) clear_rec<RowStat>(P.rks + b * ROW_WORDS);
+  emit_store<DT, true>(P, b, in, y);
 }
 
 // Greedy finish of sequence b: polls the chunk records of its k+1 target rows
@@ -752,10 +818,11 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
       publish_decision(P, b, d, tk);
     }
   }
-  Ev ev{b, 1u, false, 0};
+  const uint32_t ef = (!got || !okt || !okd) ? EV_ERR : 0u;   // it set error bits
+  Ev ev{b, 1u | ef, false, 0};
   if (linear_settle<DT>(P, b, olds, olds | bits, i, ps, early, ev.y)) {
     ev.token = true;   // and the final token
-    ev.n = 2;
+    ev.n = 2u | ef;
   }
   return ev;
 }
@@ -793,8 +860,9 @@ __device__ __forceinline__ Ev rowk_finish(const LinearParams& P, int64_t b) {
   put_rec_wave(P.rks + b * ROW_WORDS, st, P.tag);
   olds = bcast(olds);
   const int Ln = settled_L(olds | BONUS_BIT, (int)k);
-  if (Ln == (int)k && settled_L(olds, (int)k) < 0) return Ev{b, 2u, true, st.y};   // the bonus token is final
-  return Ev{b, 1u, false, 0};
+  const uint32_t ef = st.ok != 1 ? EV_ERR : 0u;   // it set error bits
+  if (Ln == (int)k && settled_L(olds, (int)k) < 0) return Ev{b, 2u | ef, true, st.y};   // the bonus token is final
+  return Ev{b, 1u | ef, false, 0};
 }
 
 // Streaming wave of chunk c of row q: the chunk's partial goes out as its record,
@@ -889,9 +957,11 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     const bool got = poll_rec(vr, v, P.tag);
     if (lane == 0) clear_rec<Verdict>(vr);
     if (!got || v.kind == 0) return Ev{0, 0u, false, 0};
-    // the token event is counted before the scan, so that its round trip overlaps it
+    // the token event is counted before the scan, and the emission's reads issued,
+    // so that their round trips overlap it
     uint32_t fo = 0;
     if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
+    const EmitPre pre = emit_prefetch(P, b);
     ResidW rx = rw;
     int yh;
     if (v.kind == 2) {
@@ -903,9 +973,10 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     } else {
       yh = (int)chunk_invcdf_us<DT, true>(kg, rt, rd, us, v.th, rx);
     }
-    if (bcast(fo) + 1 == (uint32_t)P.EV) {
+    fo = bcast(fo);
+    if ((fo & EV_COUNT) + 1 == (uint32_t)P.EV) {
       if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-      linear_emit<DT, true>(P, b, yh);
+      emit_drawn<DT>(P, b, d.L, yh, pre, fo);
     } else if (lane == 0) {
       Token t;
       t.y = yh;
@@ -917,12 +988,16 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind != 1) return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
-  // Without hold mode the token event's count goes out with the reads of the
-  // residual sums; after the pick the chosen part is reloaded and scanned, and if
-  // the count says this is the sequence's last event the wave writes the outputs.
-  // Otherwise the last event's wave waits for the token record.
+  // Without hold mode the token event's count and the emission's reads go out with
+  // the reads of the residual sums; after the pick the chosen part is reloaded and
+  // scanned, and if the count says this is the sequence's last event the wave
+  // writes the outputs. Otherwise the last event's wave waits for the token record.
   uint32_t fo = 0;
-  if (!P.hold && lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
+  EmitPre pre{};
+  if (!P.hold) {
+    if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
+    pre = emit_prefetch(P, b);
+  }
   constexpr int RR = RH * MAX_ROUNDS;   // rounds of 64 parts
   double wl[RR];
   bool ok = true;
@@ -940,7 +1015,8 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
       clear_rec<ResPart>(rec);
     }
   }
-  const bool last = !P.hold && bcast(fo) + 1 == (uint32_t)P.EV;
+  fo = bcast(fo);
+  const bool last = !P.hold && (fo & EV_COUNT) + 1 == (uint32_t)P.EV;
   ChunkPick pk;
   pk.c = -1;
   ResidW rx = rw;
@@ -1000,13 +1076,11 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     kg = load_units<DT, HU>(trow, P.V, pu, rt);
     load_units<DT, HU>(dx, P.V, pu, rd);
   }
-  // (the emission's reads follow the scan: issued before it, they would hold their
-  // registers through it, and those registers set the launch's occupancy)
   if (pk.c >= 0) y = (int)chunk_invcdf<DT, true>(kg, rt, rd, th, rx);
   if (P.hold) return Ev{b, 1u, true, y};
   if (last) {
     if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-    linear_emit<DT, true>(P, b, y);
+    emit_drawn<DT>(P, b, d.L, y, pre, fo);
   } else if (lane == 0) {
     Token t;
     t.y = y;
@@ -1097,7 +1171,9 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
 }
 
 template <int DT, bool STOCH>
-__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(3))) void linear_kernel(LinearParams P) {
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(3))) void linear_kernel(LinearParams args) {
+  (void)args;
+  const LinearParams& P = kernel_args<LinearParams>();
   const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
   if (w >= P.n_waves) return;
   const Role r = linear_role<STOCH>(P, (uint32_t)w);
@@ -1633,7 +1709,9 @@ enum WalkMode { WM_KNOWN = 0, WM_LAZY = 1, WM_TYPICAL = 2 };
 // the token of each accepted node and accepting the children whose candidate
 // equals it.
 template <int DT, int WM, int NT>
-__global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams P) {
+__global__ __launch_bounds__(NT) void tree_walk_kernel(TreeParams args) {
+  (void)args;
+  const TreeParams& P = kernel_args<TreeParams>();
   constexpr int E = DTraits<DT>::E;
   constexpr bool DRAWS = WM != WM_KNOWN;
   extern __shared__ unsigned char smem[];

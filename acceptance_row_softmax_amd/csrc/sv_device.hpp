@@ -693,6 +693,17 @@ __device__ __forceinline__ ChunkPick pick_chunk(int C, double u, const double (&
   return r;
 }
 
+// ------------------------------------------------------------------ kernel parameters
+// A kernel's by-value parameter struct, read in place in the kernel-argument
+// segment (the constant address space), field by field where the code uses it.
+// Named as a kernel parameter, every field the kernel uses is loaded into scalar
+// registers on entry and kept live through every branch, which in kernels of many
+// roles spills scalar registers to vector lanes on every wave's path.
+template <class T>
+__device__ __forceinline__ const T& kernel_args() {
+  return *(const T*)(const __attribute__((address_space(4))) T*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 // ------------------------------------------------------------------ cross-wave records
 // Waves hand data to each other inside one launch without fences: a record is an
 // array of 8-byte words, each holding a 32-bit value and the 32-bit tag of the
