@@ -147,10 +147,12 @@ __device__ __forceinline__ double residual_raw_sum(const RawN<NU>& rt, const Raw
 
 // The last residual wave's verdict on one chunk, for the wave holding it (hold
 // mode): kind 0 not picked, 1 picked (draw from the residual), 2 picked with no
-// residual mass (draw from p_t,L); th the threshold inside the chunk.
+// residual mass (draw from p_t,L); th the threshold inside the chunk; fo the
+// sequence's event count before the token event, which the last residual wave
+// counted on the drawing wave's behalf.
 struct Verdict {
   int kind;
-  int pad;
+  uint32_t fo;
   double th;
 };
 constexpr int VERD_WORDS = RecWords<Verdict>::N;   // 4
@@ -522,7 +524,8 @@ __device__ __forceinline__ EmitPre emit_prefetch(const LinearParams& P, int64_t 
 // The emission of sequence b by the wave that drew its final token y after the
 // rejection at L (the decision's), once its event count `fo` (the value before its
 // own) shows it is the last event: L needs no read of the state word, and the error
-// word is read only if an earlier event set error bits.
+// word is read only if an earlier event set error bits. `pre` must come from
+// emit_prefetch (its drafts are used as they are).
 template <int DT>
 __device__ __forceinline__ void emit_drawn(const LinearParams& P, int64_t b, int L, int y, const EmitPre& pre,
                                            uint32_t fo) {
@@ -953,15 +956,17 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     uint64_t* vr = P.verd + (b * P.CG + g) * VERD_WORDS;
     Verdict v;
     v.kind = 0;
+    v.fo = 0;
     v.th = 0.0;
     const bool got = poll_rec(vr, v, P.tag);
     if (lane == 0) clear_rec<Verdict>(vr);
     if (!got || v.kind == 0) return Ev{0, 0u, false, 0};
-    // the token event is counted before the scan, and the emission's reads issued,
-    // so that their round trips overlap it
-    uint32_t fo = 0;
-    if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
-    const EmitPre pre = emit_prefetch(P, b);
+    // the token event is already counted (by the last residual wave); if it was the
+    // sequence's last event, the emission's reads go out before the scan, so that
+    // their round trip overlaps it
+    const bool last = (v.fo & EV_COUNT) + 1 == (uint32_t)P.EV;
+    EmitPre pre{};
+    if (last) pre = emit_prefetch(P, b);
     ResidW rx = rw;
     int yh;
     if (v.kind == 2) {
@@ -973,10 +978,9 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     } else {
       yh = (int)chunk_invcdf_us<DT, true>(kg, rt, rd, us, v.th, rx);
     }
-    fo = bcast(fo);
-    if ((fo & EV_COUNT) + 1 == (uint32_t)P.EV) {
+    if (last) {
       if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-      emit_drawn<DT>(P, b, d.L, yh, pre, fo);
+      emit_drawn<DT>(P, b, d.L, yh, pre, v.fo);
     } else if (lane == 0) {
       Token t;
       t.y = yh;
@@ -988,16 +992,14 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind != 1) return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
-  // Without hold mode the token event's count and the emission's reads go out with
-  // the reads of the residual sums; after the pick the chosen part is reloaded and
-  // scanned, and if the count says this is the sequence's last event the wave
-  // writes the outputs. Otherwise the last event's wave waits for the token record.
+  // The token event's count and the emission's reads go out with the reads of the
+  // residual sums (in hold mode the count is taken on behalf of the wave that will
+  // draw, which learns it from its verdict). Whichever wave draws writes the
+  // outputs if the count says the token was the sequence's last event; otherwise
+  // the last event's wave waits for the token record.
   uint32_t fo = 0;
-  EmitPre pre{};
-  if (!P.hold) {
-    if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
-    pre = emit_prefetch(P, b);
-  }
+  if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
+  const EmitPre pre = emit_prefetch(P, b);
   constexpr int RR = RH * MAX_ROUNDS;   // rounds of 64 parts
   double wl[RR];
   bool ok = true;
@@ -1016,7 +1018,7 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     }
   }
   fo = bcast(fo);
-  const bool last = !P.hold && (fo & EV_COUNT) + 1 == (uint32_t)P.EV;
+  const bool last = (fo & EV_COUNT) + 1 == (uint32_t)P.EV;
   ChunkPick pk;
   pk.c = -1;
   ResidW rx = rw;
@@ -1060,15 +1062,15 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
       if (c < (int)CG && c != g) {
         Verdict v;
         v.kind = c == pc ? (zero ? 2 : 1) : 0;
-        v.pad = 0;
+        v.fo = fo;
         v.th = th;
         put_rec(P.verd + (b * P.CG + c) * VERD_WORDS, v, P.tag);
       }
     }
-    if (pc < 0) return Ev{b, 1u, true, rec_ok ? -1 : -2};   // nothing to draw from
-    if (pc != g) return Ev{0, 0u, false, 0};               // the holder counts the token
-    // the pick is this wave's own chunk, whose registers were not kept: the reload
-    // below serves
+    if (pc >= 0 && pc != g) return Ev{0, 0u, false, 0};   // the holder draws and emits
+    // nothing to draw from (pc < 0: the token is -1, or -2 after a timed-out read),
+    // or the pick is this wave's own chunk, whose registers were not kept: the
+    // reload below serves
   }
   // the picked part, reloaded into this wave's own registers
   if (pk.c >= 0) {
@@ -1077,7 +1079,6 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     load_units<DT, HU>(dx, P.V, pu, rd);
   }
   if (pk.c >= 0) y = (int)chunk_invcdf<DT, true>(kg, rt, rd, th, rx);
-  if (P.hold) return Ev{b, 1u, true, y};
   if (last) {
     if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
     emit_drawn<DT>(P, b, d.L, y, pre, fo);
