@@ -521,18 +521,19 @@ __device__ __forceinline__ EmitPre emit_prefetch(const LinearParams& P, int64_t 
   return e;
 }
 
-// The emission of sequence b by the wave that drew its final token y after the
-// rejection at L (the decision's), once its event count `fo` (the value before its
-// own) shows it is the last event: L needs no read of the state word, and the error
-// word is read only if an earlier event set error bits. `pre` must come from
-// emit_prefetch (its drafts are used as they are).
+// The emission of sequence b by the wave that drew its final token y with L
+// settled (a rejection at L < k, or every draft accepted, L = k), once its event
+// count `fo` (the value before its own, with its own event's EV_ERR) shows it is the
+// last event: L needs no read of the state word, and the error word is read only if
+// an event set error bits. `pre` must come from emit_prefetch (its drafts are used
+// as they are).
 template <int DT>
 __device__ __forceinline__ void emit_drawn(const LinearParams& P, int64_t b, int L, int y, const EmitPre& pre,
                                            uint32_t fo) {
   const int lane = lane_id();
   const int64_t k = P.k;
   EmitIn in;
-  in.s = 1ull << (32 + L);   // L < k: the rejected position
+  in.s = L < k ? 1ull << (32 + L) : 0ull;   // the rejected position, if any
   in.ew = 0;
   if (lane == 1 && (fo & ~EV_COUNT) != 0u)
     in.ew = __hip_atomic_load(P.errw + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -822,12 +823,25 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
     }
   }
   const uint32_t ef = (!got || !okt || !okd) ? EV_ERR : 0u;   // it set error bits
-  Ev ev{b, 1u | ef, false, 0};
-  if (linear_settle<DT>(P, b, olds, olds | bits, i, ps, early, ev.y)) {
-    ev.token = true;   // and the final token
-    ev.n = 2u | ef;
+  int y = 0;
+  if (linear_settle<DT>(P, b, olds, olds | bits, i, ps, early, y)) {
+    // L = k and the bonus token is final: this position's event and the token's,
+    // counted here with the emission's reads alongside
+    uint32_t fo = 0;
+    if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 2u | ef);
+    const EmitPre pre = emit_prefetch(P, b);
+    fo = bcast(fo);
+    if ((fo & EV_COUNT) + 2 == (uint32_t)P.EV) {
+      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+      emit_drawn<DT>(P, b, (int)k, y, pre, fo | ef);
+    } else if (lane == 0) {
+      Token t;
+      t.y = y;
+      put_rec(P.tok + b, t, P.tag);
+    }
+    return Ev{0, 0u, false, 0};
   }
-  return ev;
+  return Ev{b, 1u | ef, false, 0};
 }
 
 // Stochastic, target row k of sequence b (the row after the last draft): combined
@@ -853,18 +867,37 @@ __device__ __forceinline__ Ev rowk_finish(const LinearParams& P, int64_t b) {
   st.y = -1;
   st.ok = !got ? -1 : ((rs.M > -INFINITY && __builtin_isfinite(rs.Z) && rs.Z > 0.0) ? 1 : 0);
   sn = bcast(sn);
-  if (st.ok == 1 && settled_L(sn, (int)k) < 0)
-    st.y = softmax_draw<DT>(row_ptr<DT, true>(P, b, k, 0), V, P.C, P.c0, P.uniforms[b * (k + 1) + k], rp, rs, wl);
+  // The state update goes out before the draw, so that its round trip overlaps it
+  // (a wave that settles L = k from the state word polls for this row's record,
+  // which follows the draw).
   uint64_t olds = 0;
   if (lane == 0) {
     if (st.ok != 1) error_or(P.errw + b * CSTRIDE, (uint32_t)(st.ok < 0 ? SV_ERR_INTERNAL : SV_ERR_ROW));
     olds = state_or(P.state + b * SSTRIDE, BONUS_BIT);   // before the record (see pair_finish)
   }
+  if (st.ok == 1 && settled_L(sn, (int)k) < 0)
+    st.y = softmax_draw<DT>(row_ptr<DT, true>(P, b, k, 0), V, P.C, P.c0, P.uniforms[b * (k + 1) + k], rp, rs, wl);
   put_rec_wave(P.rks + b * ROW_WORDS, st, P.tag);
   olds = bcast(olds);
   const int Ln = settled_L(olds | BONUS_BIT, (int)k);
   const uint32_t ef = st.ok != 1 ? EV_ERR : 0u;   // it set error bits
-  if (Ln == (int)k && settled_L(olds, (int)k) < 0) return Ev{b, 2u | ef, true, st.y};   // the bonus token is final
+  if (Ln == (int)k && settled_L(olds, (int)k) < 0) {
+    // the bonus token is final: this row's event and the token's, counted here,
+    // with the emission's reads alongside
+    uint32_t fo = 0;
+    if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 2u | ef);
+    const EmitPre pre = emit_prefetch(P, b);
+    fo = bcast(fo);
+    if ((fo & EV_COUNT) + 2 == (uint32_t)P.EV) {
+      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+      emit_drawn<DT>(P, b, (int)k, st.y, pre, fo | ef);
+    } else if (lane == 0) {
+      Token t;
+      t.y = st.y;
+      put_rec(P.tok + b, t, P.tag);
+    }
+    return Ev{0, 0u, false, 0};
+  }
   return Ev{b, 1u | ef, false, 0};
 }
 
