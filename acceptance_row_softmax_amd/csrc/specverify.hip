@@ -2024,11 +2024,12 @@ inline LinearShape linear_shape(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv
 
 Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
   const LinearShape s = linear_shape(B, k, V, dt, mode);
+  const size_t RG = mode == SV_STOCHASTIC ? (size_t)(B * s.C * RH) : 0;   // residual waves (stochastic only)
   return make_layout({(size_t)(s.RQ * s.C * s.RW) * 8, (size_t)(B * k) * PST_WORDS * 8, (size_t)B * ROW_WORDS * 8,
-                      (size_t)(B * s.C * RH) * DEC_WORDS * 8, (size_t)(B * s.C * RH) * RES_WORDS * 8, (size_t)B * 8,
+                      RG * DEC_WORDS * 8, RG * RES_WORDS * 8, (size_t)B * 8,
                       (size_t)(s.groups * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
                       (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8,
-                      (size_t)(B * s.C * RH) * VERD_WORDS * 8, (size_t)8});
+                      RG * VERD_WORDS * 8, (size_t)8});
 }
 
 Layout tree_layout(int64_t B, int64_t N, int64_t V, sv_dtype dt) {
