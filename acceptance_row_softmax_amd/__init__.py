@@ -86,6 +86,8 @@ def lib():
                                                 vp, vp]
         L.spec_tree_build_greedy.restype = i64
         L.spec_tree_build_greedy.argtypes = [i64, i64, vp, i64, vp, vp, vp, vp]
+        L.spec_read_probe.restype = i32
+        L.spec_read_probe.argtypes = [vp, sz, vp, sz, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -95,7 +97,7 @@ EXPORTED = ("spec_verify_linear_workspace", "spec_verify_linear", "spec_verify_t
             "spec_workspace_clear", "spec_verify_status_string", "spec_commit_linear",
             "spec_sample_workspace", "spec_sample", "spec_tree_mask", "spec_tree_build_greedy",
             "spec_verify_tree_typical", "spec_verify_linear_commit", "spec_verify_linear_static",
-            "spec_set_wait_limit")
+            "spec_set_wait_limit", "spec_read_probe")
 SV_MAX_STATIC_WORKSPACE = 8 * 1024 * 1024
 
 
@@ -530,6 +532,30 @@ def tree_mask(parent, n_trees: int = 1, *, stream=None):
     st = lib().spec_tree_mask(n_trees, n, _ptr(parent), stride, _ptr(mask), _ptr(ef), _stream(stream))
     _check(st, "spec_tree_mask")
     return {"mask": mask, "err_flags": ef}
+
+
+def read_probe_words(*tensors) -> int:
+    """Sink words spec_read_probe needs for these tensors (one per 8 KiB chunk)."""
+    return sum((t.numel() * t.element_size() + 8191) // 8192 for t in tensors if t is not None)
+
+
+def read_probe(a, b=None, sink=None, stream=None):
+    """spec_read_probe: a plain streaming read of device tensors a and b (b may be
+    None), a measurement aid; returns the sink (each chunk's largest 32-bit word)."""
+    torch = _torch()
+    for t in (a, b):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("read_probe: contiguous device tensors")
+    need = read_probe_words(a, b)
+    if sink is None:
+        with torch.cuda.stream(_torch_stream(stream)):
+            sink = torch.empty(max(need, 1), dtype=torch.int32, device=a.device)
+    elif sink.dtype != torch.int32 or not sink.is_contiguous() or sink.numel() < need:
+        raise ValueError(f"read_probe: sink of at least {need} int32 words")
+    nb = lambda t: 0 if t is None else t.numel() * t.element_size()
+    st = lib().spec_read_probe(_ptr(a), nb(a), _ptr(b), nb(b), _ptr(sink), sink.numel(), _stream(stream))
+    _check(st, "spec_read_probe")
+    return sink
 
 
 def set_wait_limit(seconds: float):

@@ -2006,6 +2006,39 @@ __global__ __launch_bounds__(BLOCK) void clear_kernel(unsigned char* p, size_t b
   for (size_t i = n16 * 16 + (size_t)blockIdx.x * BLOCK + threadIdx.x; i < bytes; i += stride) p[i] = 0;
 }
 
+// A plain streaming read of one or two buffers with nothing else done, to measure
+// what reading the bytes of a verification costs by itself: one wave per 8 KiB
+// chunk (its eight 16-byte loads per lane issued together, as in the streaming
+// waves above), the chunk's largest 32-bit word stored to sink[wave]. Chunks
+// [0, ca) are buffer a's, the rest buffer b's; na, nb count 16-byte units.
+__global__ __launch_bounds__(BLOCK) void read_probe_kernel(const uint4* a, int64_t na, int64_t ca, const uint4* b,
+                                                           int64_t nb, int64_t nwaves, uint32_t* sink) {
+  const int64_t w = (int64_t)blockIdx.x * WPB + wave_in_block();
+  if (w >= nwaves) return;
+  const int lane = lane_id();
+  const bool in_a = w < ca;
+  const uint4* p = in_a ? a : b;
+  const int64_t n = in_a ? na : nb;
+  const int64_t u0 = (in_a ? w : w - ca) * CHUNK_UNITS;
+  uint4 v[CU];
+  if (u0 + CHUNK_UNITS <= n) {
+#pragma unroll
+    for (int j = 0; j < CU; ++j) v[j] = p[u0 + j * WAVE + lane];
+  } else {
+#pragma unroll
+    for (int j = 0; j < CU; ++j) {
+      const int64_t u = u0 + j * WAVE + lane;
+      v[j] = u < n ? p[u] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < CU; ++j) m = max(m, max(max(v[j].x, v[j].y), max(v[j].z, v[j].w)));
+#pragma unroll
+  for (int o = WAVE / 2; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if (lane == 0) sink[w] = m;
+}
+
 // ------------------------------------------------------------------ host side
 struct LinearShape {
   int64_t R, RQ, C, RW, groups;
@@ -2455,6 +2488,22 @@ sv_status spec_set_wait_limit(double seconds) {
   if (!(seconds >= 0.0 && seconds <= 60.0)) return SV_EINVAL;
   const uint64_t ticks = (uint64_t)(seconds * 1e8);
   return hipMemcpyToSymbol(HIP_SYMBOL(g_wait_ticks), &ticks, sizeof(ticks)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status spec_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink,
+                          size_t sink_words, sv_stream_t stream) {
+  if ((a_bytes && !a) || (b_bytes && !b)) return SV_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(a) & 15u) != 0 || (reinterpret_cast<uintptr_t>(b) & 15u) != 0) return SV_EINVAL;
+  const int64_t na = (int64_t)(a_bytes / 16), nb = (int64_t)(b_bytes / 16);
+  const int64_t ca = (na + CHUNK_UNITS - 1) / CHUNK_UNITS, cb = (nb + CHUNK_UNITS - 1) / CHUNK_UNITS;
+  const int64_t nw = ca + cb;
+  if (nw == 0) return SV_OK;
+  // the documented bound: one word per started 8 KiB of each buffer
+  if (!sink || sink_words < (a_bytes + 8191) / 8192 + (b_bytes + 8191) / 8192) return SV_EINVAL;
+  if (nw > MAX_WAVES) return SV_ELIMIT;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks_for(nw)), dim3(BLOCK), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(a), na, ca, static_cast<const uint4*>(b), nb, nw, sink);
+  return launch_status();
 }
 
 sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream) {

@@ -509,6 +509,28 @@ def main():
     dom_us = gpu_ms * 1e3 / K
     dominant = "linear_kernel" if linear else "tree_stream_kernel+tree_walk_kernel"
 
+    # ---------------------------------------------------------------- the same bytes, only read
+    # The same input copies read by spec_read_probe (the streaming waves' load
+    # pattern, no arithmetic, one word written per chunk), K launches timed the same
+    # way: what reading these bytes costs by itself on this GPU.
+    pr_bufs = [((s["t"], s["d"]) if linear else (s["lg"], None)) for s in sets]
+    sink = torch.empty(sv.read_probe_words(*pr_bufs[0]), dtype=torch.int32, device=dev)
+    probe = lambda i: sv.read_probe(*pr_bufs[i], sink=sink)
+    if not args.no_graph:
+        _, _, pr_ms = _graph_time(torch, probe, copies, K, args.warmup)
+    else:
+        for i in range(args.warmup):
+            probe(i % copies)
+        pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        pe0.record(stream)
+        for i in range(K):
+            probe(i % copies)
+        pe1.record(stream)
+        torch.cuda.synchronize()
+        pr_ms = pe0.elapsed_time(pe1) / K
+    plain_us = pr_ms * 1e3
+
     npos = positions(w)
     value = npos / (ms_per_step * 1e-3)
     step_gbps = alg_bytes / (ms_per_step * 1e-3) / 1e9
@@ -569,7 +591,9 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic["traffic_bytes"] if traffic else None,
                      "traffic_detail": traffic, "launch_us": dom_us,
-                     "algorithmic_bytes": alg_bytes},
+                     "algorithmic_bytes": alg_bytes,
+                     "plain_read_us": plain_us, "plain_read_GBps": alg_bytes / (plain_us * 1e-6) / 1e9,
+                     "frac_of_plain_read": plain_us / dom_us},
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -308,6 +308,21 @@ int64_t spec_tree_build_greedy(int64_t K, int64_t S, const double* accuracy, int
 /* Zero-fill `bytes` of a 16-byte aligned workspace on `stream` with a fill kernel (no host sync). */
 sv_status spec_workspace_clear(void* workspace, size_t bytes, sv_stream_t stream);
 
+/* ---------------------------------------------------------------- plain read (measurement aid)
+ * Not a step of the method: reads a_bytes of device buffer a and b_bytes of b (a
+ * verification's target and draft logits, say) with nothing else done, in the
+ * streaming waves' pattern (one wave per 8 KiB chunk, eight 16-byte loads per lane
+ * issued together), so that a benchmark can time what reading those bytes costs by
+ * itself on this GPU. Each wave stores its chunk's largest 32-bit word to
+ * sink[wave] (a's chunks first); a trailing part of a buffer shorter than 16 bytes
+ * is not read. a and b (either may be null with size 0) must be 16-byte aligned;
+ * sink holds at least ceil(a_bytes / 8192) + ceil(b_bytes / 8192) words.
+ * SV_EINVAL for a null or misaligned buffer of nonzero size or a short sink,
+ * SV_ELIMIT past the launch's wave limit; enqueues only.
+ */
+sv_status spec_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink,
+                          size_t sink_words, sv_stream_t stream);
+
 /* ---------------------------------------------------------------- wait limit (test hook)
  * How long, in seconds of the GPU's constant 100 MHz clock, any wait between the
  * waves of one launch may last before it gives up and reports SV_ERR_INTERNAL

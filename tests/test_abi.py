@@ -105,6 +105,16 @@ def test_row_stats_validation(L):
     assert L.spec_row_stats(1, 1.0, 4, 10, DUMMY, None, None, None, None, None, 0, None) == 3
 
 
+def test_read_probe_validation(L):
+    P = lambda a, ab, b, bb, sink, sw: L.spec_read_probe(a, ab, b, bb, sink, sw, None)
+    assert P(None, 0, None, 0, None, 0) == 0                       # nothing to read
+    assert P(None, 16, None, 0, DUMMY, 1) == 1                     # null buffer of nonzero size
+    assert P(DUMMY, 16, None, 8, DUMMY, 1) == 1
+    assert P(ctypes.c_void_p(0x1008), 16, None, 0, DUMMY, 1) == 1  # misaligned
+    assert P(DUMMY, 8192, DUMMY, 8193, DUMMY, 2) == 1              # sink: 1 + 2 chunks
+    assert P(DUMMY, 8192, DUMMY, 8193, None, 3) == 1
+
+
 def test_status_strings(L):
     for s in range(6):
         assert len(sv.status_string(s)) > 0
