@@ -1439,14 +1439,41 @@ __device__ __forceinline__ void tree_wave_walk(const TreeParams& P, int64_t b) {
       cv[s] = cand[i];
     }
   }
+  // every slot's token polled in the same round trip
+  static_assert(RecWords<Token>::N == 1, "one word per token record");
+  {
+    bool have[WW_SLOTS];
+#pragma unroll
+    for (int s = 0; s < WW_SLOTS; ++s) have[s] = s * WAVE + lane >= N;
+    WaitClock clk;
+    for (;;) {
+      bool all = true;
+#pragma unroll
+      for (int s = 0; s < WW_SLOTS; ++s) {
+        if (!have[s]) {
+          const uint64_t x = __hip_atomic_load(yr + s * WAVE + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(x >> 32) == P.tag) {
+            yv[s] = (int)(uint32_t)x;
+            have[s] = true;
+          } else {
+            all = false;
+          }
+        }
+      }
+      if (__ballot(!all) == 0ull) break;
+      if (!clk.more()) {
+#pragma unroll
+        for (int s = 0; s < WW_SLOTS; ++s)
+          if (!have[s]) yv[s] = -2;   // the wait gave up
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < WW_SLOTS; ++s) {
     const int i = s * WAVE + lane;
-    if (i < N) {
-      Token t;
-      yv[s] = get_rec(yr + i, t, P.tag) ? t.y : -2;
-      clear_rec<Token>(yr + i);
-    }
+    if (i < N) clear_rec<Token>(yr + i);
   }
   // validation; a bad parent is replaced by the root, so every chain ends
 #pragma unroll
