@@ -189,6 +189,26 @@ def test_data_errors():
     assert list(g["err_flags"]) == [0, 2, 1, 0, 0]
 
 
+@pytest.mark.parametrize("B", [6, 2000])
+def test_errors_after_a_drawn_rejection(B):
+    # Position 0 rejected for sure (the draft puts all its mass on its token, the
+    # target almost none), so the final token is the residual draw, which usually
+    # comes last; rows after position 0 hold an unusable value in some sequences.
+    # The drawing wave that writes the outputs must still see those error bits
+    # (hold mode at B = 6, a queued launch at B = 2000).
+    w = gen.linear_draft_target(74, 0, B, 2, 1000, gen.DT_F32, 2.0, 0.5, "stochastic", 1.0, f"errs-after{B}")
+    x = w.draft_tokens[:, 0]
+    w.draft[np.arange(B), 0, x] = 1e4
+    w.target[np.arange(B), 0, x] = -1e4
+    w.target[0, 1, 5] = np.nan          # position 1, after the rejection
+    w.target[1, 2, 7] = np.inf          # target row k
+    w.draft[2, 1, :] = -np.inf          # an unusable draft row after the rejection
+    g, o, _, _ = _check(w)
+    assert list(g["err_flags"][:4]) == [2, 2, 2, 0]
+    assert list(g["accept_len"][:4]) == [-1, -1, -1, 0]
+    assert np.all(o["accept_len"][3:] == 0)
+
+
 def test_deterministic_and_workspace_reuse():
     w1 = gen.c2_linear(7, B=8)
     w2 = gen.c2_linear(8, B=8)
