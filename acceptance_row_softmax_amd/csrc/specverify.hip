@@ -14,13 +14,17 @@
 //    the acceptance test u_i < p_t,i(x_i) / p_d,i(x_i) and records the outcome in
 //    the sequence's state word; the update that settles the first rejected position
 //    L hands rows t_L, d_L to the residual waves. Then, per sequence, the streaming
-//    waves of target row k, that row's finishing wave (the bonus draw) and one
-//    residual wave per chunk: each sums max(0, p_t,L - p_d,L) over its chunk; the
-//    last of a sequence picks the chunk holding u*S, and the correction token is
-//    drawn by an inverse-CDF scan inside it (by the wave that holds that chunk in
-//    hold mode, else after a reload);
+//    waves of target row k, that row's finishing wave (the bonus draw) and two
+//    residual waves per chunk: each sums max(0, p_t,L - p_d,L) over its half
+//    chunk; the last of a sequence picks the part holding u*S, and the correction
+//    token is drawn by an inverse-CDF scan inside it (by the wave that holds that
+//    part in hold mode, else after a reload). A launch with more residual waves
+//    than the GPU keeps waiting at once is queued: its residual waves come last and
+//    serve decision slots taken in the order the decisions are made, rejections
+//    first;
 //  * the last event of a sequence (an atomic counter per sequence) writes all of
-//    its outputs.
+//    its outputs; a wave that drew the final token with L settled issues the
+//    emission's reads together with its count.
 // No wave ever waits for work dispatched after it: finishing waves wait for the
 // streaming waves before them, residual waves for decisions of finishing waves
 // before them, and a last event only for a token whose wave has already counted
@@ -145,9 +149,9 @@ __device__ __forceinline__ double residual_raw_sum(const RawN<NU>& rt, const Raw
   return wave_sum(s);
 }
 
-// The last residual wave's verdict on one chunk, for the wave holding it (hold
+// The last residual wave's verdict on one part, for the wave holding it (hold
 // mode): kind 0 not picked, 1 picked (draw from the residual), 2 picked with no
-// residual mass (draw from p_t,L); th the threshold inside the chunk; fo the
+// residual mass (draw from p_t,L); th the threshold inside the part; fo the
 // sequence's event count before the token event, which the last residual wave
 // counted on the drawing wave's behalf.
 struct Verdict {
@@ -205,7 +209,7 @@ struct LinearParams {
   int CG;               // residual waves per sequence: RH per chunk
   int RW;               // words per chunk record
   int EV;               // events per sequence (stochastic): k pair combines, target row k, the final token
-  bool hold;            // residual waves keep their chunk until the draw is placed (see linear_residual_wave)
+  bool hold;            // residual waves keep their part until the draw is placed (see linear_residual_wave)
   bool queue;           // residual waves serve decision slots, not sequences (see publish_decision)
   float c0;
   uint32_t tag;
@@ -933,12 +937,14 @@ __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_
 // Residual wave (b, g), dispatched after the streaming waves of every row a
 // decision depends on: waits for the decision of sequence b (in a queued launch:
 // the decision in slot b, which names its sequence); if a draft was rejected, sums
-// the residual max(0, p_t,L - p_d,L) over part g of rows t_L, d_L. The sequence's last residual wave to count picks the chunk that holds u*S.
-// Without hold mode it reloads that chunk and scans it. In hold mode (a launch
-// whose residual waves can all be resident at once, so that none waits for a
-// wave that cannot start) every residual wave keeps its chunk and its unit sums
-// and waits for the last one's verdict; the wave holding the picked chunk scans it
-// from its registers.
+// the residual max(0, p_t,L - p_d,L) over part g (half a chunk) of rows t_L, d_L.
+// The sequence's last residual wave to count picks the part that holds u*S and
+// counts the token event. Without hold mode it reloads that part and scans it. In
+// hold mode (a launch whose residual waves can all be resident at once, so that
+// none waits for a wave that cannot start) every residual wave keeps its part and
+// its unit sums and waits for the last one's verdict; the wave holding the picked
+// part scans it from its registers and, if the verdict's count says so, writes
+// the outputs.
 template <int DT>
 __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
   const int lane = lane_id();
@@ -985,7 +991,7 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   const float u = P.uniforms[b * (k + 1) + k];
   if (old + 1 != CG) {
     if (!(P.hold && d.kind == 1)) return Ev{0, 0u, false, 0};
-    // hold mode: wait for the verdict on this chunk
+    // hold mode: wait for the verdict on this part
     uint64_t* vr = P.verd + (b * P.CG + g) * VERD_WORDS;
     Verdict v;
     v.kind = 0;
@@ -1088,7 +1094,7 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   const double th = pk.fallback ? (double)INFINITY : pk.theta - pk.before;
   if (P.hold) {
     // every other residual wave of the sequence waits for its verdict (one store
-    // instruction: lane c writes chunk c's kind, the picked chunk's record whole)
+    // instruction: lane c writes part c's kind, the picked part's record whole)
     const int pc = pk.c;
     for (int c0 = 0; c0 < (int)CG; c0 += WAVE) {
       const int c = c0 + lane;
