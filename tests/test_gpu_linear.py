@@ -58,14 +58,16 @@ def test_long_rows(V, mode):
     _check(w)
 
 
-def test_zero_residual_falls_back_to_the_target_row():
+@pytest.mark.parametrize("B", [16, 1200])
+def test_zero_residual_falls_back_to_the_target_row(B):
     # One dominant logit, equal in target and draft; every other draft logit is
     # 0.5 above the target's, so the draft token is rejected when u >= about 0.61.
     # In fp32 every residual term rounds to zero (the dominant probabilities agree
     # to about 1e-10), so the draw falls back to softmax of the target row. The
     # exact residual (the oracle) has all its mass on the dominant token, which the
-    # fallback draws too unless u lands in a tail of about 1e-10.
-    B, k, V = 16, 2, 3000
+    # fallback draws too unless u lands in a tail of about 1e-10. B = 16 runs in
+    # hold mode, B = 1200 (4800 residual waves) queued.
+    k, V = 2, 3000
     rng = np.random.default_rng(5)
     dom = rng.integers(0, V, size=(B, k + 1))
     t = np.zeros((B, k + 1, V))
