@@ -211,6 +211,40 @@ def test_errors_after_a_drawn_rejection(B):
     assert np.all(o["accept_len"][3:] == 0)
 
 
+@pytest.mark.parametrize("case", ["all_accepted", "all_rejected"])
+def test_queued_slots_from_one_end(case):
+    # A queued launch (MTP shape, 128 sequences) whose decisions all take slots
+    # from the back (every draft accepted) or all from the front (every draft
+    # rejected): outputs match the oracle and the workspace is all zeros again,
+    # the slot word included.
+    import torch
+    import acceptance_row_softmax_amd as sv
+    w = gen.c3_mtp(41, "stochastic", B=128)
+    B = w.B
+    if case == "all_accepted":
+        w.uniforms[:, 0] = 0.0
+    else:
+        x = w.draft_tokens[:, 0]
+        w.draft[np.arange(B), 0, x] = 0x7800    # bf16 bits of 2^113: all the draft's mass
+        w.target[np.arange(B), 0, x] = 0xF800   # -2^113: none of the target's
+    G.say(f"queued, {case}: B={B} k={w.k} V={w.V}")
+    L = sv.lib()
+    need = L.spec_verify_linear_workspace(w.B, w.k, w.V, w.dtype, sv.SV_STOCHASTIC)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    t = G.to_dev(w.target, w.dtype)
+    d = G.to_dev(w.draft, w.dtype)
+    x = G.to_dev(w.draft_tokens.astype(np.int32))
+    u = G.to_dev(w.uniforms.astype(np.float32))
+    for _ in range(2):
+        r = sv.verify_linear(t, d, x, u, mode="stochastic", temperature=w.temperature, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+    got = {k_: (v.cpu().numpy() if v is not None else None) for k_, v in r.items()}
+    o = G.oracle_linear(w)
+    G.compare_linear(got, o, True)
+    assert np.all(o["accept_len"] == (1 if case == "all_accepted" else 0))
+
+
 def test_deterministic_and_workspace_reuse():
     w1 = gen.c2_linear(7, B=8)
     w2 = gen.c2_linear(8, B=8)
