@@ -283,7 +283,7 @@ __device__ __forceinline__ bool wait_group(uint32_t* cnt, uint32_t total) {
         ok = false;
         break;
       }
-      __builtin_amdgcn_s_sleep(4);
+      __builtin_amdgcn_s_sleep(1);
     }
     counter_reset(cnt);
   }
