@@ -9,8 +9,8 @@
 //    first draft that is not its row's argmax and writes the outputs.
 //  * stochastic: for each position i < k and each sequence, the streaming waves of
 //    rows t_i and d_i (each writes its chunk's max, softmax weight sum and the draft
-//    token's logit as a tagged record and counts itself into the pair's counter
-//    without waiting), then the pair's finishing wave: it combines both rows, runs
+//    token's logit as a tagged record and ends), then the pair's finishing wave,
+//    which polls those records: it combines both rows, runs
 //    the acceptance test u_i < p_t,i(x_i) / p_d,i(x_i) and records the outcome in
 //    the sequence's state word; the update that settles the first rejected position
 //    L hands rows t_L, d_L to the residual waves. Then, per sequence, the streaming
@@ -164,19 +164,19 @@ constexpr int VERD_WORDS = RecWords<Verdict>::N;   // 4
 // ------------------------------------------------------------------ linear drafts
 // Streaming waves: one per 8 KiB chunk of a row. A streaming wave reduces its
 // chunk to a partial, writes it as the chunk's record with a single store
-// instruction (lane j stores word j), adds one to its combine group's counter, and
-// ends: it never waits for either (greedy has no counter). Every word of a record
-// is a 32-bit value with the call's 32-bit tag (see put_rec):
+// instruction (lane j stores word j) and ends without waiting for it. Every word of
+// a record is a 32-bit value with the call's 32-bit tag (see put_rec):
 //   stochastic: word 0 the chunk's max (f32 bits), words 1 and 2 the low and high
 //               halves of its f64 weight sum relative to fl32(max*c0), word 3 the
 //               row's draft-token logit if the chunk holds that token, else
 //               NOT_HELD (a NaN pattern no decoded logit has)
 //   greedy:     word 0 the chunk's max, word 1 its lowest argmax
 // A combine group is finished by a wave of its own, dispatched after the group's
-// chunks: in stochastic mode it polls the group's counter (one lane) until every
-// chunk has counted, then reads the records, polling each word until it carries the
-// tag (a count can land before the record it follows); in greedy mode it polls the
-// records directly. It clears them behind the read. Groups:
+// chunks: it polls the group's records (each lane its chunks' words) until every
+// word carries the call's tag, and clears them behind the read. Counting each
+// chunk into a group counter and polling that instead measured slower: a
+// streaming wave with a store or atomic still in flight holds its slot, and the
+// counter adds a round trip before the records are read. Groups:
 // greedy, every chunk of a sequence; stochastic, the target and draft rows of one
 // position (the pair finish runs that position's acceptance test), and the target
 // row after the last draft (the bonus draw).
@@ -198,7 +198,6 @@ struct LinearParams {
   uint64_t* verd;       // [B][CG]  Verdict records (hold mode)
   uint64_t* tok;        // [B]      Token records
   uint64_t* prob;       // [B][k]   Probs records (stochastic)
-  uint32_t* grp_cnt;    // [groups] segments counted per combine group
   uint64_t* state;      // [B]      sequence state words (stochastic)
   uint32_t* fin;        // [B]      events per sequence (stochastic)
   uint32_t* res_cnt;    // [B]      residual waves done per sequence
@@ -271,25 +270,6 @@ __device__ __forceinline__ void seg_store(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return ((uint64_t)tag << 32) | v; }
 
-// Waits (lane 0) until `total` segments have counted into a group counter, then
-// resets it; false on timeout.
-__device__ __forceinline__ bool wait_group(uint32_t* cnt, uint32_t total) {
-  bool ok = true;
-  if (lane_id() == 0) {
-    WaitClock clk;
-    for (;;) {
-      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= total) break;
-      if (!clk.more()) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    counter_reset(cnt);
-  }
-  return __shfl((int)ok, 0) != 0;
-}
-
 constexpr uint32_t NOT_HELD = 0x7fffffffu;
 
 // The chunk partials of NR consecutive rows q0, q0+1 (stochastic records; lane l
@@ -297,8 +277,11 @@ constexpr uint32_t NOT_HELD = 0x7fffffffu;
 // the row holds it), each word polled until it carries the call's tag, then zeroed.
 // One round of 64 chunks at a time (for both rows), so that only one round's words
 // are held; every round's wait counts against the same time limit. false on timeout.
+// If sp is given, lane 0 reads that sequence state word with every poll, so that
+// *sv is the state as it was when the last records arrived.
 template <int NR>
-__device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, RowParts (&rp)[NR]) {
+__device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, RowParts (&rp)[NR],
+                                          const uint64_t* sp = nullptr, uint64_t* sv = nullptr) {
   const int lane = lane_id();
   bool ok = true;
   WaitClock clk;
@@ -327,6 +310,7 @@ __device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, Row
       for (int e = 0; e < 4; ++e) w[r][e] = 0;
     bool got = false;
     for (bool go = ok; go && !got;) {   // after a timeout, later rounds are not waited for
+      if (sp && lane == 0) *sv = state_load(sp);
       bool mine = true;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -739,14 +723,12 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
   const int64_t k = P.k, V = P.V;
   const int x = P.tokens[b * k + i];
   const int64_t qt = row_q<true>(P, b, i, 0);
-  bool got = wait_group(P.grp_cnt + (b * k + i) * CSTRIDE, (uint32_t)(2 * P.C));
-  // the state as it is now, read with the records: if every earlier position is
-  // already accepted, a rejection here settles L = i without the state update's
-  // round trip
+  // the state as it was when the last records arrived: if every earlier position
+  // is already accepted, a rejection here settles L = i without the state
+  // update's round trip
   uint64_t se = 0;
-  if (lane == 0 && i > 0) se = state_load(P.state + b * SSTRIDE);
   RowParts rp[2];
-  got = read_rows<2>(P, qt, rp) && got;
+  const bool got = read_rows<2>(P, qt, rp, i > 0 ? P.state + b * SSTRIDE : nullptr, &se);
   double wl[MAX_ROUNDS];
   const RowSums st = row_sums<true, false>(rp[0], P.c0, wl, P.C);
   const RowSums sd = row_sums<true, false>(rp[1], P.c0, wl, P.C);
@@ -855,11 +837,9 @@ template <int DT>
 __device__ __forceinline__ Ev rowk_finish(const LinearParams& P, int64_t b) {
   const int lane = lane_id();
   const int64_t k = P.k, V = P.V;
-  bool got = wait_group(P.grp_cnt + (P.B * k + b) * CSTRIDE, (uint32_t)P.C);
-  uint64_t sn = 0;
-  if (lane == 0) sn = state_load(P.state + b * SSTRIDE);   // read with the records
+  uint64_t sn = 0;   // the state, read with the records
   RowParts rpa[1];
-  got = read_rows<1>(P, row_q<true>(P, b, k, 0), rpa) && got;
+  const bool got = read_rows<1>(P, row_q<true>(P, b, k, 0), rpa, P.state + b * SSTRIDE, &sn);
   const RowParts& rp = rpa[0];
   double wl[MAX_ROUNDS];
   const RowSums rs = row_sums<true, false>(rp, P.c0, wl, P.C);
@@ -905,8 +885,8 @@ __device__ __forceinline__ Ev rowk_finish(const LinearParams& P, int64_t b) {
   return Ev{b, 1u | ef, false, 0};
 }
 
-// Streaming wave of chunk c of row q: the chunk's partial goes out as its record,
-// then one count into its combine group. Nothing here waits for another wave.
+// Streaming wave of chunk c of row q: the chunk's partial goes out as its record.
+// Nothing here waits for another wave.
 template <int DT, bool STOCH>
 __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_t q32, uint32_t c32) {
   const int lane = lane_id();
@@ -926,11 +906,6 @@ __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_
     if (lane < 4) seg_store(rec + lane, tagged(word, P.tag));
   } else {
     if (lane < 2) seg_store(rec + lane, tagged(lane == 0 ? __float_as_uint(p.m) : (uint32_t)p.idx, P.tag));
-  }
-  if constexpr (STOCH) {
-    const uint32_t grp = (uint32_t)(i < P.k ? b * P.k + i : P.B * P.k + b);
-    if (lane == 0) (void)__hip_atomic_fetch_add(P.grp_cnt + (int64_t)grp * CSTRIDE, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -2074,7 +2049,7 @@ __global__ __launch_bounds__(BLOCK) void read_probe_kernel(const uint4* a, int64
 
 // ------------------------------------------------------------------ host side
 struct LinearShape {
-  int64_t R, RQ, C, RW, groups;
+  int64_t R, RQ, C, RW;
 };
 
 inline LinearShape linear_shape(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode) {
@@ -2084,7 +2059,6 @@ inline LinearShape linear_shape(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv
   s.RQ = B * s.R;
   s.C = chunks_per_row(V, dt);
   s.RW = stoch ? 4 : 2;
-  s.groups = stoch ? B * (k + 1) : B;
   return s;
 }
 
@@ -2093,7 +2067,7 @@ Layout linear_layout(int64_t B, int64_t k, int64_t V, sv_dtype dt, sv_mode mode)
   const size_t RG = mode == SV_STOCHASTIC ? (size_t)(B * s.C * RH) : 0;   // residual waves (stochastic only)
   return make_layout({(size_t)(s.RQ * s.C * s.RW) * 8, (size_t)(B * k) * PST_WORDS * 8, (size_t)B * ROW_WORDS * 8,
                       RG * DEC_WORDS * 8, RG * RES_WORDS * 8, (size_t)B * 8,
-                      (size_t)(s.groups * CSTRIDE) * 4, (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
+                      (size_t)(B * SSTRIDE) * 8, (size_t)(B * CSTRIDE) * 4,
                       (size_t)(B * CSTRIDE) * 4, (size_t)(B * CSTRIDE) * 4, (size_t)(B * k) * PROB_WORDS * 8,
                       RG * VERD_WORDS * 8, (size_t)8});
 }
@@ -2236,14 +2210,13 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.dec = reinterpret_cast<uint64_t*>(ws + lay.off[3]);
   P.res = reinterpret_cast<uint64_t*>(ws + lay.off[4]);
   P.tok = reinterpret_cast<uint64_t*>(ws + lay.off[5]);
-  P.grp_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[6]);
-  P.state = reinterpret_cast<uint64_t*>(ws + lay.off[7]);
-  P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
-  P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
-  P.slots = reinterpret_cast<uint64_t*>(ws + lay.off[13]);
-  P.errw = reinterpret_cast<uint32_t*>(ws + lay.off[10]);
-  P.prob = reinterpret_cast<uint64_t*>(ws + lay.off[11]);
-  P.verd = reinterpret_cast<uint64_t*>(ws + lay.off[12]);
+  P.state = reinterpret_cast<uint64_t*>(ws + lay.off[6]);
+  P.fin = reinterpret_cast<uint32_t*>(ws + lay.off[7]);
+  P.res_cnt = reinterpret_cast<uint32_t*>(ws + lay.off[8]);
+  P.slots = reinterpret_cast<uint64_t*>(ws + lay.off[12]);
+  P.errw = reinterpret_cast<uint32_t*>(ws + lay.off[9]);
+  P.prob = reinterpret_cast<uint64_t*>(ws + lay.off[10]);
+  P.verd = reinterpret_cast<uint64_t*>(ws + lay.off[11]);
   P.B = B;
   P.k = k;
   P.V = V;

@@ -62,7 +62,10 @@ struct RowStat {
 
 // ------------------------------------------------------------------ lanes and waves
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
-__device__ __forceinline__ int wave_in_block() { return threadIdx.x / WAVE; }
+// The wave's index in its workgroup, as a wave-uniform (scalar) value: role and
+// address arithmetic derived from it then runs on the scalar unit, and pointers
+// chosen by it come from scalar kernel-argument loads rather than vector loads.
+__device__ __forceinline__ int wave_in_block() { return __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE); }
 
 // Cross-lane steps use DPP row operations (inside rows of 16 lanes: swap
 // neighbours, swap pairs, mirror halves, mirror the row), after which every lane
