@@ -773,11 +773,20 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
   de.Md = ps.Md;
   de.Zt = ps.Zt;
   de.Zd = ps.Zd;
-  if (early && !P.queue) publish_decision(P, b, de, 0);
-  // The state update first: an atomic whose result the wave waits for also waits
-  // for every store the wave issued before it, and the records below are read by
-  // polling, so they may land later. A queued launch's early decision needs its
-  // slot first; that round trip overlaps the state update's.
+  Probs pr;
+  pr.pt = (float)pt;
+  pr.pd = (float)pd;
+  // An early decision goes out after this position's probability record, which
+  // the wave that will emit reads as soon as it has the decision (were the record
+  // not there yet, that wave would poll for it again, a round trip more).
+  if (early && !P.queue) {
+    put_rec_wave(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
+    publish_decision(P, b, de, 0);
+  }
+  // Otherwise the state update first: an atomic whose result the wave waits for
+  // also waits for every store the wave issued before it, and the records below
+  // are read by polling, so they may land later. A queued launch's early decision
+  // needs its slot first; that round trip overlaps the state update's.
   uint64_t olds = 0, taken = 0;
   if (lane == 0) {
     if (!got) error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
@@ -785,11 +794,8 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
     olds = state_or(P.state + b * SSTRIDE, bits);
     if (early && P.queue) taken = take_slot(P, false);
   }
+  if (!(early && !P.queue)) put_rec_wave(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
   if (early && P.queue) publish_decision(P, b, de, taken);
-  Probs pr;
-  pr.pt = (float)pt;
-  pr.pd = (float)pd;
-  put_rec_wave(P.prob + (b * k + i) * PROB_WORDS, pr, P.tag);
   put_rec_wave(P.pst + (b * k + i) * PST_WORDS, ps, P.tag);
   olds = bcast(olds);
   {
