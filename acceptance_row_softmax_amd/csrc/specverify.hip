@@ -22,13 +22,14 @@
 //    than the GPU keeps waiting at once is queued: its residual waves come last and
 //    serve decision slots taken in the order the decisions are made, rejections
 //    first;
-//  * the last event of a sequence (an atomic counter per sequence) writes all of
-//    its outputs; a wave that drew the final token with L settled issues the
-//    emission's reads together with its count.
+//  * one wave writes all outputs of a sequence: the wave that drew its correction
+//    token, once the sequence's other events (an atomic counter per sequence) have
+//    all counted; with every draft accepted, the last event to count. A wave that
+//    drew the final token with L settled issues the emission's reads early.
 // No wave ever waits for work dispatched after it: finishing waves wait for the
-// streaming waves before them, residual waves for decisions of finishing waves
-// before them, and a last event only for a token whose wave has already counted
-// itself. Every wait is bounded in time.
+// streaming waves before them, residual waves for decisions and events of
+// finishing waves before them, and a last event only for a token whose wave has
+// already counted itself. Every wait is bounded in time.
 //
 // Trees: a streaming launch of the same kind reduces every node's row (greedy:
 // its argmax is the node's token; stochastic: for a small batch the token is
@@ -152,8 +153,8 @@ __device__ __forceinline__ double residual_raw_sum(const RawN<NU>& rt, const Raw
 // The last residual wave's verdict on one part, for the wave holding it (hold
 // mode): kind 0 not picked, 1 picked (draw from the residual), 2 picked with no
 // residual mass (draw from p_t,L); th the threshold inside the part; fo the
-// sequence's event count before the token event, which the last residual wave
-// counted on the drawing wave's behalf.
+// sequence's event count as the last residual wave read it with the part sums
+// (the drawing wave polls it again only if some other event had not counted).
 struct Verdict {
   int kind;
   uint32_t fo;
@@ -510,11 +511,10 @@ __device__ __forceinline__ EmitPre emit_prefetch(const LinearParams& P, int64_t 
 }
 
 // The emission of sequence b by the wave that drew its final token y with L
-// settled (a rejection at L < k, or every draft accepted, L = k), once its event
-// count `fo` (the value before its own, with its own event's EV_ERR) shows it is the
-// last event: L needs no read of the state word, and the error word is read only if
-// an event set error bits. `pre` must come from emit_prefetch (its drafts are used
-// as they are).
+// settled (a rejection at L < k, or every draft accepted, L = k), once the event
+// count `fo` (the other events', with their EV_ERR) shows every other event in: L
+// needs no read of the state word, and the error word is read only if an event set
+// error bits. `pre` must come from emit_prefetch (its drafts are used as they are).
 template <int DT>
 __device__ __forceinline__ void emit_drawn(const LinearParams& P, int64_t b, int L, int y, const EmitPre& pre,
                                            uint32_t fo) {
@@ -915,17 +915,45 @@ __device__ __forceinline__ void linear_chunk_wave(const LinearParams& P, uint32_
   }
 }
 
+// The event count of sequence b once its other events (k pair decisions and target
+// row k) have all counted, for the wave that drew its correction token: that wave
+// counts no event of its own and is always the one that emits (no other event's
+// count reaches the total). `snap` is a read of the count taken earlier; polled
+// again only if it was short. A wait that gives up sets SV_ERR_INTERNAL and
+// returns with EV_ERR, so that the emission reads the error word.
+__device__ __forceinline__ uint32_t others_counted(const LinearParams& P, int64_t b, uint32_t snap) {
+  const uint32_t want = (uint32_t)P.EV - 1u;
+  if ((snap & EV_COUNT) == want) return snap;
+  uint32_t v = snap;
+  if (lane_id() == 0) {
+    WaitClock clk;
+    for (;;) {
+      v = __hip_atomic_load(P.fin + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((v & EV_COUNT) == want) break;
+      if (!clk.more()) {
+        error_or(P.errw + b * CSTRIDE, (uint32_t)SV_ERR_INTERNAL);
+        v |= EV_ERR;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  return bcast(v);
+}
+
 // Residual wave (b, g), dispatched after the streaming waves of every row a
 // decision depends on: waits for the decision of sequence b (in a queued launch:
 // the decision in slot b, which names its sequence); if a draft was rejected, sums
 // the residual max(0, p_t,L - p_d,L) over part g (half a chunk) of rows t_L, d_L.
-// The sequence's last residual wave to count picks the part that holds u*S and
-// counts the token event. Without hold mode it reloads that part and scans it. In
-// hold mode (a launch whose residual waves can all be resident at once, so that
-// none waits for a wave that cannot start) every residual wave keeps its part and
-// its unit sums and waits for the last one's verdict; the wave holding the picked
-// part scans it from its registers and, if the verdict's count says so, writes
-// the outputs.
+// The sequence's last residual wave to count picks the part that holds u*S.
+// Without hold mode it reloads that part and scans it. In hold mode (a launch
+// whose residual waves can all be resident at once, so that none waits for a wave
+// that cannot start) every residual wave keeps its part and its unit sums and
+// waits for the last one's verdict; the wave holding the picked part scans it from
+// its registers. The wave that draws writes the outputs (see others_counted): a
+// token event counted ahead of the draw let another event's wave become the last
+// one, which then waited for the token record, a round trip more (about half the
+// rejecting sequences at C2).
 template <int DT>
 __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_t b, int64_t g) {
   const int lane = lane_id();
@@ -981,12 +1009,9 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     const bool got = poll_rec(vr, v, P.tag);
     if (lane == 0) clear_rec<Verdict>(vr);
     if (!got || v.kind == 0) return Ev{0, 0u, false, 0};
-    // the token event is already counted (by the last residual wave); if it was the
-    // sequence's last event, the emission's reads go out before the scan, so that
-    // their round trip overlaps it
-    const bool last = (v.fo & EV_COUNT) + 1 == (uint32_t)P.EV;
-    EmitPre pre{};
-    if (last) pre = emit_prefetch(P, b);
+    // this wave emits: the emission's reads go out before the scan, so that their
+    // round trip overlaps it
+    const EmitPre pre = emit_prefetch(P, b);
     ResidW rx = rw;
     int yh;
     if (v.kind == 2) {
@@ -998,27 +1023,21 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     } else {
       yh = (int)chunk_invcdf_us<DT, true>(kg, rt, rd, us, v.th, rx);
     }
-    if (last) {
-      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-      emit_drawn<DT>(P, b, d.L, yh, pre, v.fo);
-    } else if (lane == 0) {
-      Token t;
-      t.y = yh;
-      put_rec(P.tok + b, t, P.tag);
-    }
+    const uint32_t fo = others_counted(P, b, v.fo);
+    if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+    emit_drawn<DT>(P, b, d.L, yh, pre, fo);
     return Ev{0, 0u, false, 0};
   }
   // last residual wave of the sequence: draw the correction token
   if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
   int y = (d.kind == 3) ? -2 : -1;
   if (d.kind != 1) return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
-  // The token event's count and the emission's reads go out with the reads of the
-  // residual sums (in hold mode the count is taken on behalf of the wave that will
-  // draw, which learns it from its verdict). Whichever wave draws writes the
-  // outputs if the count says the token was the sequence's last event; otherwise
-  // the last event's wave waits for the token record.
+  // A read of the other events' count and the emission's reads go out with the
+  // reads of the residual sums (in hold mode the count is passed on in the
+  // verdicts). Whichever wave draws the token writes the outputs, once every other
+  // event has counted (see others_counted).
   uint32_t fo = 0;
-  if (lane == 0) fo = counter_add(P.fin + b * CSTRIDE, 1u);
+  if (lane == 0) fo = __hip_atomic_load(P.fin + b * CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const EmitPre pre = emit_prefetch(P, b);
   constexpr int RR = RH * MAX_ROUNDS;   // rounds of 64 parts
   double wl[RR];
@@ -1038,7 +1057,6 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     }
   }
   fo = bcast(fo);
-  const bool last = (fo & EV_COUNT) + 1 == (uint32_t)P.EV;
   ChunkPick pk;
   pk.c = -1;
   ResidW rx = rw;
@@ -1099,14 +1117,9 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     load_units<DT, HU>(dx, P.V, pu, rd);
   }
   if (pk.c >= 0) y = (int)chunk_invcdf<DT, true>(kg, rt, rd, th, rx);
-  if (last) {
-    if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
-    emit_drawn<DT>(P, b, d.L, y, pre, fo);
-  } else if (lane == 0) {
-    Token t;
-    t.y = y;
-    put_rec(P.tok + b, t, P.tag);
-  }
+  fo = others_counted(P, b, fo);
+  if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
+  emit_drawn<DT>(P, b, d.L, y, pre, fo);
   return Ev{0, 0u, false, 0};
 }
 
