@@ -275,7 +275,8 @@ constexpr uint32_t NOT_HELD = 0x7fffffffu;
 
 // The chunk partials of NR consecutive rows q0, q0+1 (stochastic records; lane l
 // holding chunks l + 64 t of each row, and the draft token's logit if some chunk of
-// the row holds it), each word polled until it carries the call's tag, then zeroed.
+// the row holds it), each word polled until it carries the call's tag (clear_rows
+// zeroes them afterwards).
 // One round of 64 chunks at a time (for both rows), so that only one round's words
 // are held; every round's wait counts against the same time limit. false on timeout.
 // If sp is given, lane 0 reads that sequence state word with every poll, so that
@@ -340,10 +341,6 @@ __device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, Row
           xin[r] = 1;
           xv[r] = (uint32_t)w[r][3];
         }
-        // leave the record zero for the next call
-        uint64_t* q = P.seg + ((q0 + r) * P.C + c) * P.RW;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) seg_store(q + e, 0);
       }
     }
   }
@@ -355,6 +352,22 @@ __device__ __forceinline__ bool read_rows(const LinearParams& P, int64_t q0, Row
     rp[r].got = ok;
   }
   return ok;
+}
+
+// Zeroes the chunk records of NR consecutive rows from q0 for the next call (lane l:
+// chunks l + 64 t), once the wave has nothing left to wait for: a wait for a load
+// or a returning atomic also waits for every store issued before it, and these
+// device-scope stores take about a microsecond to complete.
+template <int NR>
+__device__ __forceinline__ void clear_rows(const LinearParams& P, int64_t q0) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    for (int c = lane; c < P.C; c += WAVE) {
+      uint64_t* q = P.seg + ((q0 + r) * P.C + c) * P.RW;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) seg_store(q + e, 0);
+    }
 }
 
 constexpr int TOKEN_UNKNOWN = INT_SENTINEL;
@@ -386,17 +399,28 @@ __device__ __forceinline__ EmitIn emit_load(const LinearParams& P, int64_t b, bo
   const bool has = lane < k;
   in.x = has ? P.tokens[b * k + lane] : 0;
   in.pr.pt = in.pr.pd = NAN;
-  if (STOCH && has) {
-    in.pg = get_rec(P.prob + (b * k + lane) * PROB_WORDS, in.pr, P.tag);
+  if (STOCH && has) in.pg = get_rec(P.prob + (b * k + lane) * PROB_WORDS, in.pr, P.tag);
+  return in;
+}
+
+// Leaves sequence b's words and records zero for the next call (stochastic). Issued
+// after the outputs: a wait for a load also waits for every store the wave issued
+// before it, and these device-scope stores take about a microsecond to complete,
+// so issued first they delayed every emission by that much (a read of the error
+// word, whose place among the wave's memory operations the compiler cannot count,
+// made it wait for all of them).
+__device__ __forceinline__ void emit_clear(const LinearParams& P, int64_t b, bool token_rec) {
+  const int lane = lane_id();
+  const int64_t k = P.k;
+  if (lane < k) {
     clear_rec<Probs>(P.prob + (b * k + lane) * PROB_WORDS);
     clear_rec<PairStat>(P.pst + (b * k + lane) * PST_WORDS);
   }
-  // leave the sequence's words and records zero for the next call
   if (lane == 0) counter_reset(P.state + b * SSTRIDE);
   if (lane == 1) counter_reset(P.errw + b * CSTRIDE);
-  if (lane == 2 && !token_known) clear_rec<Token>(P.tok + b);
-  if (STOCH && lane == 3) clear_rec<RowStat>(P.rks + b * ROW_WORDS);
-  return in;
+  if (lane == 2 && token_rec) clear_rec<Token>(P.tok + b);
+  if (lane == 3) clear_rec<RowStat>(P.rks + b * ROW_WORDS);
+  if (lane == 4) counter_reset(P.fin + b * CSTRIDE);
 }
 
 // Writes every output of sequence b (its last event): the first rejected
@@ -450,6 +474,7 @@ template <int DT, bool STOCH>
 __device__ __forceinline__ void linear_emit(const LinearParams& P, int64_t b, int known_y) {
   const EmitIn in = emit_load<DT, STOCH>(P, b, known_y != TOKEN_UNKNOWN);
   emit_store<DT, STOCH>(P, b, in, known_y);
+  if constexpr (STOCH) emit_clear(P, b, known_y == TOKEN_UNKNOWN);
 }
 
 // Events a wave counts when it is done: n of sequence b (n = 0: none), the final
@@ -483,7 +508,6 @@ __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, b
     }
     return;
   }
-  if (lane_id() == 0) counter_reset(P.fin + b * CSTRIDE);
   linear_emit<DT, STOCH>(P, b, token ? y : TOKEN_UNKNOWN);
 }
 
@@ -541,14 +565,9 @@ __device__ __forceinline__ void emit_drawn(const LinearParams& P, int64_t b, int
     }
     if (here) __builtin_memcpy(&in.pr, w, sizeof(Probs));
     else in.pg = get_rec(pr, in.pr, P.tag);
-    clear_rec<Probs>(pr);
-    clear_rec<PairStat>(P.pst + (b * k + lane) * PST_WORDS);
   }
-  // leave the sequence's words and records zero for the next call
-  if (lane == 0) counter_reset(P.state + b * SSTRIDE);
-  if (lane == 1) counter_reset(P.errw + b * CSTRIDE);
-  if (lane == 3) clear_rec<RowStat>(P.rks + b * ROW_WORDS);
   emit_store<DT, true>(P, b, in, y);
+  emit_clear(P, b, false);
 }
 
 // Greedy finish of sequence b: polls the chunk records of its k+1 target rows
@@ -561,6 +580,10 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
   const int lane = lane_id();
   const int64_t k = P.k;
   const int R = (int)k + 1;
+  // the drafts, read before the records: a read issued after the records' clearing
+  // stores would wait for them (a wait for a load also waits for every store before it)
+  const bool has = lane < k;
+  const int xk = has ? P.tokens[b * k + lane] : 0;
   bool ok = true;
   int am = -1;
 #pragma unroll 1
@@ -612,9 +635,8 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
       if (lane == r0 + j) am = (m > -INFINITY && idx != INT_SENTINEL) ? idx : -1;
     }
   }
-  const bool has = lane < k;
   EmitIn in;
-  in.x = has ? P.tokens[b * k + lane] : 0;
+  in.x = xk;
   in.ew = __ballot(lane < R && am < 0) ? (uint32_t)SV_ERR_ROW : 0u;
   const unsigned long long miss = __ballot(has && in.x != am);
   const int L = miss ? first_lane(miss) : (int)k;
@@ -824,7 +846,6 @@ __device__ __forceinline__ Ev pair_finish(const LinearParams& P, int64_t b, int6
     const EmitPre pre = emit_prefetch(P, b);
     fo = bcast(fo);
     if ((fo & EV_COUNT) + 2 == (uint32_t)P.EV) {
-      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
       emit_drawn<DT>(P, b, (int)k, y, pre, fo | ef);
     } else if (lane == 0) {
       Token t;
@@ -879,7 +900,6 @@ __device__ __forceinline__ Ev rowk_finish(const LinearParams& P, int64_t b) {
     const EmitPre pre = emit_prefetch(P, b);
     fo = bcast(fo);
     if ((fo & EV_COUNT) + 2 == (uint32_t)P.EV) {
-      if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
       emit_drawn<DT>(P, b, (int)k, st.y, pre, fo | ef);
     } else if (lane == 0) {
       Token t;
@@ -967,18 +987,29 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   d.Zt = d.Zd = 0.0;
   uint64_t* dr = P.dec + (b * P.CG + g) * DEC_WORDS;   // this wave's copy of the decision
   if (!poll_rec(dr, d, P.tag)) d.kind = 3;   // 3: the decision never arrived
-  if (lane == 0) clear_rec<Decision>(dr);
+  // The records this wave read are cleared for the next call on its way out: a
+  // wait for a load (or a returning atomic) also waits for every store the wave
+  // issued before it, and these device-scope stores take about a microsecond.
+  const auto done = [&]() {
+    if (lane == 0) clear_rec<Decision>(dr);
+  };
   if (P.queue) {
     // the slot's sequence; a slot whose decision never arrived names none
-    if (d.kind == 3 || d.b < 0 || d.b >= P.B) return Ev{0, 0u, false, 0};
+    if (d.kind == 3 || d.b < 0 || d.b >= P.B) {
+      done();
+      return Ev{0, 0u, false, 0};
+    }
     b = d.b;
   }
   const char* trow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 0);
   const char* drow = row_ptr<DT, true>(P, b, d.kind == 1 ? d.L : 0, 1);
   const ResidW rw = make_residw(d, P.c0);
   // No draft rejected: nothing to draw here (the bonus token is target row k's), so
-  // no count either; each residual wave has cleared its own copy of the decision.
-  if (d.kind == 0) return Ev{0, 0u, false, 0};
+  // no count either; each residual wave clears its own copy of the decision.
+  if (d.kind == 0) {
+    done();
+    return Ev{0, 0u, false, 0};
+  }
   // Counted before the sums: the count's round trip overlaps this wave's loads. The
   // last to count draws; it reads the others' records with polling reads, which
   // wait for any that are not written yet.
@@ -999,7 +1030,10 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   old = bcast(old);
   const float u = P.uniforms[b * (k + 1) + k];
   if (old + 1 != CG) {
-    if (!(P.hold && d.kind == 1)) return Ev{0, 0u, false, 0};
+    if (!(P.hold && d.kind == 1)) {
+      done();
+      return Ev{0, 0u, false, 0};
+    }
     // hold mode: wait for the verdict on this part
     uint64_t* vr = P.verd + (b * P.CG + g) * VERD_WORDS;
     Verdict v;
@@ -1007,8 +1041,11 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
     v.fo = 0;
     v.th = 0.0;
     const bool got = poll_rec(vr, v, P.tag);
-    if (lane == 0) clear_rec<Verdict>(vr);
-    if (!got || v.kind == 0) return Ev{0, 0u, false, 0};
+    if (!got || v.kind == 0) {
+      if (lane == 0) clear_rec<Verdict>(vr);
+      done();
+      return Ev{0, 0u, false, 0};
+    }
     // this wave emits: the emission's reads go out before the scan, so that their
     // round trip overlaps it
     const EmitPre pre = emit_prefetch(P, b);
@@ -1024,14 +1061,23 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
       yh = (int)chunk_invcdf_us<DT, true>(kg, rt, rd, us, v.th, rx);
     }
     const uint32_t fo = others_counted(P, b, v.fo);
-    if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
     emit_drawn<DT>(P, b, d.L, yh, pre, fo);
+    if (lane == 0) clear_rec<Verdict>(vr);
+    done();
     return Ev{0, 0u, false, 0};
   }
-  // last residual wave of the sequence: draw the correction token
-  if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
+  // last residual wave of the sequence: draw the correction token; the part
+  // records and the counter are cleared on the way out
+  const auto done_last = [&]() {
+    if (lane == 0) counter_reset(P.res_cnt + b * CSTRIDE);
+    for (int cc = lane; cc < (int)CG; cc += WAVE) clear_rec<ResPart>(P.res + (b * P.CG + cc) * RES_WORDS);
+    done();
+  };
   int y = (d.kind == 3) ? -2 : -1;
-  if (d.kind != 1) return Ev{b, 1u, true, y};   // the final token (no draw: a data error or a timed-out wait)
+  if (d.kind != 1) {   // the final token (no draw: a data error or a timed-out wait)
+    done_last();
+    return Ev{b, 1u, true, y};
+  }
   // A read of the other events' count and the emission's reads go out with the
   // reads of the residual sums (in hold mode the count is passed on in the
   // verdicts). Whichever wave draws the token writes the outputs, once every other
@@ -1053,7 +1099,6 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
       const bool gr = get_rec(rec, r, P.tag);
       ok = ok && gr;
       wl[t] = gr ? r.s : 0.0;
-      clear_rec<ResPart>(rec);
     }
   }
   fo = bcast(fo);
@@ -1105,7 +1150,10 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
         put_rec(P.verd + (b * P.CG + c) * VERD_WORDS, v, P.tag);
       }
     }
-    if (pc >= 0 && pc != g) return Ev{0, 0u, false, 0};   // the holder draws and emits
+    if (pc >= 0 && pc != g) {   // the holder draws and emits
+      done_last();
+      return Ev{0, 0u, false, 0};
+    }
     // nothing to draw from (pc < 0: the token is -1, or -2 after a timed-out read),
     // or the pick is this wave's own chunk, whose registers were not kept: the
     // reload below serves
@@ -1118,8 +1166,8 @@ __device__ __forceinline__ Ev linear_residual_wave(const LinearParams& P, int64_
   }
   if (pk.c >= 0) y = (int)chunk_invcdf<DT, true>(kg, rt, rd, th, rx);
   fo = others_counted(P, b, fo);
-  if (lane == 0) counter_reset(P.fin + b * CSTRIDE);
   emit_drawn<DT>(P, b, d.L, y, pre, fo);
+  done_last();
   return Ev{0, 0u, false, 0};
 }
 
@@ -1222,6 +1270,11 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(3))) void
     if (r.kind == ROLE_GREEDY) greedy_finish<DT>(P, r.b);
   }
   if (STOCH && ev.n) linear_event<DT, STOCH>(P, ev.b, ev.token, ev.y, ev.n);
+  if constexpr (STOCH) {
+    // the finishers' chunk records, cleared last
+    if (r.kind == ROLE_PAIR) clear_rows<2>(P, row_q<true>(P, r.b, r.c, 0));
+    else if (r.kind == ROLE_ROWK) clear_rows<1>(P, row_q<true>(P, r.b, P.k, 0));
+  }
 }
 
 // ------------------------------------------------------------------ trees
