@@ -108,14 +108,15 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(SampleParams P) {
   const int64_t q = q32, c = c32;
   const char* row = P.x + (q * P.V) * E;
   const Partial p = chunk_partial<DT, STOCH, !STOCH>(row, P.V, c, P.c0);
+  // the count before the record: a returning atomic also waits for the stores
+  // issued before it (the reader polls the record's tag, so the order is free)
   uint32_t old = 0;
   if (lane_id() == 0) {
-    put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
     old = counter_add(P.row_cnt + q * CSTRIDE, 1u);
+    put_rec(P.parts + (q * P.C + c) * PART_WORDS, p, P.tag);
   }
   old = bcast(old);
   if (old + 1 != (uint32_t)P.C) return;
-  if (lane_id() == 0) counter_reset(P.row_cnt + q * CSTRIDE);
   const RowParts rp = read_parts(P.parts + q * P.C * PART_WORDS, P.C, P.tag);
   double wl[MAX_ROUNDS];
   const RowSums rs = row_sums<STOCH>(rp, P.c0, wl);
@@ -134,6 +135,7 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(SampleParams P) {
     P.tokens[q] = y;
     if (P.err_flags) P.err_flags[q] = err;
   }
+  clear_parts<Partial>(P.parts + q * P.C * PART_WORDS, P.C, P.row_cnt + q * CSTRIDE);
 }
 
 template <int DT, bool STOCH>

@@ -28,7 +28,7 @@ struct RowParts {
   float xv;    // its logit
 };
 
-// Reads the C partials of a row and clears them.
+// Reads the C partials of a row (clear_parts zeroes them afterwards).
 __device__ __forceinline__ RowParts read_parts(uint64_t* parts, int C, uint32_t tag) {
   const int lane = lane_id();
   RowParts rp;
@@ -53,13 +53,19 @@ __device__ __forceinline__ RowParts read_parts(uint64_t* parts, int C, uint32_t 
   const unsigned long long xm = __ballot(xin != 0);
   rp.xin = xm != 0ull;
   rp.xv = __shfl(xv, xm ? first_lane(xm) : 0);
-#pragma unroll
-  for (int t = 0; t < MAX_ROUNDS; ++t) {
-    const int c = t * WAVE + lane;
-    if (c < C) clear_rec<Partial>(parts + (int64_t)c * PART_WORDS);
-  }
   rp.got = __ballot(!got) == 0ull;
   return rp;
+}
+
+// Zeroes the C partials of a row, and its arrival counter, for the next call: by
+// the wave that read them, once it has nothing left to wait for (a wait for a load
+// or a returning atomic also waits for every store the wave issued before it, and
+// a device-scope store takes about a microsecond to complete).
+template <class T>
+__device__ __forceinline__ void clear_parts(uint64_t* parts, int C, uint32_t* cnt) {
+  const int lane = lane_id();
+  for (int c = lane; c < C; c += WAVE) clear_rec<T>(parts + (int64_t)c * PART_WORDS);
+  if (lane == 0) counter_reset(cnt);
 }
 
 struct RowSums {
