@@ -366,7 +366,7 @@ __device__ __forceinline__ void clear_rows(const LinearParams& P, int64_t q0) {
     for (int c = lane; c < P.C; c += WAVE) {
       uint64_t* q = P.seg + ((q0 + r) * P.C + c) * P.RW;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) seg_store(q + e, 0);
+      for (int e = 0; e < 4; ++e) store_zero(q + e);
     }
 }
 
@@ -626,8 +626,8 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
         const int c = t * WAVE + lane;
         if (r0 + j < R && c < P.C) {
           uint64_t* p = P.seg + (row_q<false>(P, b, r0 + j, 0) * P.C + c) * P.RW;
-          seg_store(p, 0);
-          seg_store(p + 1, 0);
+          store_zero(p);
+          store_zero(p + 1);
         }
         argmax_combine(m, idx, __uint_as_float((uint32_t)w[j][t][0]), (int)(uint32_t)w[j][t][1]);
       }

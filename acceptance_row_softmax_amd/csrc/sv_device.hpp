@@ -819,11 +819,19 @@ __device__ __forceinline__ bool poll_rec(const uint64_t* src, T& v, uint32_t tag
   }
 }
 
+// Zeroing a record or a counter for the next call. Every caller makes the last
+// access its words get in the launch, so the store need not be seen by another
+// wave of the same launch: it is a plain store, which completes in its XCD's L2
+// (a device-scope store writes through to memory, about a microsecond, and a wave
+// whose last stores are still in flight holds its slot). The end of the launch
+// writes the L2 back before any later launch can read the word.
+__device__ __forceinline__ void store_zero(uint64_t* p) {
+  __hip_atomic_store(p, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
 template <class T>
 __device__ __forceinline__ void clear_rec(uint64_t* dst) {
 #pragma unroll
-  for (int i = 0; i < RecWords<T>::N; ++i)
-    __hip_atomic_store(dst + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < RecWords<T>::N; ++i) store_zero(dst + i);
 }
 
 __device__ __forceinline__ uint32_t counter_add(uint32_t* p, uint32_t v) {
@@ -842,9 +850,10 @@ __device__ __forceinline__ uint64_t state_or(uint64_t* p, uint64_t v) {
 __device__ __forceinline__ uint64_t state_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// (the last access of the counter in the launch; see store_zero)
 template <class T>
 __device__ __forceinline__ void counter_reset(T* p) {
-  __hip_atomic_store(p, (T)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p, (T)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
 }  // namespace sv
