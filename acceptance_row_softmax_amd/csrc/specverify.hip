@@ -423,7 +423,7 @@ __device__ __forceinline__ void emit_clear(const LinearParams& P, int64_t b, boo
   if (lane == 4) counter_reset(P.fin + b * CSTRIDE);
 }
 
-// Writes every output of sequence b (its last event): the first rejected
+// Writes every output of sequence b (by its one emitting wave): the first rejected
 // position from the state word, the final token (known_y, or the token record),
 // the error bits, and the accepted drafts. One writer per output.
 template <int DT, bool STOCH>
@@ -490,10 +490,12 @@ struct Ev {
 };
 constexpr uint32_t EV_ERR = 1u << 16, EV_COUNT = EV_ERR - 1u;
 
-// Counts n events of sequence b (k pair combines, target row k and the final
-// token); the last one writes the outputs. The token event carries the token: if
-// it is not the last event, the token goes to the token record for the wave that
-// will be.
+// Counts n events of sequence b (k pair combines, target row k and, where no
+// residual wave draws it, the final token); the event that completes the count
+// writes the outputs. The token event carries the token: if it is not the last
+// event, the token goes to the token record for the wave that will be. (A
+// correction token drawn by a residual wave is not counted: that wave emits, see
+// others_counted.)
 template <int DT, bool STOCH>
 __device__ __forceinline__ void linear_event(const LinearParams& P, int64_t b, bool token, int y, uint32_t n) {
   const uint32_t total = (uint32_t)P.EV;
