@@ -1458,17 +1458,6 @@ __device__ __forceinline__ void tree_typical_combine(const TreeParams& P, int64_
 constexpr int WW_SLOTS = 4;
 constexpr int64_t WAVE_WALK_NODES = WW_SLOTS * WAVE;
 
-// a[m / 64] of lane m % 64, for every lane's own m in [0, WAVE_WALK_NODES)
-__device__ __forceinline__ int ww_gather(const int (&a)[WW_SLOTS], int m) {
-  int r = 0;
-#pragma unroll
-  for (int s = 0; s < WW_SLOTS; ++s) {
-    const int v = __shfl(a[s], m & (WAVE - 1));
-    if ((m >> 6) == s) r = v;
-  }
-  return r;
-}
-
 __device__ __forceinline__ int wave_or_int(int v) {
 #pragma unroll
   for (int o = 1; o < WAVE; o <<= 1) v |= __shfl_xor(v, o);
@@ -1550,13 +1539,33 @@ __device__ __forceinline__ void tree_wave_walk(const TreeParams& P, int64_t b, i
     pv[s] = bad ? 0 : pv[s];
     st[s] = bad ? 0 : 1;   // whether the match test applies
   }
-  // match: the candidate is its parent's token
+  // The walk reads other nodes' parents, tokens, candidates and match flags by
+  // index: from this wave's rows in LDS, one read each (a cross-lane permute per
+  // slot instead made the walk take about 4 us).
+  __shared__ int ww_sh[WPB][4][WAVE_WALK_NODES];
+  int* sp = ww_sh[wave_in_block()][0];   // parents
+  int* sc = ww_sh[wave_in_block()][1];   // candidates
+  int* sy = ww_sh[wave_in_block()][2];   // tokens
+  int* sm = ww_sh[wave_in_block()][3];   // match flags
 #pragma unroll
   for (int s = 0; s < WW_SLOTS; ++s) {
-    const int yp = ww_gather(yv, pv[s]);
     const int i = s * WAVE + lane;
-    st[s] = (i > 0 && i < N && st[s] && cv[s] == yp) ? 1 : 0;
+    if (i < N) {
+      sp[i] = pv[s];
+      sc[i] = cv[s];
+      sy[i] = yv[s];
+    }
   }
+  __builtin_amdgcn_wave_barrier();
+  // match: the candidate is its parent's token (node indices are below N)
+#pragma unroll
+  for (int s = 0; s < WW_SLOTS; ++s) {
+    const int i = s * WAVE + lane;
+    const int yp = (i > 0 && i < N) ? sy[pv[s]] : 0;   // (the root has no parent to read)
+    st[s] = (i > 0 && i < N && st[s] && cv[s] == yp) ? 1 : 0;
+    if (i < N) sm[i] = st[s];
+  }
+  __builtin_amdgcn_wave_barrier();
   // every node's chain to the root: depth, and whether every node on it matched
   int cur[WW_SLOTS], d[WW_SLOTS], acc[WW_SLOTS];
   int too_deep = 0;
@@ -1571,8 +1580,8 @@ __device__ __forceinline__ void tree_wave_walk(const TreeParams& P, int64_t b, i
     int moving = 0;
 #pragma unroll
     for (int s = 0; s < WW_SLOTS; ++s) {
-      const int m = ww_gather(st, cur[s]);
-      const int up = ww_gather(pv, cur[s]);
+      const int m = sm[cur[s]];
+      const int up = sp[cur[s]];
       if (cur[s] == 0) continue;
       if (d[s] >= P.max_depth) {
         too_deep = 1;
@@ -1616,10 +1625,10 @@ __device__ __forceinline__ void tree_wave_walk(const TreeParams& P, int64_t b, i
   for (int64_t j = L + 1 + lane; j <= P.max_depth; j += WAVE) out[j] = -1;
   // the accepted path, from the deepest node up
   int node = best;
-  const int yb = ww_gather(yv, best);
+  const int yb = sy[best];
   for (int j = L - 1; j >= 0; --j) {
-    const int cn = ww_gather(cv, node);
-    const int up = ww_gather(pv, node);
+    const int cn = sc[node];
+    const int up = sp[node];
     if (lane == 0) {
       path[j] = node;
       out[j] = cn;
