@@ -50,6 +50,7 @@
 #include "sv_rows.hpp"
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <atomic>
 #include <cfloat>
 #include <cmath>
@@ -136,6 +137,7 @@ __device__ __forceinline__ ResidW make_residw(const Decision& d, float c0) {
 // halves are 32 registers per lane, where whole chunks would be 64, which would
 // set the occupancy of the whole launch.
 constexpr int RH = 2;
+constexpr int64_t EARLY_SLOTS = 32;   // queued launches: see linear_setup
 constexpr int HU = CU / RH;
 
 // Residual sum over a loaded run of units of rows t_L, d_L (same value in every
@@ -215,6 +217,7 @@ struct LinearParams {
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
   uint32_t tk0;         // stochastic: first wave of the sequence blocks (target row k, its finisher, residual waves)
+  uint32_t early;       // queued: decision slots whose residual waves come before the sequence blocks
   // optional commit by the emitting wave (spec_verify_linear_commit)
   int32_t* seq_len;     // [B] in/out
   int32_t* history;     // [B][capacity]
@@ -1225,11 +1228,20 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
       }
     } else {
       // sequence blocks: C chunk waves of target row k, its finisher and (hold
-      // mode) CG residual waves; a queued launch's residual waves after them
+      // mode) CG residual waves; a queued launch's residual waves of its first
+      // `early` decision slots before them, those of the other slots after them
       const uint32_t CG = (uint32_t)P.CG;
       const uint32_t CGb = (P.k > 0 && !P.queue) ? CG : 0u;
       const uint32_t Q = NS + 1 + CGb;
-      const uint32_t v = w - P.tk0;
+      const uint32_t E = P.early * CG;
+      uint32_t v = w - P.tk0;
+      if (v < E) {
+        r.b = v / CG;
+        r.c = v - r.b * CG;
+        r.kind = ROLE_RESID;
+        return r;
+      }
+      v -= E;
       if (v < B * Q) {
         r.b = v / Q;
         const uint32_t e = v - r.b * Q;
@@ -1244,7 +1256,7 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
           r.kind = ROLE_RESID;
         }
       } else {
-        const uint32_t x = v - B * Q;   // queued: slot x / CG, part x mod CG
+        const uint32_t x = v - B * Q + E;   // queued: slot x / CG, part x mod CG
         r.b = x / CG;
         r.c = x - r.b * CG;
         r.kind = ROLE_RESID;
@@ -2335,6 +2347,16 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.CG = RH * P.C;
   P.hold = stoch && k > 0 && B * P.CG <= stochastic_wave_capacity(dtype) / 2;
   P.queue = stoch && k > 0 && !P.hold;
+  // Queued: the residual waves of the first decision slots (the first sequences
+  // rejected) are dispatched before target row k streams, so that their reloads
+  // and draws overlap that stream instead of following it. They wait only for
+  // pair decisions, made by waves dispatched before them, and hold at most a
+  // quarter of the resident waves.
+  P.early = 0;
+  if (P.queue) {
+    const int64_t cap = stochastic_wave_capacity(dtype) / 4 / P.CG;
+    P.early = (uint32_t)std::max<int64_t>(0, std::min<int64_t>({B, (int64_t)EARLY_SLOTS, cap}));
+  }
   // see linear_role for the order of the waves
   if (!stoch) {
     P.n_waves = sh.RQ * sh.C + B;
