@@ -19,9 +19,9 @@
 //    chunk; the last of a sequence picks the part holding u*S, and the correction
 //    token is drawn by an inverse-CDF scan inside it (by the wave that holds that
 //    part in hold mode, else after a reload). A launch with more residual waves
-//    than the GPU keeps waiting at once is queued: its residual waves come last and
-//    serve decision slots taken in the order the decisions are made, rejections
-//    first;
+//    than the GPU keeps waiting at once is queued: its residual waves serve
+//    decision slots taken in the order the decisions are made, rejections first,
+//    the first slots' waves ahead of target row k's stream and the others last;
 //  * one wave writes all outputs of a sequence: the wave that drew its correction
 //    token, once the sequence's other events (an atomic counter per sequence) have
 //    all counted; with every draft accepted, the last event to count. A wave that
@@ -216,8 +216,8 @@ struct LinearParams {
   float c0;
   uint32_t tag;
   int64_t n_waves;      // waves of the launch (see linear_role)
-  uint32_t tk0;         // stochastic: first wave of the sequence blocks (target row k, its finisher, residual waves)
-  uint32_t early;       // queued: decision slots whose residual waves come before the sequence blocks
+  uint32_t tk0;         // stochastic: first wave after the position blocks (see linear_role)
+  uint32_t early;       // residual waves before the sequence blocks: hold mode every sequence's, queued the first slots'
   // optional commit by the emitting wave (spec_verify_linear_commit)
   int32_t* seq_len;     // [B] in/out
   int32_t* history;     // [B][capacity]
@@ -657,9 +657,10 @@ __device__ __forceinline__ void greedy_finish(const LinearParams& P, int64_t b) 
 // Queued launches (more residual waves than can wait on the GPU at once) place
 // each decision in a slot, in the order the decisions are made: a rejection takes
 // the next slot from the front, a sequence with every draft accepted the next one
-// from the back. Their residual waves come last in the launch, in slot order, so
-// the waves of rejecting sequences start first and the back slots' waves, which
-// have nothing to draw, start last. Lane 0 takes the slot; publish_decision turns
+// from the back. Their residual waves run in slot order (the first slots' before
+// target row k streams, the others last in the launch), so the waves of rejecting
+// sequences start first and the back slots' waves, which have nothing to draw,
+// start last. Lane 0 takes the slot; publish_decision turns
 // the value returned into the slot.
 __device__ __forceinline__ uint64_t take_slot(const LinearParams& P, bool accepted) {
   return __hip_atomic_fetch_add(P.slots, accepted ? (1ull << 32) : 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1227,12 +1228,11 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
         r.kind = ROLE_PAIR;
       }
     } else {
-      // sequence blocks: C chunk waves of target row k, its finisher and (hold
-      // mode) CG residual waves; a queued launch's residual waves of its first
-      // `early` decision slots before them, those of the other slots after them
+      // the CG residual waves of `early` sequences (hold mode: all of them) or
+      // decision slots (queued), then the sequence blocks (the C chunk waves of
+      // target row k and its finisher), then a queued launch's other slots
       const uint32_t CG = (uint32_t)P.CG;
-      const uint32_t CGb = (P.k > 0 && !P.queue) ? CG : 0u;
-      const uint32_t Q = NS + 1 + CGb;
+      const uint32_t Q = NS + 1;
       const uint32_t E = P.early * CG;
       uint32_t v = w - P.tk0;
       if (v < E) {
@@ -1249,11 +1249,8 @@ __device__ __forceinline__ Role linear_role(const LinearParams& P, uint32_t w) {
           r.q = (uint32_t)(2 * P.k) * B + r.b;
           r.c = e;
           r.kind = ROLE_STREAM;
-        } else if (e == NS) {
-          r.kind = ROLE_ROWK;
         } else {
-          r.c = e - NS - 1;
-          r.kind = ROLE_RESID;
+          r.kind = ROLE_ROWK;
         }
       } else {
         const uint32_t x = v - B * Q + E;   // queued: slot x / CG, part x mod CG
@@ -2342,17 +2339,18 @@ sv_status linear_setup(LinearParams& P, sv_mode mode, float temperature, int64_t
   P.RW = (int)sh.RW;
   P.EV = (int)(k + 2);
   P.c0 = stoch ? temperature_c0(temperature) : 1.0f;
-  // residual waves: RH per chunk (they come after every streaming wave); hold mode
+  // residual waves: RH per chunk (they come after the position blocks); hold mode
   // when all of them fit on the GPU at once, with room to spare, else queued
   P.CG = RH * P.C;
   P.hold = stoch && k > 0 && B * P.CG <= stochastic_wave_capacity(dtype) / 2;
   P.queue = stoch && k > 0 && !P.hold;
-  // Queued: the residual waves of the first decision slots (the first sequences
-  // rejected) are dispatched before target row k streams, so that their reloads
-  // and draws overlap that stream instead of following it. They wait only for
-  // pair decisions, made by waves dispatched before them, and hold at most a
-  // quarter of the resident waves.
-  P.early = 0;
+  // Residual waves dispatched before target row k streams, so that the reloads and
+  // draws of the sequences rejected first overlap that stream instead of following
+  // it: in hold mode every sequence's, in a queued launch those of the first
+  // decision slots (the first sequences rejected), at most a quarter of the
+  // resident waves. They wait only for pair decisions, made by waves dispatched
+  // before them.
+  P.early = P.hold ? (uint32_t)B : 0u;
   if (P.queue) {
     const int64_t cap = stochastic_wave_capacity(dtype) / 4 / P.CG;
     P.early = (uint32_t)std::max<int64_t>(0, std::min<int64_t>({B, (int64_t)EARLY_SLOTS, cap}));
